@@ -1,0 +1,11 @@
+"""fp64 CPU oracle of the KDA recurrent-state update.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU-baseline
+leg of the benchmark may import anything in this package; the HIP library and
+its Python binding never do.
+
+  kda_oracle.c / .h   plain C, token-by-token, OpenMP over (sequence, head)
+  kda_oracle.py       ctypes loader for the C oracle
+  kda_oracle_np.py    independent NumPy twin and the chunked (WY/UT) form
+  build.py            compiles libkda_oracle.so with gcc
+"""
