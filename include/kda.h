@@ -1,0 +1,187 @@
+/*
+ * kda.h -- C ABI of libkda.so: the Kimi Delta Attention (KDA) recurrent-state
+ * update on AMD MI355X (gfx950).
+ *
+ * What the operation is.  "vLLM Kimi K3 support" (section "Kimi K3
+ * architecture overview", KDA bullet) describes KDA as a linear-attention
+ * layer that keeps a fixed-size recurrent state per head; its section "Fused
+ * kernels and metadata optimisation" (KDA decode bullet) says one decode
+ * launch runs the short causal convolution, the recurrent update and RMSNorm
+ * so that the state is not re-read; "Kimi K3 vLLM GPU inference benchmark"
+ * (time-breakdown section) keeps that state in fp32 ("FP32 SSM cache").  The
+ * pages give no formulas.  Per (sequence b, head h, token t) this library
+ * computes:
+ *
+ *   conv     y_c = sum_{j<4} w[h][c][j] * x_c(t-3+j)   (tap 0 oldest), SiLU
+ *            over the 2*d_k + d_v channels q | k | v of the head;
+ *   norms    k^ = k / sqrt(|k|^2 + l2_eps),  q^ = q_scale * q / sqrt(|q|^2 + l2_eps)
+ *   gates    alpha_i = exp(-exp(A[h][i]) * softplus(g_i)),  beta = sigmoid(b)
+ *   state    S <- (I - beta k^ k^T) diag(alpha) S + beta k^ v^T   (d_k x d_v)
+ *   readout  o = S^T q^   (the updated state)
+ *   output   y = o / sqrt(mean(o^2) + rms_eps) * norm_w[h] * sigmoid(z)
+ *
+ * The compact per-request state blocks of the hybrid cache ("vLLM Kimi K3
+ * support", section "Hybrid KV-cache management") are modelled as a pool of
+ * fp32 state slots plus a pool of conv windows, addressed by an int32 slot
+ * table.
+ *
+ * Conventions for every call
+ *   - Tensor pointers are DEVICE pointers to row-major, contiguous arrays;
+ *     the caller owns them.  The library allocates nothing, keeps no pointer
+ *     after a call returns and holds no mutable global state (reentrant).
+ *   - Calls are asynchronous on `hip_stream` (a hipStream_t; NULL = the
+ *     default stream).  The returned status covers host-side validation,
+ *     done before any HIP call, and the launch itself; it never waits for
+ *     the GPU.
+ *   - Base pointers of state, conv_state, x_q, x_k, x_v, g, z, y, A, conv_wt,
+ *     norm_w and workspace must be 16-byte aligned; int32 tables 4-byte.
+ *   - Slot tables: -1 marks a padding row (nothing read or written except
+ *     zeros to its outputs).  Any other index outside [0, n_slots) is a caller
+ *     error found on the device: the row is skipped (outputs zeroed) and, if
+ *     cache->err_flag is set, 1 is stored there.  Two rows of one call naming
+ *     the same slot, or snapshot slots that alias live slots, are undefined.
+ *   - Shapes: d_k, d_v in {64, 128}; conv_w = 4; H >= 1.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+
+typedef enum kda_status {
+    KDA_OK = 0,
+    KDA_ERR_NULL = 1,        /* a required pointer is NULL                     */
+    KDA_ERR_SHAPE = 2,       /* a size is out of range                         */
+    KDA_ERR_DTYPE = 3,       /* unknown input dtype                            */
+    KDA_ERR_ALIGN = 4,       /* a pointer breaks the alignment rule            */
+    KDA_ERR_UNSUPPORTED = 5, /* valid but not built (d_k, d_v, conv_w, flags)   */
+    KDA_ERR_WORKSPACE = 6,   /* workspace smaller than the size query returns  */
+    KDA_ERR_LAUNCH = 7       /* the HIP launch reported an error               */
+} kda_status;
+
+typedef enum kda_dtype {
+    KDA_F32 = 0,             /* float32 inputs and conv window                 */
+    KDA_BF16 = 1             /* bfloat16 inputs and conv window                */
+} kda_dtype;
+
+/* flags */
+#define KDA_CONV_SILU 1u     /* SiLU after the conv (the usual setting)        */
+
+/* Parameters of one KDA layer (device pointers, fp32). */
+typedef struct kda_layer {
+    int32_t H, d_k, d_v, conv_w;
+    const float *A;          /* [H, d_k]  decay log-rate                        */
+    const float *conv_wt;    /* [H, 2*d_k + d_v, conv_w]  q|k|v, tap 0 oldest    */
+    const float *norm_w;     /* [H, d_v]  RMSNorm weight                        */
+    float q_scale;           /* usually d_k^-1/2                                */
+    float l2_eps;            /* usually 1e-6                                    */
+    float rms_eps;           /* usually 1e-6                                    */
+    uint32_t flags;          /* KDA_CONV_SILU                                   */
+} kda_layer;
+
+/* The recurrent-state pools (device pointers). */
+typedef struct kda_cache {
+    float *state;            /* [n_slots, H, d_k, d_v] fp32                     */
+    void *conv_state;        /* [n_slots, H, conv_w-1, 2*d_k + d_v], input dtype;
+                                row 0 oldest; holds raw (pre-conv) inputs      */
+    int32_t n_slots;
+    int32_t *err_flag;       /* optional device int32; 1 on a bad slot index   */
+} kda_cache;
+
+/* Per-token inputs (device pointers, all of `dtype`), N tokens:
+ * x_q, x_k, g [N, H, d_k]; x_v, z [N, H, d_v]; b [N, H]. */
+typedef struct kda_inputs {
+    const void *x_q, *x_k, *x_v, *g, *b, *z;
+    kda_dtype dtype;
+} kda_inputs;
+
+/*
+ * kda_decode -- one token for each of B sequences (the fused decode launch of
+ * "vLLM Kimi K3 support", section "Fused kernels and metadata optimisation").
+ *   slot_idx [B] int32: the state/window slot of each sequence.
+ *   inputs: N = B tokens, token b belongs to sequence b.
+ *   y [B, H, d_v] fp32 output.
+ * The state and window at slot_idx[b] are read once and updated in place.
+ * B = 0 is a no-op.
+ */
+kda_status kda_decode(const kda_layer *layer, const kda_cache *cache,
+                      const int32_t *slot_idx, int32_t B,
+                      const kda_inputs *inputs, float *y, void *hip_stream);
+
+/*
+ * kda_spec_verify -- target-side verification of T draft tokens per sequence
+ * (the speculative decoding of "vLLM Kimi K3 support", section "Speculative
+ * decoding with DSpark"; 3-7 and 8 draft tokens per step are quoted there and
+ * in "Kimi K3 vLLM GPU inference benchmark").  The T tokens of a sequence
+ * are processed in order from the state at slot_idx[b], which is NOT modified.
+ *   snap_slots [B, T] int32: after token t the state and window are written
+ *     to slot snap_slots[b*T + t] (-1: not kept).
+ *   draft_len [B] int32 or NULL (= T): sequence b processes its first
+ *     draft_len[b] tokens; y of the remaining tokens is zeroed.
+ *   inputs: N = B*T tokens, token (b, t) at row b*T + t.
+ *   y [B, T, H, d_v] fp32.
+ * 1 <= T <= 16.  The per-token arithmetic is the same code as kda_decode, so
+ * verify + commit(L) is bitwise equal to L decode calls.
+ */
+kda_status kda_spec_verify(const kda_layer *layer, const kda_cache *cache,
+                           const int32_t *slot_idx, const int32_t *snap_slots,
+                           int32_t B, int32_t T, const int32_t *draft_len,
+                           const kda_inputs *inputs, float *y, void *hip_stream);
+
+/*
+ * kda_spec_commit -- keep the accepted prefix of a verification.
+ *   accepted_len [B] int32 (device), each in [0, T]: copies the state and
+ *   window snapshot of token accepted_len[b]-1 (snap_slots[b*T + L-1]) into
+ *   slot_idx[b]; L = 0 keeps the pre-verify state (no copy).  A length
+ *   outside [0, T], or a needed snapshot slot of -1 / out of range, sets
+ *   err_flag and leaves that sequence untouched.
+ */
+kda_status kda_spec_commit(const kda_layer *layer, const kda_cache *cache,
+                           const int32_t *slot_idx, const int32_t *snap_slots,
+                           const int32_t *accepted_len, int32_t B, int32_t T,
+                           kda_dtype window_dtype, void *hip_stream);
+
+/*
+ * kda_chunk_prefill -- many tokens per sequence in chunks (the prefill path,
+ * "vLLM Kimi K3 support", section "Fused kernels and metadata optimisation",
+ * KDA prefill bullet).  Same result as running the tokens one by one; inside
+ * a chunk the recurrence is solved in closed form (WY/UT form) with the
+ * contractions on MFMA, and the fp32 state is carried from chunk to chunk.
+ *   slot_idx [N_seq] int32; cu_seqlens [N_seq + 1] int32 (device) with
+ *   cu_seqlens[0] = 0, non-decreasing, cu_seqlens[N_seq] = total_T.
+ *   inputs: total_T tokens; y [total_T, H, d_v] fp32.
+ *   chunk: 64.  workspace: >= kda_chunk_prefill_workspace_bytes(...).
+ * The state and window at slot_idx[s] are the start state (zero them for a
+ * fresh sequence) and are replaced by the final ones.
+ */
+kda_status kda_chunk_prefill(const kda_layer *layer, const kda_cache *cache,
+                             const int32_t *slot_idx, const int32_t *cu_seqlens,
+                             int32_t N_seq, int32_t total_T, int32_t chunk,
+                             const kda_inputs *inputs, float *y,
+                             void *workspace, size_t workspace_bytes,
+                             void *hip_stream);
+
+/* Bytes of device workspace kda_chunk_prefill needs (0 on invalid sizes). */
+size_t kda_chunk_prefill_workspace_bytes(const kda_layer *layer, int32_t total_T,
+                                         int32_t N_seq, int32_t chunk);
+
+/* Measurement helper: dst[i] = src[i] for n floats (a plain streaming copy,
+ * used to calibrate memory-traffic counters and the practical HBM ceiling). */
+kda_status kda_copy_probe(float *dst, const float *src, size_t n, void *hip_stream);
+
+/* Static text for a status code. */
+const char *kda_status_string(kda_status status);
+
+/* KDA_ABI_VERSION of the built library. */
+int32_t kda_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KDA_H */

@@ -1,0 +1,255 @@
+"""Python binding of libkda.so: the entry points of include/kda.h under the
+same names, taking torch tensors.
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity (the C ABI sees bare pointers and cannot check sizes), their device
+pointers and torch's current HIP stream are passed through, and a non-OK
+status raises ``KdaError``.  All computation happens in the HIP kernels.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import _lib
+
+
+class KdaError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        self.code = code
+        self.status = _lib.STATUS.get(code, str(code))
+        super().__init__(f"{fn}: {self.status} ({kda_status_string(code)})")
+
+
+@dataclass
+class Layer:
+    """Parameters of one KDA layer: A [H, d_k], conv_wt [H, 2 d_k + d_v, 4],
+    norm_w [H, d_v], all fp32 device tensors."""
+    A: torch.Tensor
+    conv_wt: torch.Tensor
+    norm_w: torch.Tensor
+    q_scale: Optional[float] = None     # default d_k ** -0.5
+    l2_eps: float = 1e-6
+    rms_eps: float = 1e-6
+    conv_silu: bool = True
+
+    @property
+    def H(self):
+        return self.A.shape[0]
+
+    @property
+    def d_k(self):
+        return self.A.shape[1]
+
+    @property
+    def d_v(self):
+        return self.norm_w.shape[1]
+
+    @property
+    def conv_w(self):
+        return self.conv_wt.shape[2]
+
+    def c_struct(self) -> _lib.KdaLayer:
+        for name in ("A", "conv_wt", "norm_w"):
+            _check(getattr(self, name), name, torch.float32)
+        H, dk, dv = self.H, self.d_k, self.d_v
+        if self.conv_wt.dim() != 3 or tuple(self.conv_wt.shape[:2]) != (H, 2 * dk + dv) \
+                or tuple(self.norm_w.shape) != (H, dv):
+            raise ValueError("layer parameter shapes disagree")
+        qs = dk ** -0.5 if self.q_scale is None else self.q_scale
+        return _lib.KdaLayer(H, dk, dv, self.conv_w, self.A.data_ptr(), self.conv_wt.data_ptr(),
+                             self.norm_w.data_ptr(), qs, self.l2_eps, self.rms_eps,
+                             _lib.KDA_CONV_SILU if self.conv_silu else 0)
+
+
+@dataclass
+class Cache:
+    """State pool [n_slots, H, d_k, d_v] fp32 and conv-window pool
+    [n_slots, H, conv_w - 1, 2 d_k + d_v] of the input dtype; optional int32
+    error flag (one element)."""
+    state: torch.Tensor
+    conv_state: torch.Tensor
+    err_flag: Optional[torch.Tensor] = None
+
+    @property
+    def n_slots(self):
+        return self.state.shape[0]
+
+    def c_struct(self, layer: Layer) -> _lib.KdaCache:
+        _check(self.state, "state", torch.float32)
+        _check(self.conv_state, "conv_state")
+        H, dk, dv, W = layer.H, layer.d_k, layer.d_v, layer.conv_w
+        if tuple(self.state.shape) != (self.n_slots, H, dk, dv):
+            raise ValueError(f"state shape {tuple(self.state.shape)} != [n_slots, {H}, {dk}, {dv}]")
+        if tuple(self.conv_state.shape) != (self.n_slots, H, W - 1, 2 * dk + dv):
+            raise ValueError("conv_state shape must be [n_slots, H, conv_w-1, 2 d_k + d_v]")
+        ef = None
+        if self.err_flag is not None:
+            _check(self.err_flag, "err_flag", torch.int32)
+            ef = self.err_flag.data_ptr()
+        return _lib.KdaCache(self.state.data_ptr(), self.conv_state.data_ptr(), self.n_slots, ef)
+
+
+@dataclass
+class Inputs:
+    """Per-token inputs, fp32 or bf16 device tensors: x_q, x_k, g [..., H, d_k];
+    x_v, z [..., H, d_v]; b [..., H]."""
+    x_q: torch.Tensor
+    x_k: torch.Tensor
+    x_v: torch.Tensor
+    g: torch.Tensor
+    b: torch.Tensor
+    z: torch.Tensor
+
+    @property
+    def dtype(self):
+        return self.x_q.dtype
+
+    def c_struct(self, layer: Layer, lead: tuple) -> _lib.KdaInputs:
+        dt = self.x_q.dtype
+        if dt not in (torch.float32, torch.bfloat16):
+            raise TypeError(f"inputs must be float32 or bfloat16, not {dt}")
+        H, dk, dv = layer.H, layer.d_k, layer.d_v
+        want = dict(x_q=(H, dk), x_k=(H, dk), g=(H, dk), x_v=(H, dv), z=(H, dv), b=(H,))
+        for name, tail in want.items():
+            t = getattr(self, name)
+            _check(t, name, dt)
+            if tuple(t.shape) != tuple(lead) + tail:
+                raise ValueError(f"{name} shape {tuple(t.shape)} != {tuple(lead) + tail}")
+        code = _lib.KDA_BF16 if dt == torch.bfloat16 else _lib.KDA_F32
+        return _lib.KdaInputs(self.x_q.data_ptr(), self.x_k.data_ptr(), self.x_v.data_ptr(),
+                              self.g.data_ptr(), self.b.data_ptr(), self.z.data_ptr(), code)
+
+
+def _check(t: torch.Tensor, name: str, dtype=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, not {t.dtype}")
+
+
+def _stream(stream) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _raise(fn: str, code: int):
+    if code != 0:
+        raise KdaError(fn, code)
+
+
+def kda_decode(layer: Layer, cache: Cache, slot_idx: torch.Tensor, inputs: Inputs,
+               y: torch.Tensor, stream=None) -> None:
+    """One token per sequence; slot_idx [B] int32, inputs [B, H, .], y [B, H, d_v]."""
+    _check(slot_idx, "slot_idx", torch.int32)
+    B = slot_idx.numel()
+    _check(y, "y", torch.float32)
+    if tuple(y.shape) != (B, layer.H, layer.d_v):
+        raise ValueError("y must be [B, H, d_v]")
+    L, C, I = layer.c_struct(), cache.c_struct(layer), inputs.c_struct(layer, (B,))
+    if cache.conv_state.dtype != inputs.dtype:
+        raise TypeError("conv_state dtype must equal the input dtype")
+    _raise("kda_decode", _lib.load().kda_decode(ctypes.byref(L), ctypes.byref(C), slot_idx.data_ptr(),
+                                                B, ctypes.byref(I), y.data_ptr(), _stream(stream)))
+
+
+def kda_spec_verify(layer: Layer, cache: Cache, slot_idx: torch.Tensor, snap_slots: torch.Tensor,
+                    inputs: Inputs, y: torch.Tensor, draft_len: Optional[torch.Tensor] = None,
+                    stream=None) -> None:
+    """T draft tokens per sequence: snap_slots [B, T] int32, inputs [B, T, H, .],
+    y [B, T, H, d_v]; draft_len [B] int32 or None."""
+    _check(slot_idx, "slot_idx", torch.int32)
+    _check(snap_slots, "snap_slots", torch.int32)
+    B = slot_idx.numel()
+    if snap_slots.dim() != 2 or snap_slots.shape[0] != B:
+        raise ValueError("snap_slots must be [B, T]")
+    T = snap_slots.shape[1]
+    _check(y, "y", torch.float32)
+    if tuple(y.shape) != (B, T, layer.H, layer.d_v):
+        raise ValueError("y must be [B, T, H, d_v]")
+    dl = None
+    if draft_len is not None:
+        _check(draft_len, "draft_len", torch.int32)
+        if draft_len.numel() != B:
+            raise ValueError("draft_len must be [B]")
+        dl = draft_len.data_ptr()
+    L, C, I = layer.c_struct(), cache.c_struct(layer), inputs.c_struct(layer, (B, T))
+    if cache.conv_state.dtype != inputs.dtype:
+        raise TypeError("conv_state dtype must equal the input dtype")
+    _raise("kda_spec_verify", _lib.load().kda_spec_verify(
+        ctypes.byref(L), ctypes.byref(C), slot_idx.data_ptr(), snap_slots.data_ptr(), B, T, dl,
+        ctypes.byref(I), y.data_ptr(), _stream(stream)))
+
+
+def kda_spec_commit(layer: Layer, cache: Cache, slot_idx: torch.Tensor, snap_slots: torch.Tensor,
+                    accepted_len: torch.Tensor, stream=None) -> None:
+    """Copy snapshot accepted_len[b]-1 of each sequence into its live slot."""
+    _check(slot_idx, "slot_idx", torch.int32)
+    _check(snap_slots, "snap_slots", torch.int32)
+    _check(accepted_len, "accepted_len", torch.int32)
+    B = slot_idx.numel()
+    if snap_slots.dim() != 2 or snap_slots.shape[0] != B or accepted_len.numel() != B:
+        raise ValueError("snap_slots must be [B, T] and accepted_len [B]")
+    T = snap_slots.shape[1]
+    L, C = layer.c_struct(), cache.c_struct(layer)
+    wdt = _lib.KDA_BF16 if cache.conv_state.dtype == torch.bfloat16 else _lib.KDA_F32
+    _raise("kda_spec_commit", _lib.load().kda_spec_commit(
+        ctypes.byref(L), ctypes.byref(C), slot_idx.data_ptr(), snap_slots.data_ptr(),
+        accepted_len.data_ptr(), B, T, wdt, _stream(stream)))
+
+
+def kda_chunk_prefill_workspace_bytes(layer: Layer, total_T: int, N_seq: int, chunk: int = 64) -> int:
+    L = layer.c_struct()
+    return int(_lib.load().kda_chunk_prefill_workspace_bytes(ctypes.byref(L), total_T, N_seq, chunk))
+
+
+def kda_chunk_prefill(layer: Layer, cache: Cache, slot_idx: torch.Tensor, cu_seqlens: torch.Tensor,
+                      inputs: Inputs, y: torch.Tensor, workspace: Optional[torch.Tensor] = None,
+                      chunk: int = 64, stream=None) -> None:
+    """Chunked prefill of N_seq sequences packed along the token axis:
+    slot_idx [N_seq], cu_seqlens [N_seq + 1] int32, inputs [total_T, H, .],
+    y [total_T, H, d_v].  A workspace of the size query's bytes is allocated
+    here (torch) when none is given."""
+    _check(slot_idx, "slot_idx", torch.int32)
+    _check(cu_seqlens, "cu_seqlens", torch.int32)
+    N = slot_idx.numel()
+    if cu_seqlens.numel() != N + 1:
+        raise ValueError("cu_seqlens must be [N_seq + 1]")
+    total_T = inputs.x_q.shape[0]
+    _check(y, "y", torch.float32)
+    if tuple(y.shape) != (total_T, layer.H, layer.d_v):
+        raise ValueError("y must be [total_T, H, d_v]")
+    L, C, I = layer.c_struct(), cache.c_struct(layer), inputs.c_struct(layer, (total_T,))
+    if cache.conv_state.dtype != inputs.dtype:
+        raise TypeError("conv_state dtype must equal the input dtype")
+    need = int(_lib.load().kda_chunk_prefill_workspace_bytes(ctypes.byref(L), total_T, N, chunk))
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=y.device)
+    wp, wb = (None, 0) if workspace is None else (workspace.data_ptr(), workspace.numel() * workspace.element_size())
+    _raise("kda_chunk_prefill", _lib.load().kda_chunk_prefill(
+        ctypes.byref(L), ctypes.byref(C), slot_idx.data_ptr(), cu_seqlens.data_ptr(), N, total_T,
+        chunk, ctypes.byref(I), y.data_ptr(), wp, wb, _stream(stream)))
+
+
+def kda_copy_probe(dst: torch.Tensor, src: torch.Tensor, stream=None) -> None:
+    _check(dst, "dst", torch.float32)
+    _check(src, "src", torch.float32)
+    if dst.numel() != src.numel():
+        raise ValueError("dst and src sizes differ")
+    _raise("kda_copy_probe", _lib.load().kda_copy_probe(dst.data_ptr(), src.data_ptr(), src.numel(),
+                                                        _stream(stream)))
+
+
+def kda_status_string(code: int) -> str:
+    return _lib.load().kda_status_string(int(code)).decode()
+
+
+def kda_abi_version() -> int:
+    return int(_lib.load().kda_abi_version())

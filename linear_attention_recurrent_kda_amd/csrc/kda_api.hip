@@ -1,0 +1,207 @@
+// kda_api.hip -- the extern "C" entry points of libkda.so (declared in
+// include/kda.h): host-side argument validation, then dispatch to the
+// launchers.  Validation runs before any HIP call, so every error status is
+// returned without touching the device.
+#include <math.h>
+
+#include "kda_internal.h"
+
+#define KDA_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+using namespace kda;
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool finite_nonneg(float x) { return isfinite(x) && x >= 0.f; }
+
+size_t elem_size(kda_dtype dt) { return dt == KDA_BF16 ? 2 : 4; }
+
+kda_status check_layer(const kda_layer *L) {
+    if (!L) return KDA_ERR_NULL;
+    if (!L->A || !L->conv_wt || !L->norm_w) return KDA_ERR_NULL;
+    if (L->H <= 0 || L->d_k <= 0 || L->d_v <= 0 || L->conv_w <= 0) return KDA_ERR_SHAPE;
+    if (!((L->d_k == 64 || L->d_k == 128) && (L->d_v == 64 || L->d_v == 128))) return KDA_ERR_UNSUPPORTED;
+    if (L->conv_w != 4) return KDA_ERR_UNSUPPORTED;
+    if (L->flags & ~KDA_CONV_SILU) return KDA_ERR_UNSUPPORTED;
+    if (!isfinite(L->q_scale) || !finite_nonneg(L->l2_eps) || !finite_nonneg(L->rms_eps))
+        return KDA_ERR_SHAPE;
+    if (!aligned(L->A, 16) || !aligned(L->conv_wt, 16) || !aligned(L->norm_w, 16)) return KDA_ERR_ALIGN;
+    return KDA_OK;
+}
+
+kda_status check_cache(const kda_cache *C) {
+    if (!C) return KDA_ERR_NULL;
+    if (!C->state || !C->conv_state) return KDA_ERR_NULL;
+    if (C->n_slots <= 0) return KDA_ERR_SHAPE;
+    if (!aligned(C->state, 16) || !aligned(C->conv_state, 16)) return KDA_ERR_ALIGN;
+    if (C->err_flag && !aligned(C->err_flag, 4)) return KDA_ERR_ALIGN;
+    return KDA_OK;
+}
+
+kda_status check_inputs(const kda_inputs *in) {
+    if (!in) return KDA_ERR_NULL;
+    if (in->dtype != KDA_F32 && in->dtype != KDA_BF16) return KDA_ERR_DTYPE;
+    if (!in->x_q || !in->x_k || !in->x_v || !in->g || !in->b || !in->z) return KDA_ERR_NULL;
+    if (!aligned(in->x_q, 16) || !aligned(in->x_k, 16) || !aligned(in->x_v, 16) ||
+        !aligned(in->g, 16) || !aligned(in->z, 16) || !aligned(in->b, elem_size(in->dtype)))
+        return KDA_ERR_ALIGN;
+    return KDA_OK;
+}
+
+#define KDA_TRY(expr)                      \
+    do {                                   \
+        const kda_status st_ = (expr);     \
+        if (st_ != KDA_OK) return st_;     \
+    } while (0)
+
+RecParams rec_params(const kda_layer *L, const kda_cache *C, const kda_inputs *in, float *y) {
+    RecParams p{};
+    p.A = L->A; p.conv_wt = L->conv_wt; p.norm_w = L->norm_w;
+    p.q_scale = L->q_scale; p.l2_eps = L->l2_eps; p.rms_eps = L->rms_eps;
+    p.silu = (L->flags & KDA_CONV_SILU) ? 1 : 0;
+    p.state = C->state; p.window = C->conv_state; p.n_slots = C->n_slots; p.err_flag = C->err_flag;
+    p.x_q = in->x_q; p.x_k = in->x_k; p.x_v = in->x_v; p.g = in->g; p.b = in->b; p.z = in->z;
+    p.y = y;
+    p.H = L->H;
+    return p;
+}
+
+}  // namespace
+
+KDA_EXPORT kda_status kda_decode(const kda_layer *layer, const kda_cache *cache,
+                                 const int32_t *slot_idx, int32_t B, const kda_inputs *inputs,
+                                 float *y, void *hip_stream) {
+    KDA_TRY(check_layer(layer));
+    KDA_TRY(check_cache(cache));
+    if (B < 0) return KDA_ERR_SHAPE;
+    if (B == 0) return KDA_OK;
+    KDA_TRY(check_inputs(inputs));
+    if ((size_t)B * layer->H > 0x7fffffffu) return KDA_ERR_SHAPE;
+    if (!slot_idx || !y) return KDA_ERR_NULL;
+    if (!aligned(slot_idx, 4)) return KDA_ERR_ALIGN;
+    if (!aligned(y, 16)) return KDA_ERR_ALIGN;
+    RecParams p = rec_params(layer, cache, inputs, y);
+    p.slot_idx = slot_idx;
+    p.B = B;
+    p.T = 1;
+    return launch_recurrent(p, layer->d_k, layer->d_v, inputs->dtype, false,
+                            static_cast<hipStream_t>(hip_stream));
+}
+
+KDA_EXPORT kda_status kda_spec_verify(const kda_layer *layer, const kda_cache *cache,
+                                      const int32_t *slot_idx, const int32_t *snap_slots,
+                                      int32_t B, int32_t T, const int32_t *draft_len,
+                                      const kda_inputs *inputs, float *y, void *hip_stream) {
+    KDA_TRY(check_layer(layer));
+    KDA_TRY(check_cache(cache));
+    if (B < 0 || T < 1 || T > 16) return KDA_ERR_SHAPE;
+    if (B == 0) return KDA_OK;
+    KDA_TRY(check_inputs(inputs));
+    if ((size_t)B * layer->H > 0x7fffffffu) return KDA_ERR_SHAPE;
+    if (!slot_idx || !snap_slots || !y) return KDA_ERR_NULL;
+    if (!aligned(slot_idx, 4) || !aligned(snap_slots, 4) || (draft_len && !aligned(draft_len, 4)))
+        return KDA_ERR_ALIGN;
+    if (!aligned(y, 16)) return KDA_ERR_ALIGN;
+    RecParams p = rec_params(layer, cache, inputs, y);
+    p.slot_idx = slot_idx;
+    p.snap_slots = snap_slots;
+    p.draft_len = draft_len;
+    p.B = B;
+    p.T = T;
+    return launch_recurrent(p, layer->d_k, layer->d_v, inputs->dtype, true,
+                            static_cast<hipStream_t>(hip_stream));
+}
+
+KDA_EXPORT kda_status kda_spec_commit(const kda_layer *layer, const kda_cache *cache,
+                                      const int32_t *slot_idx, const int32_t *snap_slots,
+                                      const int32_t *accepted_len, int32_t B, int32_t T,
+                                      kda_dtype window_dtype, void *hip_stream) {
+    KDA_TRY(check_layer(layer));
+    KDA_TRY(check_cache(cache));
+    if (window_dtype != KDA_F32 && window_dtype != KDA_BF16) return KDA_ERR_DTYPE;
+    if (B < 0 || T < 1 || T > 16) return KDA_ERR_SHAPE;
+    if (B == 0) return KDA_OK;
+    if ((size_t)B * layer->H > 0x7fffffffu) return KDA_ERR_SHAPE;
+    if (!slot_idx || !snap_slots || !accepted_len) return KDA_ERR_NULL;
+    if (!aligned(slot_idx, 4) || !aligned(snap_slots, 4) || !aligned(accepted_len, 4))
+        return KDA_ERR_ALIGN;
+    CommitParams p{};
+    p.state = cache->state;
+    p.window = cache->conv_state;
+    p.n_slots = cache->n_slots;
+    p.err_flag = cache->err_flag;
+    p.slot_idx = slot_idx;
+    p.snap_slots = snap_slots;
+    p.accepted_len = accepted_len;
+    p.B = B;
+    p.H = layer->H;
+    p.T = T;
+    p.state_elems = layer->d_k * layer->d_v;
+    p.window_words = (int)((size_t)(layer->conv_w - 1) * (2 * layer->d_k + layer->d_v) *
+                           elem_size(window_dtype) / 4);
+    return launch_commit(p, static_cast<hipStream_t>(hip_stream));
+}
+
+KDA_EXPORT size_t kda_chunk_prefill_workspace_bytes(const kda_layer *layer, int32_t total_T,
+                                                    int32_t N_seq, int32_t chunk) {
+    if (check_layer(layer) != KDA_OK || total_T < 0 || N_seq < 1 || chunk != 64) return 0;
+    return prefill_workspace_bytes(layer->H, layer->d_k, layer->d_v, total_T, N_seq, chunk);
+}
+
+KDA_EXPORT kda_status kda_chunk_prefill(const kda_layer *layer, const kda_cache *cache,
+                                        const int32_t *slot_idx, const int32_t *cu_seqlens,
+                                        int32_t N_seq, int32_t total_T, int32_t chunk,
+                                        const kda_inputs *inputs, float *y, void *workspace,
+                                        size_t workspace_bytes, void *hip_stream) {
+    KDA_TRY(check_layer(layer));
+    KDA_TRY(check_cache(cache));
+    KDA_TRY(check_inputs(inputs));
+    if (N_seq < 1 || total_T < 0 || chunk <= 0) return KDA_ERR_SHAPE;
+    if (chunk != 64) return KDA_ERR_UNSUPPORTED;
+    if (!slot_idx || !cu_seqlens || !y) return KDA_ERR_NULL;
+    if (!aligned(slot_idx, 4) || !aligned(cu_seqlens, 4) || !aligned(y, 16)) return KDA_ERR_ALIGN;
+    const size_t need = prefill_workspace_bytes(layer->H, layer->d_k, layer->d_v, total_T, N_seq, chunk);
+    if (need && !workspace) return KDA_ERR_NULL;
+    if (workspace_bytes < need) return KDA_ERR_WORKSPACE;
+    if (workspace && !aligned(workspace, 16)) return KDA_ERR_ALIGN;
+    PrefillParams p{};
+    p.A = layer->A; p.conv_wt = layer->conv_wt; p.norm_w = layer->norm_w;
+    p.q_scale = layer->q_scale; p.l2_eps = layer->l2_eps; p.rms_eps = layer->rms_eps;
+    p.silu = (layer->flags & KDA_CONV_SILU) ? 1 : 0;
+    p.state = cache->state; p.window = cache->conv_state; p.n_slots = cache->n_slots;
+    p.err_flag = cache->err_flag;
+    p.slot_idx = slot_idx; p.cu_seqlens = cu_seqlens;
+    p.N_seq = N_seq; p.total_T = total_T; p.chunk = chunk; p.H = layer->H;
+    p.x_q = inputs->x_q; p.x_k = inputs->x_k; p.x_v = inputs->x_v;
+    p.g = inputs->g; p.b = inputs->b; p.z = inputs->z;
+    p.y = y;
+    p.workspace = workspace;
+    p.workspace_bytes = workspace_bytes;
+    return launch_prefill(p, layer->d_k, layer->d_v, inputs->dtype,
+                          static_cast<hipStream_t>(hip_stream));
+}
+
+KDA_EXPORT kda_status kda_copy_probe(float *dst, const float *src, size_t n, void *hip_stream) {
+    if (n == 0) return KDA_OK;
+    if (!dst || !src) return KDA_ERR_NULL;
+    if (!aligned(dst, 16) || !aligned(src, 16)) return KDA_ERR_ALIGN;
+    return launch_copy_probe(dst, src, n, static_cast<hipStream_t>(hip_stream));
+}
+
+KDA_EXPORT const char *kda_status_string(kda_status s) {
+    switch (s) {
+        case KDA_OK: return "ok";
+        case KDA_ERR_NULL: return "a required pointer is null";
+        case KDA_ERR_SHAPE: return "a size or scalar parameter is out of range";
+        case KDA_ERR_DTYPE: return "unknown input dtype";
+        case KDA_ERR_ALIGN: return "a pointer is not aligned as required";
+        case KDA_ERR_UNSUPPORTED: return "unsupported configuration (d_k, d_v, conv_w, chunk or flags)";
+        case KDA_ERR_WORKSPACE: return "workspace too small";
+        case KDA_ERR_LAUNCH: return "kernel launch failed";
+    }
+    return "unknown status";
+}
+
+KDA_EXPORT int32_t kda_abi_version(void) { return KDA_ABI_VERSION; }

@@ -1,0 +1,71 @@
+// kda_internal.h -- launch parameters and launchers shared between the C-ABI
+// front end (kda_api.hip) and the kernel files.  Host-side only types.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "kda.h"
+
+namespace kda {
+
+// Everything a token-recurrent kernel (decode, verify) needs, flattened.
+struct RecParams {
+    // layer
+    const float *A, *conv_wt, *norm_w;
+    float q_scale, l2_eps, rms_eps;
+    int silu;
+    // cache
+    float *state;
+    void *window;
+    int n_slots;
+    int32_t *err_flag;
+    // tables
+    const int32_t *slot_idx;    // [B]
+    const int32_t *snap_slots;  // [B, T] (verify)
+    const int32_t *draft_len;   // [B] or null (verify)
+    // inputs, rows n = b (decode) or b*T + t (verify)
+    const void *x_q, *x_k, *x_v, *g, *b, *z;
+    float *y;
+    int B, H, T;
+};
+
+struct CommitParams {
+    float *state;
+    void *window;
+    int n_slots;
+    int32_t *err_flag;
+    const int32_t *slot_idx, *snap_slots, *accepted_len;
+    int B, H, T;
+    int state_elems;   // d_k * d_v
+    int window_words;  // (conv_w - 1) * C_h * sizeof(input) / 4
+};
+
+struct PrefillParams {
+    // layer
+    const float *A, *conv_wt, *norm_w;
+    float q_scale, l2_eps, rms_eps;
+    int silu;
+    // cache
+    float *state;
+    void *window;
+    int n_slots;
+    int32_t *err_flag;
+    const int32_t *slot_idx, *cu_seqlens;
+    int N_seq, total_T, chunk, H;
+    const void *x_q, *x_k, *x_v, *g, *b, *z;
+    float *y;
+    void *workspace;
+    size_t workspace_bytes;
+};
+
+kda_status launch_recurrent(const RecParams &p, int d_k, int d_v, kda_dtype dt, bool verify,
+                            hipStream_t stream);
+kda_status launch_commit(const CommitParams &p, hipStream_t stream);
+kda_status launch_prefill(const PrefillParams &p, int d_k, int d_v, kda_dtype dt,
+                          hipStream_t stream);
+size_t prefill_workspace_bytes(int H, int d_k, int d_v, int total_T, int N_seq, int chunk);
+kda_status launch_copy_probe(float *dst, const float *src, size_t n, hipStream_t stream);
+
+}  // namespace kda

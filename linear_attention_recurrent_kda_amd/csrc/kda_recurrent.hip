@@ -1,0 +1,383 @@
+// kda_recurrent.hip -- token-recurrent KDA kernels for gfx950: fused decode,
+// speculative verification with per-token snapshots, and the commit copy.
+//
+// One workgroup owns one (sequence, head).  Its d_k x d_v fp32 state tile is
+// loaded from HBM once, at kernel entry, into registers (float4 per lane,
+// d_v contiguous so each wave instruction moves whole 512 B rows), and it is
+// written back once.  The delta rule is independent per state column given
+// (alpha, beta, k^, v), so the only cross-lane work per token is the
+// reduction over the d_k rows for u = S'^T k^ and p = S'^T q^ (wave butterfly
+// + one LDS exchange between waves) and the RMSNorm over d_v.
+//
+// Per token (see include/kda.h for the definition):
+//   conv + SiLU of the q|k|v channels (one lane per channel; the window of
+//   raw inputs lives in the cache and is shifted in place), L2 norms and the
+//   gates (one wave per token), then
+//     S' = diag(alpha) S,  u = S'^T k^,  p = S'^T q^          (one pass)
+//     d  = beta (v - u),   S = S' + k^ d^T,  o = p + (k^.q^) d  (= S^T q^)
+//     y  = o / sqrt(mean(o^2) + eps_r) * w * sigmoid(z)
+// Decode and verify instantiate the same code, so verify + commit(L) equals
+// L decode launches bit for bit.
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+template <int DK, int DV, int NT>
+struct RecGeo {
+    static constexpr int CG = DV / 4;      // float4 column groups
+    static constexpr int RG = NT / CG;     // row groups
+    static constexpr int RPT = DK / RG;    // state rows per lane
+    static constexpr int NW = NT / kWave;  // waves per workgroup
+    static constexpr int CH = 2 * DK + DV; // conv channels per head
+    static_assert(NT % CG == 0 && DK % RG == 0 && RPT >= 1, "tile does not divide");
+    static_assert(CG <= kWave && kWave % CG == 0, "a wave must hold whole rows");
+};
+
+// Per-token values shared through LDS.  conv[] holds the conv outputs
+// q | k | v; the norm pass overwrites q and k with q^ and k^ in place.
+template <int DK, int DV>
+struct TokenLds {
+    float conv[2 * DK + DV + 1];   // + 1: sink for lanes without a channel
+    float alpha[DK];
+    float gate[DV];   // norm_w * sigmoid(z)
+    float beta;
+    float kq;         // k^ . q^
+};
+
+// Raw operands of the conv for the channels one lane owns (c = tid + NT*k):
+// the tap weights, the three window entries and the T new inputs.
+template <int DK, int DV, int NT, typename Tin, int TMAX>
+struct ConvRegs {
+    static constexpr int CH = 2 * DK + DV;
+    static constexpr int CPT = (CH + NT - 1) / NT;
+    float4 w[CPT];
+    Tin x[CPT][3 + TMAX];
+};
+
+// All loads are unconditional (out-of-range channel slots and tokens re-read a
+// valid element) so the compiler issues them back to back, ahead of the state
+// tile, without branches that would force waits.  Requires T >= 1.
+template <int DK, int DV, int NT, typename Tin, int TMAX, bool VERIFY>
+__device__ __forceinline__ void conv_fetch(const RecParams &p, int tid, int b, int h, int slot, int T,
+                                           ConvRegs<DK, DV, NT, Tin, TMAX> &cr) {
+    constexpr int CH = 2 * DK + DV;
+    const Tin *win = static_cast<const Tin *>(p.window) + ((size_t)slot * p.H + h) * 3 * CH;
+#pragma unroll
+    for (int k = 0; k < cr.CPT; ++k) {
+        const int c = min(tid + NT * k, CH - 1);
+        cr.w[k] = *reinterpret_cast<const float4 *>(p.conv_wt + ((size_t)h * CH + c) * 4);
+        cr.x[k][0] = win[c];
+        cr.x[k][1] = win[CH + c];
+        cr.x[k][2] = win[2 * CH + c];
+        const bool isq = c < DK, isk = !isq && c < 2 * DK;
+        const Tin *src = isq ? static_cast<const Tin *>(p.x_q)
+                             : (isk ? static_cast<const Tin *>(p.x_k) : static_cast<const Tin *>(p.x_v));
+        const int stride = isq || isk ? DK : DV;
+        const int off = isq ? c : (isk ? c - DK : c - 2 * DK);
+#pragma unroll
+        for (int t = 0; t < TMAX; ++t) {
+            const int tt = min(t, T - 1);
+            const size_t n = VERIFY ? (size_t)b * p.T + tt : (size_t)b;
+            cr.x[k][3 + t] = src[(n * p.H + h) * stride + off];
+        }
+    }
+}
+
+// Conv (+ activation) of the owned channels for every token into LDS; the
+// window rows after each token go to the live slot (decode) or to the
+// token's snapshot slot (verify).
+template <int DK, int DV, int NT, typename Tin, int TMAX, bool VERIFY>
+__device__ __forceinline__ void conv_compute(const RecParams &p, int tid, int b, int h, int slot, int T,
+                                             const ConvRegs<DK, DV, NT, Tin, TMAX> &cr,
+                                             TokenLds<DK, DV> *tok) {
+    constexpr int CH = 2 * DK + DV;
+#pragma unroll
+    for (int k = 0; k < cr.CPT; ++k) {
+        // computed by every lane (a lane without a channel writes to the sink
+        // entry), so no branch separates the loads from their first use
+        const int c = tid + NT * k;
+        const bool own = c < CH;
+        const int cs = own ? c : CH;
+        const float4 w = cr.w[k];
+#pragma unroll
+        for (int t = 0; t < TMAX; ++t) {
+            if (t >= T) continue;
+            float acc = w.x * to_f32(cr.x[k][t]);
+            acc = fmaf(w.y, to_f32(cr.x[k][t + 1]), acc);
+            acc = fmaf(w.z, to_f32(cr.x[k][t + 2]), acc);
+            acc = fmaf(w.w, to_f32(cr.x[k][t + 3]), acc);
+            tok[t].conv[cs] = p.silu ? acc * sigmoid(acc) : acc;
+            if (VERIFY && own) {
+                const int ss = p.snap_slots[(size_t)b * p.T + t];
+                if (ss >= 0 && ss < p.n_slots) {
+                    Tin *sw = static_cast<Tin *>(p.window) + ((size_t)ss * p.H + h) * 3 * CH;
+                    sw[c] = cr.x[k][t + 1];
+                    sw[CH + c] = cr.x[k][t + 2];
+                    sw[2 * CH + c] = cr.x[k][t + 3];
+                }
+            }
+        }
+        if (!VERIFY && own) {
+            Tin *win = static_cast<Tin *>(p.window) + ((size_t)slot * p.H + h) * 3 * CH;
+            win[c] = cr.x[k][1];
+            win[CH + c] = cr.x[k][2];
+            win[2 * CH + c] = cr.x[k][3];
+        }
+    }
+}
+
+// Raw gate operands of the tokens one wave prepares (t = wave + NW*j).
+template <int DK, int DV, typename Tin, int TPW>
+struct PrepRegs {
+    static constexpr int EK = DK / kWave, EV = DV / kWave;
+    float A[EK], w[EV];
+    Tin g[TPW][EK], z[TPW][EV], b[TPW];
+};
+
+template <int DK, int DV, int NW, typename Tin, int TPW, bool VERIFY>
+__device__ __forceinline__ void prep_fetch(const RecParams &p, int wave, int lane, int b, int h, int T,
+                                           PrepRegs<DK, DV, Tin, TPW> &pr) {
+#pragma unroll
+    for (int e = 0; e < pr.EK; ++e) pr.A[e] = p.A[h * DK + lane + kWave * e];
+#pragma unroll
+    for (int e = 0; e < pr.EV; ++e) pr.w[e] = p.norm_w[h * DV + lane + kWave * e];
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+        const int t = min(wave + NW * j, T - 1);
+        const size_t n = VERIFY ? (size_t)b * p.T + t : (size_t)b;
+        const Tin *g = static_cast<const Tin *>(p.g) + (n * p.H + h) * DK;
+        const Tin *z = static_cast<const Tin *>(p.z) + (n * p.H + h) * DV;
+#pragma unroll
+        for (int e = 0; e < pr.EK; ++e) pr.g[j][e] = g[lane + kWave * e];
+#pragma unroll
+        for (int e = 0; e < pr.EV; ++e) pr.z[j][e] = z[lane + kWave * e];
+        pr.b[j] = static_cast<const Tin *>(p.b)[n * p.H + h];
+    }
+}
+
+// L2 norms, k^.q^ and gates of one token, by one whole wave.
+template <int DK, int DV, typename Tin, int TPW>
+__device__ __forceinline__ void prep_token(const RecParams &p, int lane, int j,
+                                           const PrepRegs<DK, DV, Tin, TPW> &pr,
+                                           TokenLds<DK, DV> &tk) {
+    constexpr int EK = DK / kWave, EV = DV / kWave;
+    float qv[EK], kv[EK];
+    float sq = 0.f, sk = 0.f;
+#pragma unroll
+    for (int e = 0; e < EK; ++e) {
+        qv[e] = tk.conv[lane + kWave * e];
+        kv[e] = tk.conv[DK + lane + kWave * e];
+        sq = fmaf(qv[e], qv[e], sq);
+        sk = fmaf(kv[e], kv[e], sk);
+    }
+    sq = wave_sum(sq);
+    sk = wave_sum(sk);
+    const float rq = p.q_scale / sqrtf(sq + p.l2_eps);
+    const float rk = 1.0f / sqrtf(sk + p.l2_eps);
+    float kq = 0.f;
+#pragma unroll
+    for (int e = 0; e < EK; ++e) {
+        qv[e] *= rq;
+        kv[e] *= rk;
+        kq = fmaf(qv[e], kv[e], kq);
+        tk.conv[lane + kWave * e] = qv[e];
+        tk.conv[DK + lane + kWave * e] = kv[e];
+    }
+    kq = wave_sum(kq);
+#pragma unroll
+    for (int e = 0; e < EK; ++e)
+        tk.alpha[lane + kWave * e] = expf(-expf(pr.A[e]) * softplus(to_f32(pr.g[j][e])));
+#pragma unroll
+    for (int e = 0; e < EV; ++e)
+        tk.gate[lane + kWave * e] = pr.w[e] * sigmoid(to_f32(pr.z[j][e]));
+    if (lane == 0) {
+        tk.beta = sigmoid(to_f32(pr.b[j]));
+        tk.kq = kq;
+    }
+}
+
+template <int DK, int DV, int NT, typename Tin, int TMAX, bool VERIFY>
+__global__ __launch_bounds__(NT) void kda_recurrent_kernel(RecParams p) {
+    using G = RecGeo<DK, DV, NT>;
+    __shared__ TokenLds<DK, DV> tok[TMAX];
+    __shared__ float4 red[G::NW][2][G::CG];
+
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave, wave = tid / kWave;
+    const int b = blockIdx.x / p.H, h = blockIdx.x % p.H;
+    const int cg = tid % G::CG, rg = tid / G::CG;
+
+    int T = 1;
+    if (VERIFY) T = p.draft_len ? min(max(p.draft_len[b], 0), p.T) : p.T;
+    const int slot = p.slot_idx[b];
+    const int y_rows = VERIFY ? p.T : 1;
+    float *yb = p.y + ((size_t)b * y_rows * p.H + h) * DV;   // token t at + t*H*DV
+    const bool bad = slot < 0 || slot >= p.n_slots;
+    if (bad && slot != -1 && tid == 0) flag_error(p.err_flag);
+    // zero the outputs of tokens this workgroup will not produce
+    for (int t = bad ? 0 : T; t < y_rows; ++t)
+        for (int j = tid; j < DV; j += NT) yb[(size_t)t * p.H * DV + j] = 0.f;
+    if (bad || T == 0) return;
+
+    // 1. fetch the small operands first, then issue the single read of the
+    //    state tile, so the conv/gate math below waits only for the former
+    constexpr int TPW = (TMAX + G::NW - 1) / G::NW;
+    ConvRegs<DK, DV, NT, Tin, TMAX> cr;
+    conv_fetch<DK, DV, NT, Tin, TMAX, VERIFY>(p, tid, b, h, slot, T, cr);
+    PrepRegs<DK, DV, Tin, TPW> pr;
+    prep_fetch<DK, DV, G::NW, Tin, TPW, VERIFY>(p, wave, lane, b, h, T, pr);
+    float *S = p.state + ((size_t)slot * p.H + h) * DK * DV;
+    float4 s[G::RPT];
+#pragma unroll
+    for (int i = 0; i < G::RPT; ++i)
+        s[i] = *reinterpret_cast<const float4 *>(S + (size_t)(rg + G::RG * i) * DV + 4 * cg);
+
+    // 2. conv (+ window update / window snapshots)
+    conv_compute<DK, DV, NT, Tin, TMAX, VERIFY>(p, tid, b, h, slot, T, cr, tok);
+    __syncthreads();
+    // 3. norms and gates, one wave per token
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+        const int t = wave + G::NW * j;
+        if (t < T) prep_token<DK, DV, Tin, TPW>(p, lane, j, pr, tok[t]);
+    }
+    __syncthreads();
+
+    // 4. the recurrence, tokens in order, state in registers
+    for (int t = 0; t < T; ++t) {
+        const TokenLds<DK, DV> &tk = tok[t];
+        float4 u = make_float4(0.f, 0.f, 0.f, 0.f), pq = u;
+#pragma unroll
+        for (int i = 0; i < G::RPT; ++i) {
+            const int r = rg + G::RG * i;
+            s[i] = s[i] * tk.alpha[r];
+            u = fma4(tk.conv[DK + r], s[i], u);
+            pq = fma4(tk.conv[r], s[i], pq);
+        }
+        // sum over the row groups inside the wave, then across waves
+#pragma unroll
+        for (int m = G::CG; m < kWave; m <<= 1) {
+            u.x += __shfl_xor(u.x, m, kWave); u.y += __shfl_xor(u.y, m, kWave);
+            u.z += __shfl_xor(u.z, m, kWave); u.w += __shfl_xor(u.w, m, kWave);
+            pq.x += __shfl_xor(pq.x, m, kWave); pq.y += __shfl_xor(pq.y, m, kWave);
+            pq.z += __shfl_xor(pq.z, m, kWave); pq.w += __shfl_xor(pq.w, m, kWave);
+        }
+        if (lane < G::CG) { red[wave][0][cg] = u; red[wave][1][cg] = pq; }
+        __syncthreads();
+        float4 U = red[0][0][cg], P = red[0][1][cg];
+#pragma unroll
+        for (int w = 1; w < G::NW; ++w) {
+            const float4 a = red[w][0][cg], c = red[w][1][cg];
+            U.x += a.x; U.y += a.y; U.z += a.z; U.w += a.w;
+            P.x += c.x; P.y += c.y; P.z += c.z; P.w += c.w;
+        }
+        const float beta = tk.beta;
+        const float4 v = *reinterpret_cast<const float4 *>(&tk.conv[2 * DK + 4 * cg]);
+        const float4 d = make_float4(beta * (v.x - U.x), beta * (v.y - U.y),
+                                     beta * (v.z - U.z), beta * (v.w - U.w));
+#pragma unroll
+        for (int i = 0; i < G::RPT; ++i) s[i] = fma4(tk.conv[DK + rg + G::RG * i], d, s[i]);
+
+        if (VERIFY) {
+            const int ss = p.snap_slots[(size_t)b * p.T + t];
+            if (ss >= 0 && ss < p.n_slots) {
+                float *D = p.state + ((size_t)ss * p.H + h) * DK * DV;
+#pragma unroll
+                for (int i = 0; i < G::RPT; ++i)
+                    *reinterpret_cast<float4 *>(D + (size_t)(rg + G::RG * i) * DV + 4 * cg) = s[i];
+            } else if (ss != -1 && tid == 0) {
+                flag_error(p.err_flag);
+            }
+        }
+        // output: o = p + (k^.q^) d, RMSNorm over d_v, gate
+        if (tid < G::CG) {
+            const float kq = tk.kq;
+            const float4 o = make_float4(fmaf(kq, d.x, P.x), fmaf(kq, d.y, P.y),
+                                         fmaf(kq, d.z, P.z), fmaf(kq, d.w, P.w));
+            float ss2 = o.x * o.x;
+            ss2 = fmaf(o.y, o.y, ss2);
+            ss2 = fmaf(o.z, o.z, ss2);
+            ss2 = fmaf(o.w, o.w, ss2);
+#pragma unroll
+            for (int m = 1; m < G::CG; m <<= 1) ss2 += __shfl_xor(ss2, m, kWave);
+            const float r = 1.0f / sqrtf(ss2 * (1.0f / DV) + p.rms_eps);
+            const float4 gt = *reinterpret_cast<const float4 *>(&tk.gate[4 * cg]);
+            *reinterpret_cast<float4 *>(yb + (size_t)t * p.H * DV + 4 * cg) =
+                make_float4(o.x * r * gt.x, o.y * r * gt.y, o.z * r * gt.z, o.w * r * gt.w);
+        }
+        __syncthreads();   // red[] is rewritten by the next token
+    }
+
+    // 5. the single write of the state tile (decode only: verify leaves S0)
+    if (!VERIFY) {
+#pragma unroll
+        for (int i = 0; i < G::RPT; ++i)
+            *reinterpret_cast<float4 *>(S + (size_t)(rg + G::RG * i) * DV + 4 * cg) = s[i];
+    }
+}
+
+// Commit: copy the snapshot of the last accepted token into the live slot.
+__global__ __launch_bounds__(256) void kda_commit_kernel(CommitParams p) {
+    const int b = blockIdx.x / p.H, h = blockIdx.x % p.H;
+    const int L = p.accepted_len[b];
+    const int dst = p.slot_idx[b];
+    if (L == 0 || dst == -1) return;
+    const bool bad_len = L < 0 || L > p.T;
+    const int src = bad_len ? -1 : p.snap_slots[(size_t)b * p.T + L - 1];
+    if (bad_len || dst < 0 || dst >= p.n_slots || src < 0 || src >= p.n_slots) {
+        if (threadIdx.x == 0) flag_error(p.err_flag);
+        return;
+    }
+    const float4 *s4 = reinterpret_cast<const float4 *>(p.state + ((size_t)src * p.H + h) * p.state_elems);
+    float4 *d4 = reinterpret_cast<float4 *>(p.state + ((size_t)dst * p.H + h) * p.state_elems);
+    for (int i = threadIdx.x; i < p.state_elems / 4; i += blockDim.x) d4[i] = s4[i];
+    const uint32_t *sw = static_cast<const uint32_t *>(p.window) + ((size_t)src * p.H + h) * p.window_words;
+    uint32_t *dw = static_cast<uint32_t *>(p.window) + ((size_t)dst * p.H + h) * p.window_words;
+    for (int i = threadIdx.x; i < p.window_words; i += blockDim.x) dw[i] = sw[i];
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+constexpr int kRecThreads = 256;
+
+template <int DK, int DV, typename Tin>
+static kda_status launch_rec_typed(const RecParams &p, bool verify, hipStream_t stream) {
+    const dim3 grid((unsigned)(p.B * p.H)), block(kRecThreads);
+    if (!verify) {
+        hipLaunchKernelGGL((kda_recurrent_kernel<DK, DV, kRecThreads, Tin, 1, false>), grid, block,
+                           0, stream, p);
+    } else if (p.T <= 8) {
+        hipLaunchKernelGGL((kda_recurrent_kernel<DK, DV, kRecThreads, Tin, 8, true>), grid, block,
+                           0, stream, p);
+    } else {
+        hipLaunchKernelGGL((kda_recurrent_kernel<DK, DV, kRecThreads, Tin, 16, true>), grid, block,
+                           0, stream, p);
+    }
+    return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+template <int DK, int DV>
+static kda_status launch_rec_dt(const RecParams &p, kda_dtype dt, bool verify, hipStream_t s) {
+    return dt == KDA_BF16 ? launch_rec_typed<DK, DV, uint16_t>(p, verify, s)
+                          : launch_rec_typed<DK, DV, float>(p, verify, s);
+}
+
+kda_status launch_recurrent(const RecParams &p, int d_k, int d_v, kda_dtype dt, bool verify,
+                            hipStream_t stream) {
+    if (p.B == 0) return KDA_OK;
+    if (d_k == 128 && d_v == 128) return launch_rec_dt<128, 128>(p, dt, verify, stream);
+    if (d_k == 64 && d_v == 64) return launch_rec_dt<64, 64>(p, dt, verify, stream);
+    if (d_k == 128 && d_v == 64) return launch_rec_dt<128, 64>(p, dt, verify, stream);
+    if (d_k == 64 && d_v == 128) return launch_rec_dt<64, 128>(p, dt, verify, stream);
+    return KDA_ERR_UNSUPPORTED;
+}
+
+kda_status launch_commit(const CommitParams &p, hipStream_t stream) {
+    if (p.B == 0) return KDA_OK;
+    hipLaunchKernelGGL(kda_commit_kernel, dim3((unsigned)(p.B * p.H)), dim3(256), 0, stream, p);
+    return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+}  // namespace kda

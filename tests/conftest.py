@@ -18,3 +18,17 @@ def oracle_c():
     from oracle import kda_oracle
     kda_oracle.lib()
     return kda_oracle
+
+
+def pytest_collection_modifyitems(config, items):
+    """GPU tests need a GPU; without one (e.g. the CPU container) they are
+    skipped.  With a GPU present a missing libkda.so fails them loudly."""
+    if not any("gpu" in item.keywords for item in items):
+        return
+    import torch
+    if torch.cuda.is_available():
+        return
+    skip = pytest.mark.skip(reason="no GPU in this process")
+    for item in items:
+        if "gpu" in item.keywords:
+            item.add_marker(skip)
