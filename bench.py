@@ -1,0 +1,324 @@
+"""Benchmark of the KDA recurrent-state hot path on one MI355X.
+
+A step is one kda_decode launch over the batched decode workload (B = 64
+sequences, H = 32 heads, d_k = d_v = 128, bf16 inputs, fp32 states in a
+1024-slot pool addressed by a random slot table): slot resolution, conv +
+SiLU, L2 norms, gates, the state read / delta update / write, RMSNorm and the
+output gate.  Inputs for every step are resident in HBM before timing starts.
+
+Prints ONE JSON line: the metric (token·heads/s), the roofline object of the
+decode kernel (algorithmic bytes per launch over the mean launch duration from
+HIP events on the launch stream), the fp64 oracle timed on the host cores on a
+bounded sample, and side measurements (MALL-defeating cold variant, copy
+ceiling, spec-verify/commit, chunked prefill).
+
+  python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--no-cpu-baseline]
+                  [--no-extras]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "KDA decode state updates/s (token·heads/s) + achieved HBM GB/s at B=64"
+
+# algorithmic bytes per (token, head) of one decode step at H=32, d_k=d_v=128,
+# bf16 inputs, B=64 (shared per-head parameters amortised over the batch)
+def decode_bytes_per_token_head(H=32, dk=128, dv=128, B=64, in_bytes=2):
+    ch = 2 * dk + dv
+    state = 2 * dk * dv * 4                      # read + write
+    inputs = (3 * dk + 2 * dv) * in_bytes + in_bytes   # x_q, x_k, g, x_v, z + b
+    window = 2 * 3 * ch * in_bytes               # read + write
+    out = dv * 4
+    params = (dk + ch * 4 + dv) * 4 / B          # A, conv_wt, norm_w per head / B
+    return state + inputs + window + out + params
+
+
+def verify_bytes_per_seq_head(T=8, dk=128, dv=128, B=16, in_bytes=2):
+    ch = 2 * dk + dv
+    return (dk * dv * 4 + 3 * ch * in_bytes                  # S0 + window read
+            + T * ((3 * dk + 2 * dv) * in_bytes + in_bytes)   # inputs
+            + T * (dk * dv * 4 + 3 * ch * in_bytes)           # snapshots
+            + T * dv * 4                                      # outputs
+            + (dk + ch * 4 + dv) * 4 / B)                     # params
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "linear_attention_recurrent_kda_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".h")):
+            h.update(open(os.path.join(d, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after the timed region, run one plain copy of this many MiB "
+                         "(a known-size kernel for calibrating memory counters)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build measures one GPU; the KDA path has no cross-GPU exchange "
+              "(heads and sequences shard with no collective), so --gpus must be 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from linear_attention_recurrent_kda_amd import api, synth
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    cfg = synth.WORKLOADS["decode_b64"]
+    B, H, dk, dv, n_slots = cfg["B"], cfg["H"], cfg["d_k"], cfg["d_v"], cfg["n_slots"]
+    K, W = args.steps, args.warmup
+    g = synth.rng(cfg["seed"])
+    p = synth.layer_params(g, H, dk, dv)
+    td = lambda a, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(dt)
+    layer = api.Layer(td(p["A"]), td(p["conv_wt"]), td(p["norm_w"]))
+    # pools: 2 GiB of fp32 state; slots not in the table hold seeded values
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(cfg["seed"])
+    state = (torch.randn((n_slots, H, dk, dv), generator=gen, device=dev) * 0.05)
+    win = torch.randn((n_slots, H, 3, 2 * dk + dv), generator=gen, device=dev).to(torch.bfloat16)
+    cache = api.Cache(state, win, torch.zeros(1, dtype=torch.int32, device=dev))
+    slots = td(synth.slot_table(g, B, n_slots), torch.int32)
+    # inputs of every step, resident in HBM before timing
+    nsteps = W + K
+    inp = synth.token_inputs(g, (nsteps, B), H, dk, dv, "bf16")
+    dinp = {k: td(v, torch.bfloat16) for k, v in inp.items()}
+    step_inputs = [api.Inputs(*(dinp[k][t] for k in ("x_q", "x_k", "x_v", "g", "b", "z")))
+                   for t in range(nsteps)]
+    y = torch.empty((B, H, dv), device=dev)
+    stream = torch.cuda.current_stream()
+    # every launch's arguments are marshalled before timing starts
+    calls = [api.kda_decode_prepared(layer, cache, slots, step_inputs[t], y) for t in range(nsteps)]
+
+    for t in range(W):
+        calls[t]()
+    torch.cuda.synchronize()
+    # timed region: K back-to-back launches between two events on the launch
+    # stream; the mean launch duration is their span / K (launch gaps included)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(K):
+        calls[W + i]()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    mean_kern_s = e0.elapsed_time(e1) / 1e3 / K
+    bytes_launch = decode_bytes_per_token_head(H, dk, dv, B) * B * H
+    achieved = bytes_launch / mean_kern_s / 1e9
+    value = B * H * K / wall
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "token·heads/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": wall / K * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "decode_b64", "B": B, "H": H, "d_k": dk, "d_v": dv,
+                   "n_slots": n_slots, "input_dtype": "bf16", "state_dtype": "f32",
+                   "seed": cfg["seed"], "parallelism": "single-gpu"},
+        "achieved_gbs_wall": bytes_launch * K / wall / 1e9,
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": None,
+            "kernel": "kda_recurrent_kernel<128,128,256,bf16,1,decode>",
+            "bytes_per_launch": bytes_launch,
+            "mean_launch_us": mean_kern_s * 1e6,
+        },
+    }
+    traffic = load_traffic()
+    if traffic is not None:
+        # counter bytes per launch over the same mean launch duration (GB/s)
+        out["roofline"]["traffic"] = traffic / mean_kern_s / 1e9
+        out["roofline"]["traffic_bytes_per_launch"] = traffic
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        api.kda_copy_probe(dst, src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    if not args.no_extras:
+        out["extras"] = extras(torch, api, synth, layer, cache, step_inputs, y, slots, B, H, dk, dv,
+                               n_slots, W, K, stream)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(synth, p, inp, B, H, dk, dv)
+    print(json.dumps(out), flush=True)
+
+
+def load_traffic():
+    """HBM bytes per launch of the decode kernel from the committed rocprofv3
+    counter summary, if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "decode_b64_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def timed(torch, stream, fn, reps):
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    fn()
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(reps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / 1e3 / reps
+
+
+def extras(torch, api, synth, layer, cache, step_inputs, y, slots, B, H, dk, dv, n_slots, W, K, stream):
+    ex = {}
+    # cold variant: 16 disjoint 64-slot sets rotated per step (2 GiB working
+    # set, larger than the 256 MB Infinity Cache)
+    perm = torch.from_numpy(np.random.default_rng(7).permutation(n_slots).astype(np.int32)).to("cuda:0")
+    sets = perm.reshape(n_slots // B, B)
+    nrot = sets.shape[0]
+    steps = min(K, len(step_inputs) - W)
+    warm = [api.kda_decode_prepared(layer, cache, sets[t], step_inputs[t % len(step_inputs)], y)
+            for t in range(nrot)]
+    calls = [api.kda_decode_prepared(layer, cache, sets[i % nrot], step_inputs[W + i], y)
+             for i in range(steps)]
+    for c in warm:
+        c()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for c in calls:
+        c()
+    b.record(stream)
+    torch.cuda.synchronize()
+    s = a.elapsed_time(b) / 1e3 / steps
+    bl = decode_bytes_per_token_head(H, dk, dv, B) * B * H
+    ex["decode_b64_cold"] = {"us_per_step": s * 1e6, "token_heads_per_s": B * H / s,
+                             "algorithmic_gbs": bl / s / 1e9, "frac_of_8tbs": bl / s / 8e12}
+    # copy ceiling (1 GiB each way)
+    n = 1 << 28
+    src = torch.empty(n, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    dst = torch.empty_like(src)
+    s = timed(torch, stream, lambda: api.kda_copy_probe(dst, src), 10)
+    ex["copy_probe_1gib"] = {"gbs": 2 * n * 4 / s / 1e9, "us": s * 1e6}
+    del src, dst
+    # spec-verify B=16 x T=8 and commit
+    cfg = synth.WORKLOADS["spec_verify_b16_t8"]
+    Bv, T = cfg["B"], cfg["T"]
+    g = synth.rng(cfg["seed"])
+    vin = synth.token_inputs(g, (Bv, T), H, dk, dv, "bf16")
+    td = lambda a, dt=torch.bfloat16: torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0").to(dt)
+    vinp = api.Inputs(*(td(vin[k]) for k in ("x_q", "x_k", "x_v", "g", "b", "z")))
+    live = slots[:Bv].contiguous()
+    rest = torch.from_numpy(np.setdiff1d(np.arange(n_slots), slots.cpu().numpy())[:Bv * T]
+                            .astype(np.int32)).to("cuda:0").reshape(Bv, T)
+    yv = torch.empty((Bv, T, H, dv), device="cuda:0")
+    acc = td(synth.accepted_lengths(g, Bv, T), torch.int32)
+    sv = timed(torch, stream, lambda: api.kda_spec_verify(layer, cache, live, rest, vinp, yv), 20)
+    sc = timed(torch, stream, lambda: api.kda_spec_commit(layer, cache, live, rest, acc), 20)
+    vb = verify_bytes_per_seq_head(T, dk, dv, Bv) * Bv * H
+    Lm = float(acc.float().mean().item())
+    cb = Bv * H * (dk * dv * 4 + 3 * (2 * dk + dv) * 2) * 2
+    ex["spec_verify_b16_t8"] = {"us_per_call": sv * 1e6, "token_heads_per_s": Bv * T * H / sv,
+                                "algorithmic_gbs": vb / sv / 1e9, "frac_of_8tbs": vb / sv / 8e12}
+    ex["spec_commit_b16"] = {"us_per_call": sc * 1e6, "mean_accepted": Lm,
+                             "algorithmic_gbs": cb / sc / 1e9}
+    ex["chunk_prefill_t32k"] = prefill_extra(torch, api, synth, stream)
+    return ex
+
+
+def prefill_extra(torch, api, synth, stream):
+    cfg = synth.WORKLOADS["prefill_t32k"]
+    H, dk, dv, T = cfg["H"], cfg["d_k"], cfg["d_v"], cfg["T"]
+    g = synth.rng(cfg["seed"])
+    p = synth.layer_params(g, H, dk, dv)
+    td = lambda a, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0").to(dt)
+    layer = api.Layer(td(p["A"]), td(p["conv_wt"]), td(p["norm_w"]))
+    inp = synth.token_inputs(g, (T,), H, dk, dv, "bf16")
+    I = api.Inputs(*(td(inp[k], torch.bfloat16) for k in ("x_q", "x_k", "x_v", "g", "b", "z")))
+    cache = api.Cache(torch.zeros((1, H, dk, dv), device="cuda:0"),
+                      torch.zeros((1, H, 3, 2 * dk + dv), dtype=torch.bfloat16, device="cuda:0"))
+    sl = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    cu = torch.tensor([0, T], dtype=torch.int32, device="cuda:0")
+    y = torch.empty((T, H, dv), device="cuda:0")
+    try:
+        ws_n = api.kda_chunk_prefill_workspace_bytes(layer, T, 1)
+        ws = torch.empty(max(ws_n, 16), dtype=torch.uint8, device="cuda:0")
+        run = lambda: api.kda_chunk_prefill(layer, cache, sl, cu, I, y, ws)
+        run()
+    except api.KdaError as e:
+        return {"status": e.status}
+    s = timed(torch, stream, run, 5)
+    in_b = T * H * ((3 * dk + 2 * dv) * 2 + 2)
+    out_b = T * H * dv * 4
+    st_b = 2 * H * dk * dv * 4
+    tot = in_b + out_b + st_b
+    return {"us_per_call": s * 1e6, "tokens_per_s": T / s, "token_heads_per_s": T * H / s,
+            "algorithmic_gbs": tot / s / 1e9, "frac_of_8tbs": tot / s / 8e12,
+            "workspace_bytes": ws_n}
+
+
+def cpu_baseline(synth, p, inp, B, H, dk, dv):
+    """The fp64 oracle (as it is, untuned) on the host cores: a bounded sample
+    of the same workload (all 64 sequences x 32 heads, a few steps)."""
+    from oracle import kda_oracle
+    from oracle.kda_oracle_np import Layer as OLayer
+    ol = OLayer(p["A"], p["conv_wt"], p["norm_w"])
+    cores = kda_oracle.threads(0)
+    tb = {k: np.ascontiguousarray(np.swapaxes(v, 0, 1), dtype=np.float64)
+          for k, v in inp.items()}                              # [B, steps, ...]
+    st = np.zeros((B, H, dk, dv))
+    win = np.zeros((B, H, 3, 2 * dk + dv))
+    n, el, runs = tb["x_q"].shape[1], 0.0, 0
+    # repeat the staged steps (carrying the state) until ~10 s of oracle work
+    while el < 10.0 and runs < 200:
+        t0 = time.perf_counter()
+        o = kda_oracle.run(ol, st, win, tb["x_q"], tb["x_k"], tb["x_v"], tb["g"], tb["b"], tb["z"])
+        el += time.perf_counter() - t0
+        st, win, runs = o["state"], o["window"], runs + 1
+    return {"value": B * H * n * runs / el, "unit": "token·heads/s", "cores": cores, "kind": "oracle",
+            "sample": f"decode_b64: {runs} x {n} steps x {B} sequences x {H} heads (fp64, OpenMP "
+                      f"over sequence x head), {el:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -160,6 +160,33 @@ def kda_decode(layer: Layer, cache: Cache, slot_idx: torch.Tensor, inputs: Input
                                                 B, ctypes.byref(I), y.data_ptr(), _stream(stream)))
 
 
+def kda_decode_prepared(layer: Layer, cache: Cache, slot_idx: torch.Tensor, inputs: Inputs,
+                        y: torch.Tensor, stream=None):
+    """Check and marshal the arguments of one kda_decode call once; return a
+    zero-argument callable that issues exactly that call (for launch loops
+    where per-call Python overhead would leave the GPU idle).  The callable
+    keeps the tensors alive; it raises KdaError on a non-OK status."""
+    _check(slot_idx, "slot_idx", torch.int32)
+    B = slot_idx.numel()
+    _check(y, "y", torch.float32)
+    if tuple(y.shape) != (B, layer.H, layer.d_v):
+        raise ValueError("y must be [B, H, d_v]")
+    L, C, I = layer.c_struct(), cache.c_struct(layer), inputs.c_struct(layer, (B,))
+    if cache.conv_state.dtype != inputs.dtype:
+        raise TypeError("conv_state dtype must equal the input dtype")
+    fn = _lib.load().kda_decode
+    args = (ctypes.byref(L), ctypes.byref(C), slot_idx.data_ptr(), B, ctypes.byref(I),
+            y.data_ptr(), _stream(stream))
+    keep = (L, C, I, layer, cache, slot_idx, inputs, y)
+
+    def call():
+        rc = fn(*args)
+        if rc:
+            raise KdaError("kda_decode", rc)
+    call.keep = keep
+    return call
+
+
 def kda_spec_verify(layer: Layer, cache: Cache, slot_idx: torch.Tensor, snap_slots: torch.Tensor,
                     inputs: Inputs, y: torch.Tensor, draft_len: Optional[torch.Tensor] = None,
                     stream=None) -> None:
