@@ -1,0 +1,193 @@
+"""GPU parity of kda_chunk_prefill against the token-by-token fp64 oracle:
+brute force on small sizes (chunk boundaries, partial chunks, T = 1), several
+packed sequences with their own start states and windows, prefill followed
+by decode, the full 32768-token workload on sampled heads, error handling."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import DEV, TOL, host, layer_pair, new_cache, parity_error, state_rel_err, tdt, to_dev
+from linear_attention_recurrent_kda_amd import api, synth
+from oracle import kda_oracle
+
+pytestmark = pytest.mark.gpu
+
+KEYS = ("x_q", "x_k", "x_v", "g", "b", "z")
+
+
+def dev_inputs(inp, dtype):
+    return api.Inputs(*(to_dev(inp[k], tdt(dtype)) for k in KEYS))
+
+
+def run_prefill(dl, cache, slots, lens, inp, dtype):
+    """inp arrays are packed [total_T, H, .]; lens per sequence."""
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    total = int(cu[-1])
+    y = torch.full((total, dl.H, dl.d_v), 7.0, device=DEV)
+    api.kda_chunk_prefill(dl, cache, torch.from_numpy(np.asarray(slots, np.int32)).to(DEV),
+                          torch.from_numpy(cu).to(DEV), dev_inputs(inp, dtype), y)
+    torch.cuda.synchronize()
+    return host(y), cu
+
+
+def oracle_seq(ol, s0, w0, inp, a, b, y_tokens=None):
+    """Oracle over packed tokens [a, b) as one sequence."""
+    sub = {k: v[None, a:b] for k, v in inp.items()}
+    return kda_oracle.run(ol, s0[None], w0[None], sub["x_q"], sub["x_k"], sub["x_v"], sub["g"],
+                          sub["b"], sub["z"], y_tokens=y_tokens)
+
+
+def check_tokens(y_gpu, y_orc):
+    """Per-token check: max |d| over the token's H x d_v outputs <= TOL x RMS."""
+    errs = [parity_error(y_gpu[t], y_orc[t]) for t in range(y_gpu.shape[0])]
+    if not errs:
+        return 0.0
+    worst = int(np.argmax(errs))
+    print(f"  prefill parity: worst token {worst} max|d|/RMS = {errs[worst]:.3e}", flush=True)
+    assert errs[worst] <= TOL, f"token {worst}: {errs[worst]:.3e}"
+    return errs[worst]
+
+
+@pytest.mark.parametrize("T", [1, 2, 63, 64, 65, 130, 257])
+def test_single_sequence_brute_force(T):
+    g = synth.rng(900 + T)
+    H, dk, dv = 4, 128, 128
+    params = synth.layer_params(g, H, dk, dv)
+    dl, ol = layer_pair(params)
+    inp = synth.token_inputs(g, (T,), H, dk, dv, "bf16")
+    s0 = synth.random_state(g, (H, dk, dv), 0.2)
+    w0 = synth.window_inputs(g, (), H, dk, dv, "bf16")
+    cache = new_cache(3, H, dk, dv, "bf16", fill_seed=1)
+    cache.state[1] = torch.from_numpy(s0).to(DEV)
+    cache.conv_state[1] = to_dev(w0, torch.bfloat16)
+    other = cache.state[[0, 2]].clone()
+    y, _ = run_prefill(dl, cache, [1], [T], inp, "bf16")
+    o = oracle_seq(ol, s0, w0, inp, 0, T)
+    check_tokens(y, o["y"][0])
+    assert state_rel_err(host(cache.state[1:2]), o["state"]) < 1e-4
+    assert np.array_equal(host(cache.conv_state[1:2]), o["window"])
+    assert torch.equal(cache.state[[0, 2]], other)
+    assert cache.err_flag.item() == 0
+
+
+@pytest.mark.parametrize("dk,dv,dtype", [(64, 64, "f32"), (64, 128, "bf16"), (128, 64, "bf16")])
+def test_other_head_sizes(dk, dv, dtype):
+    g = synth.rng(950 + dk + dv)
+    H, T = 2, 150
+    params = synth.layer_params(g, H, dk, dv)
+    dl, ol = layer_pair(params)
+    inp = synth.token_inputs(g, (T,), H, dk, dv, dtype)
+    cache = new_cache(2, H, dk, dv, dtype)
+    y, _ = run_prefill(dl, cache, [1], [T], inp, dtype)
+    o = oracle_seq(ol, np.zeros((H, dk, dv)), np.zeros((H, 3, 2 * dk + dv)), inp, 0, T)
+    check_tokens(y, o["y"][0])
+    assert state_rel_err(host(cache.state[1:2]), o["state"]) < 1e-4
+
+
+def test_packed_sequences_with_padding():
+    """Four packed sequences (lengths 70, 0, 2, 129) with their own start
+    states and windows, one padding row (-1), slots in permuted order."""
+    g = synth.rng(970)
+    H, dk, dv = 3, 128, 128
+    params = synth.layer_params(g, H, dk, dv)
+    dl, ol = layer_pair(params)
+    lens = [70, 0, 2, 129, 5]
+    slots = [4, 0, 2, 1, -1]
+    total = sum(lens)
+    inp = synth.token_inputs(g, (total,), H, dk, dv, "bf16")
+    cache = new_cache(6, H, dk, dv, "bf16", fill_seed=2)
+    s_before = host(cache.state)
+    w_before = host(cache.conv_state)
+    y, cu = run_prefill(dl, cache, slots, lens, inp, "bf16")
+    assert cache.err_flag.item() == 0
+    for i, (sl, ln) in enumerate(zip(slots, lens)):
+        a, b = cu[i], cu[i + 1]
+        if sl < 0:
+            assert np.all(y[a:b] == 0.0)
+            continue
+        o = oracle_seq(ol, s_before[sl], w_before[sl], inp, a, b)
+        check_tokens(y[a:b], o["y"][0])
+        assert state_rel_err(host(cache.state[sl:sl + 1]), o["state"]) < 1e-4
+        assert np.array_equal(host(cache.conv_state[sl:sl + 1]), o["window"])
+    # slots nobody named are untouched
+    assert np.array_equal(host(cache.state[[3, 5]]), s_before[[3, 5]])
+
+
+def test_prefill_then_decode_continues_the_sequence():
+    g = synth.rng(980)
+    H, dk, dv, T, D = 4, 128, 128, 100, 20
+    params = synth.layer_params(g, H, dk, dv)
+    dl, ol = layer_pair(params)
+    inp = synth.token_inputs(g, (T + D,), H, dk, dv, "bf16")
+    cache = new_cache(2, H, dk, dv, "bf16")
+    pre = {k: v[:T] for k, v in inp.items()}
+    y_pre, _ = run_prefill(dl, cache, [1], [T], pre, "bf16")
+    slot = torch.tensor([1], dtype=torch.int32, device=DEV)
+    ys = []
+    for t in range(T, T + D):
+        I = api.Inputs(*(to_dev(inp[k][t:t + 1], torch.bfloat16) for k in KEYS))
+        y = torch.empty((1, H, dv), device=DEV)
+        api.kda_decode(dl, cache, slot, I, y)
+        ys.append(host(y)[0])
+    o = oracle_seq(ol, np.zeros((H, dk, dv)), np.zeros((H, 3, 2 * dk + dv)), inp, 0, T + D)
+    check_tokens(y_pre, o["y"][0, :T])
+    check_tokens(np.stack(ys), o["y"][0, T:])
+
+
+def test_full_length_32k_sampled():
+    """The long-prompt workload at full size: B=1, T=32768, H=32, d=128.
+    All heads checked on the first 2048 tokens; 4 sampled heads checked over
+    all 32768 tokens (outputs of the last chunk, final state)."""
+    cfg = synth.WORKLOADS["prefill_t32k"]
+    g = synth.rng(cfg["seed"])
+    H, dk, dv, T = cfg["H"], cfg["d_k"], cfg["d_v"], cfg["T"]
+    params = synth.layer_params(g, H, dk, dv)
+    dl, ol = layer_pair(params)
+    inp = synth.token_inputs(g, (T,), H, dk, dv, "bf16")
+    cache = new_cache(1, H, dk, dv, "bf16")
+    print("  running prefill on the GPU", flush=True)
+    y, _ = run_prefill(dl, cache, [0], [T], inp, "bf16")
+    print("  oracle: all heads, first 2048 tokens", flush=True)
+    z0, w0 = np.zeros((H, dk, dv)), np.zeros((H, 3, 2 * dk + dv))
+    o = oracle_seq(ol, z0, w0, inp, 0, 2048)
+    check_tokens(y[:2048], o["y"][0])
+    heads = [0, 9, 22, 31]
+    print("  oracle: 4 heads, all tokens", flush=True)
+    sub = {k: v[:, heads] for k, v in inp.items()}
+    o2 = oracle_seq(ol.heads(heads), z0[heads], w0[heads], sub, 0, T)
+    check_tokens(y[-64:, heads], o2["y"][0, -64:])
+    err = state_rel_err(host(cache.state[0:1, heads]), o2["state"])
+    print(f"  final state rel err (4 heads) {err:.3e}", flush=True)
+    assert err < 1e-3
+
+
+def test_invalid_cu_seqlens_flags_and_leaves_state():
+    g = synth.rng(990)
+    H, dk, dv = 2, 64, 64
+    params = synth.layer_params(g, H, dk, dv)
+    dl, _ = layer_pair(params)
+    inp = synth.token_inputs(g, (10,), H, dk, dv, "bf16")
+    cache = new_cache(3, H, dk, dv, "bf16", fill_seed=3)
+    before = cache.state.clone()
+    y = torch.full((10, H, dv), 5.0, device=DEV)
+    bad_cu = torch.tensor([0, 7, 4, 10], dtype=torch.int32, device=DEV)
+    api.kda_chunk_prefill(dl, cache, torch.tensor([0, 1, 2], dtype=torch.int32, device=DEV),
+                          bad_cu, dev_inputs(inp, "bf16"), y)
+    torch.cuda.synchronize()
+    assert cache.err_flag.item() == 1
+    assert torch.equal(cache.state, before)
+    assert torch.count_nonzero(y) == 0
+
+
+def test_prefill_deterministic():
+    g = synth.rng(995)
+    H, dk, dv, T = 4, 128, 128, 200
+    params = synth.layer_params(g, H, dk, dv)
+    dl, _ = layer_pair(params)
+    inp = synth.token_inputs(g, (T,), H, dk, dv, "bf16")
+    outs = []
+    for _ in range(2):
+        cache = new_cache(1, H, dk, dv, "bf16")
+        y, _ = run_prefill(dl, cache, [0], [T], inp, "bf16")
+        outs.append((y, host(cache.state)))
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
