@@ -43,3 +43,42 @@ __device__ __forceinline__ void flag_error(int32_t *err_flag) {
 }
 
 }  // namespace kda
+
+// ---------------------------------------------------------------------------
+// MFMA helpers (gfx950, v_mfma_f32_16x16x32_bf16).  Lane l of a wave holds
+//   A operand: A[l % 16][8 (l / 16) + e], e < 8    (16 x 32 tile)
+//   B operand: B[8 (l / 16) + e][l % 16], e < 8    (32 x 16 tile)
+//   result   : D[4 (l / 16) + r][l % 16], r < 4    (16 x 16 fp32)
+// "bf16x3": an fp32 operand x is split as hi = bf16(x), lo = bf16(x - hi);
+// a.b ~ ah.bh + ah.bl + al.bh keeps about 16 significant bits per operand
+// (relative error ~1e-5), with fp32 accumulation.
+// ---------------------------------------------------------------------------
+namespace kda {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+struct Split8 {
+    bf16x8 hi, lo;
+};
+
+__device__ __forceinline__ Split8 split8(const float *x, float sign = 1.0f) {
+    Split8 s;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float v = sign * x[e];
+        const __bf16 h = (__bf16)v;
+        s.hi[e] = h;
+        s.lo[e] = (__bf16)(v - (float)h);
+    }
+    return s;
+}
+
+__device__ __forceinline__ f32x4 mma3(const Split8 &a, const Split8 &b, f32x4 acc) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.hi, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.lo, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.lo, b.hi, acc, 0, 0, 0);
+    return acc;
+}
+
+}  // namespace kda

@@ -177,22 +177,39 @@ __global__ __launch_bounds__(256) void kda_prefill_prep_kernel(PrefillParams p, 
 }
 
 // ---------------------------------------------------------------------------
-// intra: one workgroup (256 lanes) per (chunk, head)
+// intra: one workgroup (4 waves) per (chunk, head).  The Gram matrices A, P,
+// the triangular inverse T = (I + A)^-1 and [W | U~] = T [diag(beta) K^ e^G |
+// diag(beta) V] are formed here; every contraction runs on MFMA in bf16x3.
+//
+// Gram tiles are 16 x 16 token blocks.  For a t-block starting at token r,
+// e^(G_t - G_s) = e^(G_t - G_r) e^(G_r - G_s): the first factor is <= 1 for
+// t >= r and the second is <= 1 for s < r, so an off-diagonal tile is a plain
+// product of two scaled operands.  In a diagonal tile s >= r makes the second
+// factor >= 1; it is used only when the block's decay span is at most 2^60
+// (checked per block), otherwise the tile is summed directly with one
+// exponential per term.
 // ---------------------------------------------------------------------------
 template <int DK, int DV>
 struct __align__(16) IntraLds {
-    static constexpr int DM = DK > DV ? DK : DV;
-    float G[kChunk][DK];        // log2-decay prefix sums
-    float k[kChunk][DK];        // k^, later the W right-hand side / solution
-    float q[kChunk][DM];        // q^, later beta v / U~ (row stride DV then)
-    float A[kChunk][kChunk + 1];
+    static constexpr int QW = DK >= 68 ? DK : 68;
+    float q[kChunk][QW];           // q^, later T = (I + A)^-1
+    float k[kChunk][DK];           // k^
+    float G[kChunk][DK];           // log2-decay prefix sums
+    float A[kChunk][kChunk + 1];   // beta_t (K K^T * decay), strictly lower part used
+    float Z[3][16][17];            // block-inverse scratch
+    float D[4][16][17];            // per-wave scratch of the direct tile path
     float beta[kChunk];
+    int safe[4];
 };
+
+constexpr float kSafeSpan = 60.f;
 
 template <int DK, int DV>
 __global__ __launch_bounds__(256) void kda_prefill_intra_kernel(PrefillParams p, PrefillWs ws) {
+    constexpr int KS = DK / 32, QW = IntraLds<DK, DV>::QW;
     __shared__ IntraLds<DK, DV> L;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int lr = lane % 16, lk = lane / 16;
     const int gidx = blockIdx.x, h = blockIdx.y, H = p.H;
     if (ws.meta[0] != 1) return;
     const int32_t *cs = ws.meta + 1;
@@ -202,15 +219,21 @@ __global__ __launch_bounds__(256) void kda_prefill_intra_kernel(PrefillParams p,
     const int c = gidx - cs[s];
     const int t0 = p.cu_seqlens[s] + c * kChunk;
     const int n = min(kChunk, p.cu_seqlens[s + 1] - t0);
+    const size_t gh = (size_t)gidx * H + h;
 
-    // 1. load k^, q^, log2 alpha, beta of the chunk (rows >= n are zero)
-    for (int e = tid; e < kChunk * DK; e += 256) {
-        const int r = e / DK, i = e % DK;
-        const bool in = r < n;
-        const size_t src = ((size_t)(t0 + r) * H + h) * DK + i;
-        L.k[r][i] = in ? ws.kh[src] : 0.f;
-        L.q[r][i] = in ? ws.qh[src] : 0.f;
-        L.G[r][i] = in ? ws.la[src] : 0.f;
+    // 1. k^, q^, log2 alpha, beta of the chunk (rows >= n are zero)
+    for (int e = tid; e < kChunk * DK / 4; e += 256) {
+        const int r = e / (DK / 4), i = 4 * (e % (DK / 4));
+        float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), qv = kv, gv = kv;
+        if (r < n) {
+            const size_t src = ((size_t)(t0 + r) * H + h) * DK + i;
+            kv = *reinterpret_cast<const float4 *>(ws.kh + src);
+            qv = *reinterpret_cast<const float4 *>(ws.qh + src);
+            gv = *reinterpret_cast<const float4 *>(ws.la + src);
+        }
+        *reinterpret_cast<float4 *>(&L.k[r][i]) = kv;
+        *reinterpret_cast<float4 *>(&L.q[r][i]) = qv;
+        *reinterpret_cast<float4 *>(&L.G[r][i]) = gv;
     }
     if (tid < kChunk) L.beta[tid] = tid < n ? ws.beta[(size_t)(t0 + tid) * H + h] : 0.f;
     __syncthreads();
@@ -220,91 +243,234 @@ __global__ __launch_bounds__(256) void kda_prefill_intra_kernel(PrefillParams p,
         for (int r = 0; r < kChunk; ++r) { acc += L.G[r][tid]; L.G[r][tid] = acc; }
     }
     __syncthreads();
-    // 3. A (s < t) and P (s <= t), 4x4 tiles of (t, s) per lane, lower tiles only
-    float *P = ws.P + ((size_t)gidx * H + h) * kChunk * kChunk;
-    for (int tile = tid; tile < 256; tile += 256) {
-        const int ti = tile / 16, si = tile % 16;
-        float a[4][4] = {}, pq[4][4] = {};
-        if (si <= ti) {
-            for (int i = 0; i < DK; ++i) {
-                float gt[4], kt[4], qt[4], gs[4], ks[4];
+    // 3. per 16-token block: may the diagonal tile use the scaled factors?
+    {
+        float span = 0.f;
+        for (int i = lane; i < DK; i += kWave) span = fmaxf(span, L.G[16 * wave][i] - L.G[16 * wave + 15][i]);
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    gt[u] = L.G[4 * ti + u][i]; kt[u] = L.k[4 * ti + u][i]; qt[u] = L.q[4 * ti + u][i];
-                    gs[u] = L.G[4 * si + u][i]; ks[u] = L.k[4 * si + u][i];
-                }
-#pragma unroll
-                for (int u = 0; u < 4; ++u)
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        // only s <= t is used; clamp the exponent so unused
-                        // entries (s > t) stay finite
-                        const float e = exp2f(fminf(gt[u] - gs[v], 0.f)) * ks[v];
-                        a[u][v] = fmaf(kt[u], e, a[u][v]);
-                        pq[u][v] = fmaf(qt[u], e, pq[u][v]);
-                    }
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int t = 4 * ti + u, sv = 4 * si + v;
-                L.A[t][sv] = sv < t ? L.beta[t] * a[u][v] : 0.f;
-                P[t * kChunk + sv] = sv <= t ? pq[u][v] : 0.f;
-            }
+        for (int m = 32; m >= 1; m >>= 1) span = fmaxf(span, __shfl_xor(span, m, kWave));
+        if (lane == 0) L.safe[wave] = span <= kSafeSpan ? 1 : 0;
     }
     __syncthreads();
-    // 4. decayed factors for the state recurrence and the outputs
-    const size_t gh = (size_t)gidx * H + h;
+
+    // 4. A and P in 16 x 16 tiles; tile (bt, bs) covers t in block bt, s in block bs
+    float *Pg = ws.P + gh * kChunk * kChunk;
+    for (int tile = wave; tile < 16; tile += 4) {
+        const int bt = tile / 4, bs = tile % 4;
+        f32x4 aA = {0.f, 0.f, 0.f, 0.f}, aP = aA;
+        if (bs > bt) {
+            // above the diagonal: P is zero there (A is never read there)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) Pg[(16 * bt + 4 * lk + rr) * kChunk + 16 * bs + lr] = 0.f;
+            continue;
+        }
+        const int r = 16 * bt;
+        if (bs < bt || L.safe[bt]) {
+            const int t = 16 * bt + lr, sr = 16 * bs + lr;
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) {
+                float ka[8], qa[8], kb[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int ch = 32 * kk + 8 * lk + e;
+                    const float gr = L.G[r][ch];
+                    const float et = exp2f(L.G[t][ch] - gr);
+                    const float es = exp2f(gr - L.G[sr][ch]);
+                    ka[e] = L.k[t][ch] * et;
+                    qa[e] = L.q[t][ch] * et;
+                    kb[e] = L.k[sr][ch] * es;
+                }
+                const Split8 b = split8(kb);
+                aA = mma3(split8(ka), b, aA);
+                aP = mma3(split8(qa), b, aP);
+            }
+        } else {
+            // direct: lane owns row t = r + lr and columns s = r + 4 lk + j
+            float da[4] = {0.f, 0.f, 0.f, 0.f}, dp[4] = {0.f, 0.f, 0.f, 0.f};
+            const int t = r + lr;
+            for (int ch = 0; ch < DK; ++ch) {
+                const float gt = L.G[t][ch], kt = L.k[t][ch], qt = L.q[t][ch];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int sv = r + 4 * lk + j;
+                    const float e = exp2f(fminf(gt - L.G[sv][ch], 0.f)) * L.k[sv][ch];
+                    da[j] = fmaf(kt, e, da[j]);
+                    dp[j] = fmaf(qt, e, dp[j]);
+                }
+            }
+            // move to the MFMA result layout through this wave's scratch
+            // (the tile's block of A is written only by this wave)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                L.A[t][r + 4 * lk + j] = da[j];
+                L.D[wave][lr][4 * lk + j] = dp[j];
+            }
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                aA[rr] = L.A[r + 4 * lk + rr][r + lr];
+                aP[rr] = L.D[wave][4 * lk + rr][lr];
+            }
+            __builtin_amdgcn_wave_barrier();
+        }
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int t = 16 * bt + 4 * lk + rr, sv = 16 * bs + lr;
+            L.A[t][sv] = sv < t ? L.beta[t] * aA[rr] : 0.f;
+            Pg[t * kChunk + sv] = sv <= t ? aP[rr] : 0.f;
+        }
+    }
+    // 5. decayed factors for the scan: Q^ e^G, (K^ e^(G_C - G))^T, e^(G_C)
     const int last = max(n - 1, 0);
     for (int e = tid; e < kChunk * DK; e += 256) {
         const int r = e / DK, i = e % DK;
-        const float gl = L.G[last][i];
         ws.Qg[gh * kChunk * DK + r * DK + i] = L.q[r][i] * exp2f(L.G[r][i]);
-        ws.KdT[gh * DK * kChunk + i * kChunk + r] = L.k[r][i] * exp2f(fminf(gl - L.G[r][i], 0.f));
+    }
+    for (int e = tid; e < kChunk * DK; e += 256) {
+        const int i = e / kChunk, r = e % kChunk;
+        ws.KdT[gh * DK * kChunk + e] = L.k[r][i] * exp2f(fminf(L.G[last][i] - L.G[r][i], 0.f));
     }
     if (tid < DK) ws.gC[gh * DK + tid] = exp2f(L.G[last][tid]);
-    __syncthreads();   // q and G are free from here on
-    // 5. right-hand sides in place: k <- beta k e^G (for W), q <- beta v (for U~)
-    for (int e = tid; e < kChunk * DK; e += 256) {
-        const int r = e / DK, i = e % DK;
-        L.k[r][i] = L.beta[r] * L.k[r][i] * exp2f(L.G[r][i]);
-    }
-    for (int e = tid; e < kChunk * DV; e += 256) {
-        const int r = e / DV, j = e % DV;
-        reinterpret_cast<float *>(L.q)[r * DV + j] =
-            r < n ? L.beta[r] * ws.vv[((size_t)(t0 + r) * H + h) * DV + j] : 0.f;
-    }
+    __syncthreads();   // q^ is free from here on: T lives in its place
+
+    // 6. T = (I + A)^-1 by 16 x 16 blocks
+    float(*T)[QW] = L.q;
+    for (int e = tid; e < kChunk * kChunk; e += 256) T[e / kChunk][e % kChunk] = 0.f;
     __syncthreads();
-    // 6. forward substitution (I + A) X = R, in place, one lane per column
-    for (int col = tid; col < DK + DV; col += 256) {
-        float *x = col < DK ? &L.k[0][col] : reinterpret_cast<float *>(L.q) + (col - DK);
-        const int ld = col < DK ? DK : DV;
-        for (int t = 1; t < kChunk; ++t) {
-            float acc = x[t * ld];
-            for (int sv = 0; sv < t; ++sv) acc = fmaf(-L.A[t][sv], x[sv * ld], acc);
-            x[t * ld] = acc;
+    if (tid < 64) {   // diagonal blocks: column j of (I + A_bb)^-1
+        const int b = tid / 16, j = tid % 16, o = 16 * b;
+        float x[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float acc = i == j ? 1.f : 0.f;
+#pragma unroll
+            for (int m = 0; m < i; ++m) acc = fmaf(-L.A[o + i][o + m], x[m], acc);
+            x[i] = acc;
+            T[o + i][o + j] = i >= j ? acc : 0.f;
         }
     }
     __syncthreads();
-    for (int e = tid; e < kChunk * DK; e += 256)
-        ws.W[gh * kChunk * DK + e] = L.k[e / DK][e % DK];
-    for (int e = tid; e < kChunk * DV; e += 256)
-        ws.Ut[gh * kChunk * DV + e] = reinterpret_cast<float *>(L.q)[e];
+    for (int b = 1; b < 4; ++b) {
+        // Z_b' = sum_{b' <= m < b} A_bm T_mb'  for every b' < b
+        for (int e = tid; e < b * 256; e += 256) {
+            const int bp = e / 256, i = (e / 16) % 16, j = e % 16;
+            float acc = 0.f;
+            for (int m = 16 * bp; m < 16 * b; ++m) acc = fmaf(L.A[16 * b + i][m], T[m][16 * bp + j], acc);
+            L.Z[bp][i][j] = acc;
+        }
+        __syncthreads();
+        // T_bb' = -T_bb Z_b'
+        for (int e = tid; e < b * 256; e += 256) {
+            const int bp = e / 256, i = (e / 16) % 16, j = e % 16;
+            float acc = 0.f;
+#pragma unroll
+            for (int m = 0; m < 16; ++m) acc = fmaf(T[16 * b + i][16 * b + m], L.Z[bp][m][j], acc);
+            T[16 * b + i][16 * bp + j] = -acc;
+        }
+        __syncthreads();
+    }
+
+    // 7. [W | U~] = T R with R = [diag(beta) K^ e^G | diag(beta) V]  (MFMA)
+    Split8 ta[4][2];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = T[16 * rt + lr][32 * k2 + 8 * lk + e];
+            ta[rt][k2] = split8(x);
+        }
+    constexpr int NCT = (DK + DV) / 16;
+    for (int ct = wave; ct < NCT; ct += 4) {
+        const int col = 16 * ct + lr;
+        const bool isw = col < DK;
+        Split8 rb[2];
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int sv = 32 * k2 + 8 * lk + e;
+                if (isw) x[e] = L.beta[sv] * L.k[sv][col] * exp2f(L.G[sv][col]);
+                else x[e] = sv < n ? L.beta[sv] * ws.vv[((size_t)(t0 + sv) * H + h) * DV + (col - DK)] : 0.f;
+            }
+            rb[k2] = split8(x);
+        }
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            acc = mma3(ta[rt][0], rb[0], acc);
+            if (rt >= 2) acc = mma3(ta[rt][1], rb[1], acc);   // T is lower triangular
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int t = 16 * rt + 4 * lk + rr;
+                if (isw) ws.W[gh * kChunk * DK + t * DK + col] = acc[rr];
+                else ws.Ut[gh * kChunk * DV + t * DV + (col - DK)] = acc[rr];
+            }
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
-// scan: one workgroup per (sequence, head, 16 state columns)
+// scan: one workgroup (4 waves) per (sequence, head, 16 state columns).
+// Per chunk, wave w owns rows 16w..16w+15 of the chunk and state row tiles
+// TS*w .. TS*w+TS-1; all products run on MFMA in bf16x3 with fp32
+// accumulation.  The next chunk's operands are loaded while the current one
+// is computed (two register buffers).
 // ---------------------------------------------------------------------------
+template <int DK>
+struct ScanOps {
+    static constexpr int KS = DK / 32, TS = DK / 64;
+    float w[KS][8];        // W rows (A operand, K = d_k)
+    float q[KS][8];        // Q^ e^G rows
+    float pm[2][8];        // P rows (K = token)
+    float kd[TS][2][8];    // Kd^T rows (K = token)
+    float ut[4];           // U~ (result layout)
+    float gc[TS][4];       // e^(G_C) of the state rows this lane updates
+};
+
+template <int DK, int DV>
+__device__ __forceinline__ void scan_load(const PrefillWs &ws, size_t gh, int wave, int lr, int lk, int j0,
+                                          ScanOps<DK> &o) {
+    constexpr int KS = DK / 32, TS = DK / 64;
+    const float *W = ws.W + gh * kChunk * DK + (16 * wave + lr) * DK + 8 * lk;
+    const float *Q = ws.Qg + gh * kChunk * DK + (16 * wave + lr) * DK + 8 * lk;
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+        *reinterpret_cast<float4 *>(&o.w[k][0]) = *reinterpret_cast<const float4 *>(W + 32 * k);
+        *reinterpret_cast<float4 *>(&o.w[k][4]) = *reinterpret_cast<const float4 *>(W + 32 * k + 4);
+        *reinterpret_cast<float4 *>(&o.q[k][0]) = *reinterpret_cast<const float4 *>(Q + 32 * k);
+        *reinterpret_cast<float4 *>(&o.q[k][4]) = *reinterpret_cast<const float4 *>(Q + 32 * k + 4);
+    }
+    const float *P = ws.P + gh * kChunk * kChunk + (16 * wave + lr) * kChunk + 8 * lk;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        *reinterpret_cast<float4 *>(&o.pm[k][0]) = *reinterpret_cast<const float4 *>(P + 32 * k);
+        *reinterpret_cast<float4 *>(&o.pm[k][4]) = *reinterpret_cast<const float4 *>(P + 32 * k + 4);
+    }
+#pragma unroll
+    for (int m = 0; m < TS; ++m) {
+        const float *K = ws.KdT + gh * DK * kChunk + (16 * (TS * wave + m) + lr) * kChunk + 8 * lk;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            *reinterpret_cast<float4 *>(&o.kd[m][k][0]) = *reinterpret_cast<const float4 *>(K + 32 * k);
+            *reinterpret_cast<float4 *>(&o.kd[m][k][4]) = *reinterpret_cast<const float4 *>(K + 32 * k + 4);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o.gc[m][r] = ws.gC[gh * DK + 16 * (TS * wave + m) + 4 * lk + r];
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) o.ut[r] = ws.Ut[gh * kChunk * DV + (16 * wave + 4 * lk + r) * DV + j0 + lr];
+}
+
 template <int DK, int DV, typename Tin>
 __global__ __launch_bounds__(256) void kda_prefill_scan_kernel(PrefillParams p, PrefillWs ws) {
-    constexpr int CB = kColBlock, CH = 2 * DK + DV;
-    constexpr int EPT = DK * CB / 256;          // state entries per lane in the update
-    static_assert(EPT >= 1 && CB % EPT == 0, "state block does not divide");
-    __shared__ __align__(16) float S[DK][CB];
+    constexpr int CB = kColBlock, CH = 2 * DK + DV, KS = DK / 32, TS = DK / 64;
+    __shared__ __align__(16) float S[2][DK][CB];
     __shared__ __align__(16) float U[kChunk][CB];
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int lr = lane % 16, lk = lane / 16;
     const int s = blockIdx.x, h = blockIdx.y, j0 = blockIdx.z * CB, H = p.H;
     if (ws.meta[0] != 1) return;
     const int slot = p.slot_idx[s];
@@ -345,58 +511,117 @@ __global__ __launch_bounds__(256) void kda_prefill_scan_kernel(PrefillParams p, 
     }
 
     float *Sg = p.state + ((size_t)slot * H + h) * DK * DV;
-    for (int e = tid; e < DK * CB; e += 256) S[e / CB][e % CB] = Sg[(e / CB) * DV + j0 + e % CB];
+    for (int e = tid; e < DK * CB; e += 256) S[0][e / CB][e % CB] = Sg[(e / CB) * DV + j0 + e % CB];
     __syncthreads();
 
-    const int ut = tid / 4, uq = tid % 4;        // U / O: row ut, columns 4uq..4uq+3
-    const int si = tid / (CB / EPT), sc0 = (tid % (CB / EPT)) * EPT;   // S update: row si, EPT columns
-    for (int c = 0; c < nch; ++c) {
-        const size_t gh = (size_t)(g0 + c) * H + h;
-        const int t0 = p.cu_seqlens[s] + c * kChunk;
-        const int n = min(kChunk, p.cu_seqlens[s + 1] - t0);
-        // U = U~ - W S
-        const float *Wr = ws.W + gh * kChunk * DK + ut * DK;
-        float4 u = *reinterpret_cast<const float4 *>(ws.Ut + gh * kChunk * DV + ut * DV + j0 + 4 * uq);
-        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-        const float *Qr = ws.Qg + gh * kChunk * DK + ut * DK;
-        for (int i = 0; i < DK; i += 4) {
-            const float4 w4 = *reinterpret_cast<const float4 *>(Wr + i);
-            const float4 q4 = *reinterpret_cast<const float4 *>(Qr + i);
-            const float wv[4] = {w4.x, w4.y, w4.z, w4.w}, qv[4] = {q4.x, q4.y, q4.z, q4.w};
+    auto load_sb = [&](int buf, Split8 (&sb)[KS]) {
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const float4 sv = *reinterpret_cast<const float4 *>(&S[i + m][4 * uq]);
-                u = fma4(-wv[m], sv, u);
-                o = fma4(qv[m], sv, o);
+        for (int k = 0; k < KS; ++k) {
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = S[buf][32 * k + 8 * lk + e][lr];
+            sb[k] = split8(x);
+        }
+    };
+    // bf16x3 product with the three partial products in separate
+    // accumulators (short dependency chains), summed at the end
+    struct Acc3 {
+        f32x4 hh, hl, lh;
+    };
+    auto zero3 = [](Acc3 &a) {
+        a.hh = f32x4{0.f, 0.f, 0.f, 0.f};
+        a.hl = a.hh;
+        a.lh = a.hh;
+    };
+    auto mma3s = [](const Split8 &x, const Split8 &y, Acc3 &a) {
+        a.hh = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x.hi, y.hi, a.hh, 0, 0, 0);
+        a.hl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x.hi, y.lo, a.hl, 0, 0, 0);
+        a.lh = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x.lo, y.hi, a.lh, 0, 0, 0);
+    };
+    auto sum3 = [](const Acc3 &a, int r) { return a.hh[r] + (a.hl[r] + a.lh[r]); };
+
+    // sequence bounds in registers: a load inside the chunk loop would have
+    // to wait behind the prefetch of the next chunk
+    const int seq_t0 = p.cu_seqlens[s], seq_t1 = p.cu_seqlens[s + 1];
+    float ypend[4];          // outputs of the previous chunk, stored one step late
+    int ypend_t0 = 0, ypend_n = 0;
+    auto flush_y = [&]() {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = 16 * wave + 4 * lk + r;
+            if (t < ypend_n) p.y[((size_t)(ypend_t0 + t) * H + h) * DV + j0 + lr] = ypend[r];
+        }
+    };
+
+    // chunk c reads the state from S[c & 1] and writes the next one to
+    // S[(c + 1) & 1]; two barriers per chunk
+    auto chunk_step = [&](int c, const ScanOps<DK> &o, Split8 (&sb)[KS]) {
+        const int cur = c & 1;
+        const int t0 = seq_t0 + c * kChunk;
+        const int n = min(kChunk, seq_t1 - t0);
+        // U = U~ - W S ; O = Q^e^G S
+        Acc3 au, ao;
+        zero3(au);
+        zero3(ao);
+#pragma unroll
+        for (int k = 0; k < KS; ++k) {
+            mma3s(split8(o.w[k], -1.0f), sb[k], au);
+            mma3s(split8(o.q[k]), sb[k], ao);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) U[16 * wave + 4 * lk + r][lr] = o.ut[r] + sum3(au, r);
+        __syncthreads();
+        Split8 ub[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = U[32 * k + 8 * lk + e][lr];
+            ub[k] = split8(x);
+        }
+        // O += P U  (P rows beyond the chunk and above the diagonal are 0)
+#pragma unroll
+        for (int k = 0; k < 2; ++k) mma3s(split8(o.pm[k]), ub[k], ao);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ypend[r] = sum3(ao, r);
+        ypend_t0 = t0;
+        ypend_n = n;
+        // S' = diag(e^G_C) S + Kd^T U  into the other buffer
+#pragma unroll
+        for (int m = 0; m < TS; ++m) {
+            Acc3 as;
+            zero3(as);
+#pragma unroll
+            for (int k = 0; k < 2; ++k) mma3s(split8(o.kd[m][k]), ub[k], as);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * (TS * wave + m) + 4 * lk + r;
+                S[cur ^ 1][row][lr] = o.gc[m][r] * S[cur][row][lr] + sum3(as, r);
             }
         }
-        *reinterpret_cast<float4 *>(&U[ut][4 * uq]) = u;
         __syncthreads();
-        // O = Q^e^G S + P U (rows >= n of P and U are zero)
-        const float *Pr = ws.P + gh * kChunk * kChunk + ut * kChunk;
-        for (int sv = 0; sv <= ut; ++sv) o = fma4(Pr[sv], *reinterpret_cast<const float4 *>(&U[sv][4 * uq]), o);
-        if (ut < n)
-            *reinterpret_cast<float4 *>(p.y + ((size_t)(t0 + ut) * H + h) * DV + j0 + 4 * uq) = o;
-        // S = diag(e^G_C) S + Kd^T U
-        const float gcv = ws.gC[gh * DK + si];
-        const float *Kr = ws.KdT + gh * DK * kChunk + si * kChunk;
-        float acc[EPT];
-#pragma unroll
-        for (int m = 0; m < EPT; ++m) acc[m] = gcv * S[si][sc0 + m];
-        for (int t = 0; t < kChunk; t += 4) {
-            const float4 k4 = *reinterpret_cast<const float4 *>(Kr + t);
-            const float kv[4] = {k4.x, k4.y, k4.z, k4.w};
-#pragma unroll
-            for (int m2 = 0; m2 < 4; ++m2)
-#pragma unroll
-                for (int m = 0; m < EPT; ++m) acc[m] = fmaf(kv[m2], U[t + m2][sc0 + m], acc[m]);
-        }
-        __syncthreads();   // every lane has read S and U of this chunk
-#pragma unroll
-        for (int m = 0; m < EPT; ++m) S[si][sc0 + m] = acc[m];
-        __syncthreads();
+        load_sb(cur ^ 1, sb);
+    };
+
+    Split8 sb[KS];
+    load_sb(0, sb);
+    ScanOps<DK> cur, nxt;
+    if (nch > 0) scan_load<DK, DV>(ws, (size_t)g0 * H + h, wave, lr, lk, j0, cur);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the loop starts with nothing in flight
+    for (int c = 0; c < nch; ++c) {
+        // the next chunk's operands load while this chunk computes
+        if (c + 1 < nch) scan_load<DK, DV>(ws, (size_t)(g0 + c + 1) * H + h, wave, lr, lk, j0, nxt);
+        flush_y();
+        chunk_step(c, cur, sb);
+        // all of them (and the output stores issued above) have landed by
+        // now; an explicit vmcnt(0) tells the compiler so, instead of
+        // conservative waits inside the next step
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        cur = nxt;
     }
-    for (int e = tid; e < DK * CB; e += 256) Sg[(e / CB) * DV + j0 + e % CB] = S[e / CB][e % CB];
+    flush_y();
+    const int fin = nch & 1;
+    for (int e = tid; e < DK * CB; e += 256) Sg[(e / CB) * DV + j0 + e % CB] = S[fin][e / CB][e % CB];
 }
 
 // ---------------------------------------------------------------------------
