@@ -234,6 +234,22 @@ def extras(torch, api, synth, layer, cache, step_inputs, y, slots, B, H, dk, dv,
     bl = decode_bytes_per_token_head(H, dk, dv, B) * B * H
     ex["decode_b64_cold"] = {"us_per_step": s * 1e6, "token_heads_per_s": B * H / s,
                              "algorithmic_gbs": bl / s / 1e9, "frac_of_8tbs": bl / s / 8e12}
+    # the same two workloads with non-temporal state traffic (KDA_STREAM_STATE)
+    sl_layer = api.Layer(layer.A, layer.conv_wt, layer.norm_w, layer.q_scale, layer.l2_eps,
+                         layer.rms_eps, layer.conv_silu, stream_state=True)
+    for name, sl_fn in (("decode_b64_stream", lambda i: slots), ("decode_b64_cold_stream", lambda i: sets[i % nrot])):
+        cl = [api.kda_decode_prepared(sl_layer, cache, sl_fn(i), step_inputs[W + i], y) for i in range(steps)]
+        for c in cl[:nrot]:
+            c()
+        torch.cuda.synchronize()
+        a.record(stream)
+        for c in cl:
+            c()
+        b.record(stream)
+        torch.cuda.synchronize()
+        s = a.elapsed_time(b) / 1e3 / steps
+        ex[name] = {"us_per_step": s * 1e6, "token_heads_per_s": B * H / s,
+                    "algorithmic_gbs": bl / s / 1e9, "frac_of_8tbs": bl / s / 8e12}
     # copy ceiling (1 GiB each way)
     n = 1 << 28
     src = torch.empty(n, dtype=torch.float32, device="cuda:0").fill_(1.0)

@@ -72,6 +72,13 @@ typedef enum kda_dtype {
 
 /* flags */
 #define KDA_CONV_SILU 1u     /* SiLU after the conv (the usual setting)        */
+#define KDA_STREAM_STATE 2u  /* decode / verify: non-temporal state loads and
+                                stores.  Faster when the states a call touches
+                                do not stay cache-resident until the next call
+                                (many layers, large batches); slower when they
+                                do (a 128 MiB working set re-used call after
+                                call fits the 256 MB Infinity Cache).  Results
+                                are bitwise identical either way.              */
 
 /* Parameters of one KDA layer (device pointers, fp32). */
 typedef struct kda_layer {
@@ -82,7 +89,7 @@ typedef struct kda_layer {
     float q_scale;           /* usually d_k^-1/2                                */
     float l2_eps;            /* usually 1e-6                                    */
     float rms_eps;           /* usually 1e-6                                    */
-    uint32_t flags;          /* KDA_CONV_SILU                                   */
+    uint32_t flags;          /* KDA_CONV_SILU | KDA_STREAM_STATE                */
 } kda_layer;
 
 /* The recurrent-state pools (device pointers). */

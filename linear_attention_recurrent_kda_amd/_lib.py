@@ -13,6 +13,7 @@ LIB_PATH = os.path.join(HERE, "libkda.so")
 KDA_F32 = 0
 KDA_BF16 = 1
 KDA_CONV_SILU = 1
+KDA_STREAM_STATE = 2
 
 STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE",
           4: "KDA_ERR_ALIGN", 5: "KDA_ERR_UNSUPPORTED", 6: "KDA_ERR_WORKSPACE",

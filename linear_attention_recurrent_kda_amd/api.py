@@ -35,6 +35,7 @@ class Layer:
     l2_eps: float = 1e-6
     rms_eps: float = 1e-6
     conv_silu: bool = True
+    stream_state: bool = False          # non-temporal state traffic (KDA_STREAM_STATE)
 
     @property
     def H(self):
@@ -62,7 +63,8 @@ class Layer:
         qs = dk ** -0.5 if self.q_scale is None else self.q_scale
         return _lib.KdaLayer(H, dk, dv, self.conv_w, self.A.data_ptr(), self.conv_wt.data_ptr(),
                              self.norm_w.data_ptr(), qs, self.l2_eps, self.rms_eps,
-                             _lib.KDA_CONV_SILU if self.conv_silu else 0)
+                             (_lib.KDA_CONV_SILU if self.conv_silu else 0)
+                             | (_lib.KDA_STREAM_STATE if self.stream_state else 0))
 
 
 @dataclass

@@ -24,7 +24,7 @@ kda_status check_layer(const kda_layer *L) {
     if (L->H <= 0 || L->d_k <= 0 || L->d_v <= 0 || L->conv_w <= 0) return KDA_ERR_SHAPE;
     if (!((L->d_k == 64 || L->d_k == 128) && (L->d_v == 64 || L->d_v == 128))) return KDA_ERR_UNSUPPORTED;
     if (L->conv_w != 4) return KDA_ERR_UNSUPPORTED;
-    if (L->flags & ~KDA_CONV_SILU) return KDA_ERR_UNSUPPORTED;
+    if (L->flags & ~(KDA_CONV_SILU | KDA_STREAM_STATE)) return KDA_ERR_UNSUPPORTED;
     if (!isfinite(L->q_scale) || !finite_nonneg(L->l2_eps) || !finite_nonneg(L->rms_eps))
         return KDA_ERR_SHAPE;
     if (!aligned(L->A, 16) || !aligned(L->conv_wt, 16) || !aligned(L->norm_w, 16)) return KDA_ERR_ALIGN;
@@ -61,6 +61,7 @@ RecParams rec_params(const kda_layer *L, const kda_cache *C, const kda_inputs *i
     p.A = L->A; p.conv_wt = L->conv_wt; p.norm_w = L->norm_w;
     p.q_scale = L->q_scale; p.l2_eps = L->l2_eps; p.rms_eps = L->rms_eps;
     p.silu = (L->flags & KDA_CONV_SILU) ? 1 : 0;
+    p.stream_state = (L->flags & KDA_STREAM_STATE) ? 1 : 0;
     p.state = C->state; p.window = C->conv_state; p.n_slots = C->n_slots; p.err_flag = C->err_flag;
     p.x_q = in->x_q; p.x_k = in->x_k; p.x_v = in->x_v; p.g = in->g; p.b = in->b; p.z = in->z;
     p.y = y;

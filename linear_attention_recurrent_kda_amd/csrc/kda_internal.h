@@ -16,6 +16,7 @@ struct RecParams {
     const float *A, *conv_wt, *norm_w;
     float q_scale, l2_eps, rms_eps;
     int silu;
+    int stream_state;           // non-temporal state loads / stores
     // cache
     float *state;
     void *window;

@@ -189,12 +189,15 @@ __global__ __launch_bounds__(256) void kda_prefill_prep_kernel(PrefillParams p, 
 // (checked per block), otherwise the tile is summed directly with one
 // exponential per term.
 // ---------------------------------------------------------------------------
+// Rows of q, k and G are padded by one word so that lanes reading down a
+// column (different tokens, same channel) hit different LDS banks.
 template <int DK, int DV>
 struct __align__(16) IntraLds {
-    static constexpr int QW = DK >= 68 ? DK : 68;
+    static constexpr int KW = DK + 1;
+    static constexpr int QW = KW >= 68 ? KW : 68;
     float q[kChunk][QW];           // q^, later T = (I + A)^-1
-    float k[kChunk][DK];           // k^
-    float G[kChunk][DK];           // log2-decay prefix sums
+    float k[kChunk][KW];           // k^
+    float G[kChunk][KW];           // log2-decay prefix sums
     float A[kChunk][kChunk + 1];   // beta_t (K K^T * decay), strictly lower part used
     float Z[3][16][17];            // block-inverse scratch
     float D[4][16][17];            // per-wave scratch of the direct tile path
@@ -221,26 +224,42 @@ __global__ __launch_bounds__(256) void kda_prefill_intra_kernel(PrefillParams p,
     const int n = min(kChunk, p.cu_seqlens[s + 1] - t0);
     const size_t gh = (size_t)gidx * H + h;
 
-    // 1. k^, q^, log2 alpha, beta of the chunk (rows >= n are zero)
+    // 1. k^, q^ and beta of the chunk (rows >= n are zero); lanes < d_k also
+    //    form the log2-decay prefix sums of their channel straight from memory
     for (int e = tid; e < kChunk * DK / 4; e += 256) {
         const int r = e / (DK / 4), i = 4 * (e % (DK / 4));
-        float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), qv = kv, gv = kv;
+        float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), qv = kv;
         if (r < n) {
             const size_t src = ((size_t)(t0 + r) * H + h) * DK + i;
             kv = *reinterpret_cast<const float4 *>(ws.kh + src);
             qv = *reinterpret_cast<const float4 *>(ws.qh + src);
-            gv = *reinterpret_cast<const float4 *>(ws.la + src);
         }
-        *reinterpret_cast<float4 *>(&L.k[r][i]) = kv;
-        *reinterpret_cast<float4 *>(&L.q[r][i]) = qv;
-        *reinterpret_cast<float4 *>(&L.G[r][i]) = gv;
+        L.k[r][i] = kv.x; L.k[r][i + 1] = kv.y; L.k[r][i + 2] = kv.z; L.k[r][i + 3] = kv.w;
+        L.q[r][i] = qv.x; L.q[r][i + 1] = qv.y; L.q[r][i + 2] = qv.z; L.q[r][i + 3] = qv.w;
+    }
+    if (tid < DK) {
+        const float *la = ws.la + ((size_t)t0 * H + h) * DK + tid;
+        float acc = 0.f;
+#pragma unroll 8
+        for (int r = 0; r < kChunk; ++r) {
+            acc += r < n ? la[(size_t)r * H * DK] : 0.f;   // non-increasing in r
+            L.G[r][tid] = acc;
+        }
     }
     if (tid < kChunk) L.beta[tid] = tid < n ? ws.beta[(size_t)(t0 + tid) * H + h] : 0.f;
-    __syncthreads();
-    // 2. prefix sums over the chunk, per key channel (non-increasing in t)
-    if (tid < DK) {
-        float acc = 0.f;
-        for (int r = 0; r < kChunk; ++r) { acc += L.G[r][tid]; L.G[r][tid] = acc; }
+    // the V operand of step 7 is read now, so its latency hides behind steps 3-6
+    constexpr int NU = DV / 64;                  // U~ column tiles per wave
+    float vpre[NU][2][8];
+#pragma unroll
+    for (int m = 0; m < NU; ++m) {
+        const int col = 16 * (wave + 4 * (DK / 64 + m)) + lr - DK;
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int sv = 32 * k2 + 8 * lk + e;
+                vpre[m][k2][e] = sv < n ? ws.vv[((size_t)(t0 + sv) * H + h) * DV + col] : 0.f;
+            }
     }
     __syncthreads();
     // 3. per 16-token block: may the diagonal tile use the scaled factors?
@@ -253,13 +272,17 @@ __global__ __launch_bounds__(256) void kda_prefill_intra_kernel(PrefillParams p,
     }
     __syncthreads();
 
-    // 4. A and P in 16 x 16 tiles; tile (bt, bs) covers t in block bt, s in block bs
+    // 4. A and P in 16 x 16 tiles; tile (bt, bs) covers t in block bt, s in
+    //    block bs.  The 10 tiles on or below the diagonal go 3,3,2,2 to the
+    //    waves; the 6 above it (P = 0 there, A is never read there) 2,2,1,1.
     float *Pg = ws.P + gh * kChunk * kChunk;
     for (int tile = wave; tile < 16; tile += 4) {
-        const int bt = tile / 4, bs = tile % 4;
+        // lower tiles 0..9 in row order, then the upper ones
+        const int lbt[16] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3, 0, 0, 0, 1, 1, 2};
+        const int lbs[16] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3, 1, 2, 3, 2, 3, 3};
+        const int bt = lbt[tile], bs = lbs[tile];
         f32x4 aA = {0.f, 0.f, 0.f, 0.f}, aP = aA;
         if (bs > bt) {
-            // above the diagonal: P is zero there (A is never read there)
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) Pg[(16 * bt + 4 * lk + rr) * kChunk + 16 * bs + lr] = 0.f;
             continue;
@@ -382,9 +405,11 @@ __global__ __launch_bounds__(256) void kda_prefill_intra_kernel(PrefillParams p,
             ta[rt][k2] = split8(x);
         }
     constexpr int NCT = (DK + DV) / 16;
-    for (int ct = wave; ct < NCT; ct += 4) {
+#pragma unroll
+    for (int ci = 0; ci < NCT / 4; ++ci) {
+        const int ct = wave + 4 * ci;
         const int col = 16 * ct + lr;
-        const bool isw = col < DK;
+        const bool isw = ci < DK / 64;             // wave-uniform
         Split8 rb[2];
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
@@ -393,7 +418,7 @@ __global__ __launch_bounds__(256) void kda_prefill_intra_kernel(PrefillParams p,
             for (int e = 0; e < 8; ++e) {
                 const int sv = 32 * k2 + 8 * lk + e;
                 if (isw) x[e] = L.beta[sv] * L.k[sv][col] * exp2f(L.G[sv][col]);
-                else x[e] = sv < n ? L.beta[sv] * ws.vv[((size_t)(t0 + sv) * H + h) * DV + (col - DK)] : 0.f;
+                else x[e] = L.beta[sv] * vpre[ci - DK / 64][k2][e];
             }
             rb[k2] = split8(x);
         }

@@ -23,6 +23,29 @@
 
 namespace kda {
 
+// State tile traffic: read once, written once per launch.  With STREAM the
+// accesses carry the non-temporal hint, so a working set larger than the
+// caches does not thrash them (and a small, re-used one is not kept either).
+template <bool STREAM>
+__device__ __forceinline__ float4 load_state4(const float *p) {
+    if (STREAM) {
+        typedef float v4 __attribute__((ext_vector_type(4)));
+        const v4 x = __builtin_nontemporal_load(reinterpret_cast<const v4 *>(p));
+        return make_float4(x[0], x[1], x[2], x[3]);
+    }
+    return *reinterpret_cast<const float4 *>(p);
+}
+template <bool STREAM>
+__device__ __forceinline__ void store_state4(float *p, float4 v) {
+    if (STREAM) {
+        typedef float v4 __attribute__((ext_vector_type(4)));
+        const v4 x = {v.x, v.y, v.z, v.w};
+        __builtin_nontemporal_store(x, reinterpret_cast<v4 *>(p));
+        return;
+    }
+    *reinterpret_cast<float4 *>(p) = v;
+}
+
 template <int DK, int DV, int NT>
 struct RecGeo {
     static constexpr int CG = DV / 4;      // float4 column groups
@@ -197,7 +220,7 @@ __device__ __forceinline__ void prep_token(const RecParams &p, int lane, int j,
     }
 }
 
-template <int DK, int DV, int NT, typename Tin, int TMAX, bool VERIFY>
+template <int DK, int DV, int NT, typename Tin, int TMAX, bool VERIFY, bool STREAM>
 __global__ __launch_bounds__(NT) void kda_recurrent_kernel(RecParams p) {
     using G = RecGeo<DK, DV, NT>;
     __shared__ TokenLds<DK, DV> tok[TMAX];
@@ -205,8 +228,8 @@ __global__ __launch_bounds__(NT) void kda_recurrent_kernel(RecParams p) {
 
     const int tid = threadIdx.x;
     const int lane = tid % kWave, wave = tid / kWave;
-    const int b = blockIdx.x / p.H, h = blockIdx.x % p.H;
     const int cg = tid % G::CG, rg = tid / G::CG;
+    const int b = blockIdx.x / p.H, h = blockIdx.x % p.H;
 
     int T = 1;
     if (VERIFY) T = p.draft_len ? min(max(p.draft_len[b], 0), p.T) : p.T;
@@ -230,8 +253,7 @@ __global__ __launch_bounds__(NT) void kda_recurrent_kernel(RecParams p) {
     float *S = p.state + ((size_t)slot * p.H + h) * DK * DV;
     float4 s[G::RPT];
 #pragma unroll
-    for (int i = 0; i < G::RPT; ++i)
-        s[i] = *reinterpret_cast<const float4 *>(S + (size_t)(rg + G::RG * i) * DV + 4 * cg);
+    for (int i = 0; i < G::RPT; ++i) s[i] = load_state4<STREAM>(S + (size_t)(rg + G::RG * i) * DV + 4 * cg);
 
     // 2. conv (+ window update / window snapshots)
     conv_compute<DK, DV, NT, Tin, TMAX, VERIFY>(p, tid, b, h, slot, T, cr, tok);
@@ -284,8 +306,7 @@ __global__ __launch_bounds__(NT) void kda_recurrent_kernel(RecParams p) {
             if (ss >= 0 && ss < p.n_slots) {
                 float *D = p.state + ((size_t)ss * p.H + h) * DK * DV;
 #pragma unroll
-                for (int i = 0; i < G::RPT; ++i)
-                    *reinterpret_cast<float4 *>(D + (size_t)(rg + G::RG * i) * DV + 4 * cg) = s[i];
+                for (int i = 0; i < G::RPT; ++i) store_state4<STREAM>(D + (size_t)(rg + G::RG * i) * DV + 4 * cg, s[i]);
             } else if (ss != -1 && tid == 0) {
                 flag_error(p.err_flag);
             }
@@ -312,8 +333,7 @@ __global__ __launch_bounds__(NT) void kda_recurrent_kernel(RecParams p) {
     // 5. the single write of the state tile (decode only: verify leaves S0)
     if (!VERIFY) {
 #pragma unroll
-        for (int i = 0; i < G::RPT; ++i)
-            *reinterpret_cast<float4 *>(S + (size_t)(rg + G::RG * i) * DV + 4 * cg) = s[i];
+        for (int i = 0; i < G::RPT; ++i) store_state4<STREAM>(S + (size_t)(rg + G::RG * i) * DV + 4 * cg, s[i]);
     }
 }
 
@@ -340,19 +360,22 @@ __global__ __launch_bounds__(256) void kda_commit_kernel(CommitParams p) {
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-constexpr int kRecThreads = 256;
+#ifndef KDA_REC_THREADS
+#define KDA_REC_THREADS 256
+#endif
+constexpr int kRecThreads = KDA_REC_THREADS;   // lanes per (sequence, head) workgroup
 
-template <int DK, int DV, typename Tin>
+template <int DK, int DV, typename Tin, bool STREAM>
 static kda_status launch_rec_typed(const RecParams &p, bool verify, hipStream_t stream) {
     const dim3 grid((unsigned)(p.B * p.H)), block(kRecThreads);
     if (!verify) {
-        hipLaunchKernelGGL((kda_recurrent_kernel<DK, DV, kRecThreads, Tin, 1, false>), grid, block,
+        hipLaunchKernelGGL((kda_recurrent_kernel<DK, DV, kRecThreads, Tin, 1, false, STREAM>), grid, block,
                            0, stream, p);
     } else if (p.T <= 8) {
-        hipLaunchKernelGGL((kda_recurrent_kernel<DK, DV, kRecThreads, Tin, 8, true>), grid, block,
+        hipLaunchKernelGGL((kda_recurrent_kernel<DK, DV, kRecThreads, Tin, 8, true, STREAM>), grid, block,
                            0, stream, p);
     } else {
-        hipLaunchKernelGGL((kda_recurrent_kernel<DK, DV, kRecThreads, Tin, 16, true>), grid, block,
+        hipLaunchKernelGGL((kda_recurrent_kernel<DK, DV, kRecThreads, Tin, 16, true, STREAM>), grid, block,
                            0, stream, p);
     }
     return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
@@ -360,8 +383,11 @@ static kda_status launch_rec_typed(const RecParams &p, bool verify, hipStream_t 
 
 template <int DK, int DV>
 static kda_status launch_rec_dt(const RecParams &p, kda_dtype dt, bool verify, hipStream_t s) {
-    return dt == KDA_BF16 ? launch_rec_typed<DK, DV, uint16_t>(p, verify, s)
-                          : launch_rec_typed<DK, DV, float>(p, verify, s);
+    if (p.stream_state)
+        return dt == KDA_BF16 ? launch_rec_typed<DK, DV, uint16_t, true>(p, verify, s)
+                              : launch_rec_typed<DK, DV, float, true>(p, verify, s);
+    return dt == KDA_BF16 ? launch_rec_typed<DK, DV, uint16_t, false>(p, verify, s)
+                          : launch_rec_typed<DK, DV, float, false>(p, verify, s);
 }
 
 kda_status launch_recurrent(const RecParams &p, int d_k, int d_v, kda_dtype dt, bool verify,

@@ -307,3 +307,29 @@ def test_repeated_runs_bitwise_identical():
         outs.append((y.clone(), cache.state.clone(), cache.conv_state.clone()))
     for a, b in zip(outs[0], outs[1]):
         assert torch.equal(a, b)
+
+
+def test_stream_state_flag_is_bitwise_identical():
+    """KDA_STREAM_STATE only changes cache hints: decode and verify results
+    are bitwise the same with and without it."""
+    g = synth.rng(740)
+    H, dk, dv, B, T = 4, 128, 128, 6, 5
+    params = synth.layer_params(g, H, dk, dv)
+    dl, _ = layer_pair(params)
+    ds, _ = layer_pair(params)
+    ds.stream_state = True
+    inp = synth.token_inputs(g, (B,), H, dk, dv, "bf16")
+    vin = synth.token_inputs(g, (B, T), H, dk, dv, "bf16")
+    outs = []
+    for layer in (dl, ds):
+        cache = new_cache(B + B * T, H, dk, dv, "bf16", fill_seed=12)
+        live = torch.arange(B, dtype=torch.int32, device=DEV)
+        snaps = torch.arange(B, B + B * T, dtype=torch.int32, device=DEV).reshape(B, T)
+        y = torch.empty((B, H, dv), device=DEV)
+        api.kda_decode(layer, cache, live, inputs_dev(inp, "bf16"), y)
+        yv = torch.empty((B, T, H, dv), device=DEV)
+        api.kda_spec_verify(layer, cache, live, snaps, inputs_dev(vin, "bf16"), yv)
+        torch.cuda.synchronize()
+        outs.append((y, yv, cache.state.clone(), cache.conv_state.clone()))
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
