@@ -31,21 +31,26 @@ constexpr int kChunk = 64;
 constexpr int kColBlock = 16;
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Device pointers into the caller's workspace (fp32 unless noted).
+// Device pointers into the caller's workspace.  The per-chunk factors the
+// scan multiplies on MFMA are stored pre-split as bf16 pairs (hi = bf16(x),
+// lo = bf16(x - hi)), in the row-major layout the scan's operand loads read.
 struct PrefillWs {
-    int32_t *meta;        // [0]: 1 if cu_seqlens is valid; [1 + s]: first chunk of s, s <= N
-    float *qh, *kh, *vv;  // [T, H, d]
-    float *la;            // [T, H, d_k]  log2(alpha)
-    float *beta;          // [T, H]
-    float *W, *Ut, *Qg;   // [G, H, 64, d]
-    float *KdT;           // [G, H, d_k, 64]
-    float *P;             // [G, H, 64, 64]
-    float *gC;            // [G, H, d_k]  e^(G_C)
+    int32_t *meta;            // [0]: 1 if cu_seqlens is valid; [1 + s]: first chunk of s, s <= N
+    float *qh, *kh, *vv;      // [T, H, d]  fp32
+    float *la;                // [T, H, d_k]  log2(alpha)
+    float *beta;              // [T, H]
+    float *kT;                // [G, H, d_k, 64]  k^ of each chunk, transposed
+    uint16_t *Wn_hi, *Wn_lo;  // [G, H, 64, d_k]  -W
+    uint16_t *Q_hi, *Q_lo;    // [G, H, 64, d_k]  Q^ e^G
+    uint16_t *K_hi, *K_lo;    // [G, H, d_k, 64]  (K^ e^(G_C - G))^T
+    uint16_t *P_hi, *P_lo;    // [G, H, 64, 64]
+    float *Ut;                // [G, H, 64, d_v]
+    float *gC;                // [G, H, d_k]  e^(G_C)
     int G_max;
 };
 
 struct WsLayout {
-    size_t meta, qh, kh, vv, la, beta, W, Ut, Qg, KdT, P, gC, total;
+    size_t meta, qh, kh, vv, la, beta, kT, Wn_hi, Wn_lo, Q_hi, Q_lo, K_hi, K_lo, P_hi, P_lo, Ut, gC, total;
 };
 
 static size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
@@ -62,11 +67,16 @@ static WsLayout ws_layout(int H, int dk, int dv, int total_T, int N_seq) {
     l.vv = take(4 * TH * dv);
     l.la = take(4 * TH * dk);
     l.beta = take(4 * TH);
-    l.W = take(4 * GH * kChunk * dk);
+    l.kT = take(4 * GH * dk * kChunk);
+    l.Wn_hi = take(2 * GH * kChunk * dk);
+    l.Wn_lo = take(2 * GH * kChunk * dk);
+    l.Q_hi = take(2 * GH * kChunk * dk);
+    l.Q_lo = take(2 * GH * kChunk * dk);
+    l.K_hi = take(2 * GH * dk * kChunk);
+    l.K_lo = take(2 * GH * dk * kChunk);
+    l.P_hi = take(2 * GH * kChunk * kChunk);
+    l.P_lo = take(2 * GH * kChunk * kChunk);
     l.Ut = take(4 * GH * kChunk * dv);
-    l.Qg = take(4 * GH * kChunk * dk);
-    l.KdT = take(4 * GH * dk * kChunk);
-    l.P = take(4 * GH * kChunk * kChunk);
     l.gC = take(4 * GH * dk);
     l.total = off;
     return l;
@@ -162,11 +172,14 @@ __global__ __launch_bounds__(256) void kda_prefill_prep_kernel(PrefillParams p, 
     const float rk = 1.0f / sqrtf(sk + p.l2_eps);
     const size_t th = (size_t)t * H + h;
     const Tin *g = static_cast<const Tin *>(p.g) + th * DK;
+    // the chunk-transposed copy of k^ (row i of chunk g holds its 64 tokens)
+    const size_t kt_base = ((size_t)(ws.meta[1 + s] + pos / kChunk) * H + h) * DK * kChunk + pos % kChunk;
 #pragma unroll
     for (int e = 0; e < EK; ++e) {
         const int i = lane + kWave * e;
         ws.qh[th * DK + i] = conv[e] * rq;
         ws.kh[th * DK + i] = conv[EK + e] * rk;
+        ws.kT[kt_base + (size_t)i * kChunk] = conv[EK + e] * rk;
         // alpha below 2^-200 is 0 in fp32 either way; the floor keeps the
         // prefix sums finite (g = +inf would give -inf - -inf = NaN later)
         ws.la[th * DK + i] = fmaxf(-expf(p.A[h * DK + i]) * softplus(to_f32(g[i])) * kLog2e, -200.f);
@@ -188,28 +201,47 @@ __global__ __launch_bounds__(256) void kda_prefill_prep_kernel(PrefillParams p, 
 // factor >= 1; it is used only when the block's decay span is at most 2^60
 // (checked per block), otherwise the tile is summed directly with one
 // exponential per term.
+//
+// q^ and k^ are read from the workspace (they stay in L2 across the tiles);
+// LDS holds only the decay prefix sums, A and T, so two workgroups share a CU.
 // ---------------------------------------------------------------------------
-// Rows of q, k and G are padded by one word so that lanes reading down a
-// column (different tokens, same channel) hit different LDS banks.
 template <int DK, int DV>
 struct __align__(16) IntraLds {
-    static constexpr int KW = DK + 1;
-    static constexpr int QW = KW >= 68 ? KW : 68;
-    float q[kChunk][QW];           // q^, later T = (I + A)^-1
-    float k[kChunk][KW];           // k^
-    float G[kChunk][KW];           // log2-decay prefix sums
-    float A[kChunk][kChunk + 1];   // beta_t (K K^T * decay), strictly lower part used
-    float Z[3][16][17];            // block-inverse scratch
-    float D[4][16][17];            // per-wave scratch of the direct tile path
+    static constexpr int KW = DK + 1;   // padded rows: column reads hit distinct banks
+    float G[kChunk][KW];                // log2-decay prefix sums
+    float A[kChunk][kChunk + 1];        // beta_t (K K^T * decay), strictly lower part used
+    float T[kChunk][kChunk + 4];        // (I + A)^-1
+    float Z[3][16][17];                 // block-inverse scratch
+    float D[4][16][17];                 // per-wave scratch of the direct tile path
     float beta[kChunk];
     int safe[4];
 };
 
 constexpr float kSafeSpan = 60.f;
 
+// bf16 pair of an fp32 value, as raw bits
+__device__ __forceinline__ void split_bits(float x, uint16_t &hi, uint16_t &lo) {
+    const __bf16 h = (__bf16)x;
+    const __bf16 l = (__bf16)(x - (float)h);
+    hi = __builtin_bit_cast(uint16_t, h);
+    lo = __builtin_bit_cast(uint16_t, l);
+}
+
+// 8 consecutive fp32 values of a workspace row (16-byte aligned), or zeros
+// for a row past the end of the chunk (it may lie past the array)
+__device__ __forceinline__ void load8(const float *src, bool valid, float *x) {
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+    if (valid) {
+        a = *reinterpret_cast<const float4 *>(src);
+        b = *reinterpret_cast<const float4 *>(src + 4);
+    }
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
 template <int DK, int DV>
-__global__ __launch_bounds__(256) void kda_prefill_intra_kernel(PrefillParams p, PrefillWs ws) {
-    constexpr int KS = DK / 32, QW = IntraLds<DK, DV>::QW;
+__global__ __launch_bounds__(256, 2) void kda_prefill_intra_kernel(PrefillParams p, PrefillWs ws) {
+    constexpr int KS = DK / 32;
     __shared__ IntraLds<DK, DV> L;
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int lr = lane % 16, lk = lane / 16;
@@ -223,30 +255,30 @@ __global__ __launch_bounds__(256) void kda_prefill_intra_kernel(PrefillParams p,
     const int t0 = p.cu_seqlens[s] + c * kChunk;
     const int n = min(kChunk, p.cu_seqlens[s + 1] - t0);
     const size_t gh = (size_t)gidx * H + h;
+    const size_t row0 = (size_t)t0 * H + h;              // workspace row of token t0
+    const size_t rstride = (size_t)H;                    // rows between consecutive tokens
+    auto kh_row = [&](int r) { return ws.kh + (row0 + r * rstride) * DK; };
+    auto qh_row = [&](int r) { return ws.qh + (row0 + r * rstride) * DK; };
 
-    // 1. k^, q^ and beta of the chunk (rows >= n are zero); lanes < d_k also
-    //    form the log2-decay prefix sums of their channel straight from memory
+    // 1. log2 alpha of the chunk into LDS (coalesced; rows >= n are zero),
+    //    then per-channel prefix sums: lane (channel, part) sums its run of
+    //    rows in registers, and the parts are chained through LDS
     for (int e = tid; e < kChunk * DK / 4; e += 256) {
         const int r = e / (DK / 4), i = 4 * (e % (DK / 4));
-        float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), qv = kv;
-        if (r < n) {
-            const size_t src = ((size_t)(t0 + r) * H + h) * DK + i;
-            kv = *reinterpret_cast<const float4 *>(ws.kh + src);
-            qv = *reinterpret_cast<const float4 *>(ws.qh + src);
-        }
-        L.k[r][i] = kv.x; L.k[r][i + 1] = kv.y; L.k[r][i + 2] = kv.z; L.k[r][i + 3] = kv.w;
-        L.q[r][i] = qv.x; L.q[r][i + 1] = qv.y; L.q[r][i + 2] = qv.z; L.q[r][i + 3] = qv.w;
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (r < n) v = *reinterpret_cast<const float4 *>(ws.la + (row0 + r * rstride) * DK + i);
+        L.G[r][i] = v.x; L.G[r][i + 1] = v.y; L.G[r][i + 2] = v.z; L.G[r][i + 3] = v.w;
     }
-    if (tid < DK) {
-        const float *la = ws.la + ((size_t)t0 * H + h) * DK + tid;
+    if (tid < kChunk) L.beta[tid] = tid < n ? ws.beta[row0 + tid * rstride] : 0.f;
+    constexpr int NPART = 256 / DK, RP = kChunk / NPART;
+    const int pch = tid % DK, part = tid / DK;
+    float run[RP];
+    __syncthreads();
+    {
         float acc = 0.f;
-#pragma unroll 8
-        for (int r = 0; r < kChunk; ++r) {
-            acc += r < n ? la[(size_t)r * H * DK] : 0.f;   // non-increasing in r
-            L.G[r][tid] = acc;
-        }
+#pragma unroll
+        for (int j = 0; j < RP; ++j) { acc += L.G[part * RP + j][pch]; run[j] = acc; }
     }
-    if (tid < kChunk) L.beta[tid] = tid < n ? ws.beta[(size_t)(t0 + tid) * H + h] : 0.f;
     // the V operand of step 7 is read now, so its latency hides behind steps 3-6
     constexpr int NU = DV / 64;                  // U~ column tiles per wave
     float vpre[NU][2][8];
@@ -258,11 +290,24 @@ __global__ __launch_bounds__(256) void kda_prefill_intra_kernel(PrefillParams p,
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int sv = 32 * k2 + 8 * lk + e;
-                vpre[m][k2][e] = sv < n ? ws.vv[((size_t)(t0 + sv) * H + h) * DV + col] : 0.f;
+                vpre[m][k2][e] = sv < n ? ws.vv[(row0 + sv * rstride) * DV + col] : 0.f;
             }
     }
+    __syncthreads();   // every part has read its raw rows
+#pragma unroll
+    for (int j = 0; j < RP; ++j) L.G[part * RP + j][pch] = run[j];
     __syncthreads();
-    // 3. per 16-token block: may the diagonal tile use the scaled factors?
+    {
+        float off = 0.f;   // totals of the earlier parts, in order
+        for (int q = 0; q < part; ++q) off += L.G[q * RP + RP - 1][pch];
+        __syncthreads();
+        if (part > 0) {
+#pragma unroll
+            for (int j = 0; j < RP; ++j) L.G[part * RP + j][pch] = run[j] + off;
+        }
+    }
+    __syncthreads();
+    // 2. per 16-token block: may the diagonal tile use the scaled factors?
     {
         float span = 0.f;
         for (int i = lane; i < DK; i += kWave) span = fmaxf(span, L.G[16 * wave][i] - L.G[16 * wave + 15][i]);
@@ -272,57 +317,71 @@ __global__ __launch_bounds__(256) void kda_prefill_intra_kernel(PrefillParams p,
     }
     __syncthreads();
 
-    // 4. A and P in 16 x 16 tiles; tile (bt, bs) covers t in block bt, s in
+    // 3. A and P in 16 x 16 tiles; tile (bt, bs) covers t in block bt, s in
     //    block bs.  The 10 tiles on or below the diagonal go 3,3,2,2 to the
     //    waves; the 6 above it (P = 0 there, A is never read there) 2,2,1,1.
-    float *Pg = ws.P + gh * kChunk * kChunk;
+    uint16_t *Ph = ws.P_hi + gh * kChunk * kChunk, *Pl = ws.P_lo + gh * kChunk * kChunk;
     for (int tile = wave; tile < 16; tile += 4) {
-        // lower tiles 0..9 in row order, then the upper ones
         const int lbt[16] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3, 0, 0, 0, 1, 1, 2};
         const int lbs[16] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3, 1, 2, 3, 2, 3, 3};
         const int bt = lbt[tile], bs = lbs[tile];
         f32x4 aA = {0.f, 0.f, 0.f, 0.f}, aP = aA;
         if (bs > bt) {
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) Pg[(16 * bt + 4 * lk + rr) * kChunk + 16 * bs + lr] = 0.f;
+            for (int rr = 0; rr < 4; ++rr) {
+                const int idx = (16 * bt + 4 * lk + rr) * kChunk + 16 * bs + lr;
+                Ph[idx] = 0;
+                Pl[idx] = 0;
+            }
             continue;
         }
         const int r = 16 * bt;
         if (bs < bt || L.safe[bt]) {
             const int t = 16 * bt + lr, sr = 16 * bs + lr;
+            const float *kt = kh_row(t), *qt = qh_row(t), *ks = kh_row(sr);
+            float ka[KS][8], qa[KS][8], kb[KS][8];
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) {   // all operand loads first
+                const int c0 = 32 * kk + 8 * lk;
+                load8(kt + c0, t < n, ka[kk]);
+                load8(qt + c0, t < n, qa[kk]);
+                load8(ks + c0, sr < n, kb[kk]);
+            }
 #pragma unroll
             for (int kk = 0; kk < KS; ++kk) {
-                float ka[8], qa[8], kb[8];
+                const int c0 = 32 * kk + 8 * lk;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const int ch = 32 * kk + 8 * lk + e;
-                    const float gr = L.G[r][ch];
-                    const float et = exp2f(L.G[t][ch] - gr);
-                    const float es = exp2f(gr - L.G[sr][ch]);
-                    ka[e] = L.k[t][ch] * et;
-                    qa[e] = L.q[t][ch] * et;
-                    kb[e] = L.k[sr][ch] * es;
+                    const float gr = L.G[r][c0 + e];
+                    const float et = exp2f(L.G[t][c0 + e] - gr);
+                    ka[kk][e] *= et;
+                    qa[kk][e] *= et;
+                    kb[kk][e] *= exp2f(gr - L.G[sr][c0 + e]);
                 }
-                const Split8 b = split8(kb);
-                aA = mma3(split8(ka), b, aA);
-                aP = mma3(split8(qa), b, aP);
+                const Split8 b = split8(kb[kk]);
+                aA = mma3(split8(ka[kk]), b, aA);
+                aP = mma3(split8(qa[kk]), b, aP);
             }
         } else {
             // direct: lane owns row t = r + lr and columns s = r + 4 lk + j
             float da[4] = {0.f, 0.f, 0.f, 0.f}, dp[4] = {0.f, 0.f, 0.f, 0.f};
             const int t = r + lr;
+            const float *kt = kh_row(t), *qt = qh_row(t);
             for (int ch = 0; ch < DK; ++ch) {
-                const float gt = L.G[t][ch], kt = L.k[t][ch], qt = L.q[t][ch];
+                float kv = 0.f, qv = 0.f;
+                if (t < n) { kv = kt[ch]; qv = qt[ch]; }
+                const float gt = L.G[t][ch];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int sv = r + 4 * lk + j;
-                    const float e = exp2f(fminf(gt - L.G[sv][ch], 0.f)) * L.k[sv][ch];
-                    da[j] = fmaf(kt, e, da[j]);
-                    dp[j] = fmaf(qt, e, dp[j]);
+                    float ks = 0.f;
+                    if (sv < n) ks = kh_row(sv)[ch];
+                    const float e = exp2f(fminf(gt - L.G[sv][ch], 0.f)) * ks;
+                    da[j] = fmaf(kv, e, da[j]);
+                    dp[j] = fmaf(qv, e, dp[j]);
                 }
             }
-            // move to the MFMA result layout through this wave's scratch
-            // (the tile's block of A is written only by this wave)
+            // to the MFMA result layout through this wave's scratch
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 L.A[t][r + 4 * lk + j] = da[j];
@@ -340,25 +399,49 @@ __global__ __launch_bounds__(256) void kda_prefill_intra_kernel(PrefillParams p,
         for (int rr = 0; rr < 4; ++rr) {
             const int t = 16 * bt + 4 * lk + rr, sv = 16 * bs + lr;
             L.A[t][sv] = sv < t ? L.beta[t] * aA[rr] : 0.f;
-            Pg[t * kChunk + sv] = sv <= t ? aP[rr] : 0.f;
+            split_bits(sv <= t ? aP[rr] : 0.f, Ph[t * kChunk + sv], Pl[t * kChunk + sv]);
         }
     }
-    // 5. decayed factors for the scan: Q^ e^G, (K^ e^(G_C - G))^T, e^(G_C)
+    // 4. decayed factors for the scan: Q^ e^G (rows), (K^ e^(G_C - G))^T, e^(G_C)
     const int last = max(n - 1, 0);
-    for (int e = tid; e < kChunk * DK; e += 256) {
-        const int r = e / DK, i = e % DK;
-        ws.Qg[gh * kChunk * DK + r * DK + i] = L.q[r][i] * exp2f(L.G[r][i]);
+    for (int e8 = tid; e8 < kChunk * DK / 8; e8 += 256) {
+        const int r = e8 / (DK / 8), i0 = 8 * (e8 % (DK / 8));
+        float x[8];
+        load8(qh_row(r) + i0, r < n, x);
+        bf16x8 hv, lv;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float v = x[e] * exp2f(L.G[r][i0 + e]);
+            const __bf16 hb = (__bf16)v;
+            hv[e] = hb;
+            lv[e] = (__bf16)(v - (float)hb);
+        }
+        *reinterpret_cast<bf16x8 *>(ws.Q_hi + gh * kChunk * DK + r * DK + i0) = hv;
+        *reinterpret_cast<bf16x8 *>(ws.Q_lo + gh * kChunk * DK + r * DK + i0) = lv;
     }
-    for (int e = tid; e < kChunk * DK; e += 256) {
-        const int i = e / kChunk, r = e % kChunk;
-        ws.KdT[gh * DK * kChunk + e] = L.k[r][i] * exp2f(fminf(L.G[last][i] - L.G[r][i], 0.f));
+    const float *kT = ws.kT + gh * DK * kChunk;
+    for (int e8 = tid; e8 < kChunk * DK / 8; e8 += 256) {
+        const int i = e8 / (kChunk / 8), r0 = 8 * (e8 % (kChunk / 8));
+        const float gl = L.G[last][i];
+        float kx[8];
+        load8(kT + i * kChunk + r0, true, kx);   // rows past n are masked below
+        bf16x8 hv, lv;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int r = r0 + e;
+            float v = 0.f;
+            if (r < n) v = kx[e] * exp2f(fminf(gl - L.G[r][i], 0.f));
+            const __bf16 hb = (__bf16)v;
+            hv[e] = hb;
+            lv[e] = (__bf16)(v - (float)hb);
+        }
+        *reinterpret_cast<bf16x8 *>(ws.K_hi + gh * DK * kChunk + i * kChunk + r0) = hv;
+        *reinterpret_cast<bf16x8 *>(ws.K_lo + gh * DK * kChunk + i * kChunk + r0) = lv;
     }
     if (tid < DK) ws.gC[gh * DK + tid] = exp2f(L.G[last][tid]);
-    __syncthreads();   // q^ is free from here on: T lives in its place
 
-    // 6. T = (I + A)^-1 by 16 x 16 blocks
-    float(*T)[QW] = L.q;
-    for (int e = tid; e < kChunk * kChunk; e += 256) T[e / kChunk][e % kChunk] = 0.f;
+    // 5. T = (I + A)^-1 by 16 x 16 blocks
+    for (int e = tid; e < kChunk * kChunk; e += 256) L.T[e / kChunk][e % kChunk] = 0.f;
     __syncthreads();
     if (tid < 64) {   // diagonal blocks: column j of (I + A_bb)^-1
         const int b = tid / 16, j = tid % 16, o = 16 * b;
@@ -369,7 +452,7 @@ __global__ __launch_bounds__(256) void kda_prefill_intra_kernel(PrefillParams p,
 #pragma unroll
             for (int m = 0; m < i; ++m) acc = fmaf(-L.A[o + i][o + m], x[m], acc);
             x[i] = acc;
-            T[o + i][o + j] = i >= j ? acc : 0.f;
+            L.T[o + i][o + j] = i >= j ? acc : 0.f;
         }
     }
     __syncthreads();
@@ -378,7 +461,7 @@ __global__ __launch_bounds__(256) void kda_prefill_intra_kernel(PrefillParams p,
         for (int e = tid; e < b * 256; e += 256) {
             const int bp = e / 256, i = (e / 16) % 16, j = e % 16;
             float acc = 0.f;
-            for (int m = 16 * bp; m < 16 * b; ++m) acc = fmaf(L.A[16 * b + i][m], T[m][16 * bp + j], acc);
+            for (int m = 16 * bp; m < 16 * b; ++m) acc = fmaf(L.A[16 * b + i][m], L.T[m][16 * bp + j], acc);
             L.Z[bp][i][j] = acc;
         }
         __syncthreads();
@@ -387,13 +470,14 @@ __global__ __launch_bounds__(256) void kda_prefill_intra_kernel(PrefillParams p,
             const int bp = e / 256, i = (e / 16) % 16, j = e % 16;
             float acc = 0.f;
 #pragma unroll
-            for (int m = 0; m < 16; ++m) acc = fmaf(T[16 * b + i][16 * b + m], L.Z[bp][m][j], acc);
-            T[16 * b + i][16 * bp + j] = -acc;
+            for (int m = 0; m < 16; ++m) acc = fmaf(L.T[16 * b + i][16 * b + m], L.Z[bp][m][j], acc);
+            L.T[16 * b + i][16 * bp + j] = -acc;
         }
         __syncthreads();
     }
 
-    // 7. [W | U~] = T R with R = [diag(beta) K^ e^G | diag(beta) V]  (MFMA)
+    // 6. [W | U~] = T R with R = [diag(beta) K^ e^G | diag(beta) V]  (MFMA);
+    //    W is stored negated and split for the scan, U~ in fp32
     Split8 ta[4][2];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
@@ -401,7 +485,7 @@ __global__ __launch_bounds__(256) void kda_prefill_intra_kernel(PrefillParams p,
         for (int k2 = 0; k2 < 2; ++k2) {
             float x[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = T[16 * rt + lr][32 * k2 + 8 * lk + e];
+            for (int e = 0; e < 8; ++e) x[e] = L.T[16 * rt + lr][32 * k2 + 8 * lk + e];
             ta[rt][k2] = split8(x);
         }
     constexpr int NCT = (DK + DV) / 16;
@@ -414,10 +498,11 @@ __global__ __launch_bounds__(256) void kda_prefill_intra_kernel(PrefillParams p,
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
             float x[8];
+            if (isw) load8(kT + col * kChunk + 32 * k2 + 8 * lk, true, x);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int sv = 32 * k2 + 8 * lk + e;
-                if (isw) x[e] = L.beta[sv] * L.k[sv][col] * exp2f(L.G[sv][col]);
+                if (isw) x[e] = sv < n ? L.beta[sv] * x[e] * exp2f(L.G[sv][col]) : 0.f;
                 else x[e] = L.beta[sv] * vpre[ci - DK / 64][k2][e];
             }
             rb[k2] = split8(x);
@@ -430,8 +515,12 @@ __global__ __launch_bounds__(256) void kda_prefill_intra_kernel(PrefillParams p,
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
                 const int t = 16 * rt + 4 * lk + rr;
-                if (isw) ws.W[gh * kChunk * DK + t * DK + col] = acc[rr];
-                else ws.Ut[gh * kChunk * DV + t * DV + (col - DK)] = acc[rr];
+                if (isw) {
+                    const size_t o = gh * kChunk * DK + t * DK + col;
+                    split_bits(-acc[rr], ws.Wn_hi[o], ws.Wn_lo[o]);
+                } else {
+                    ws.Ut[gh * kChunk * DV + t * DV + (col - DK)] = acc[rr];
+                }
             }
         }
     }
@@ -447,41 +536,39 @@ __global__ __launch_bounds__(256) void kda_prefill_intra_kernel(PrefillParams p,
 template <int DK>
 struct ScanOps {
     static constexpr int KS = DK / 32, TS = DK / 64;
-    float w[KS][8];        // W rows (A operand, K = d_k)
-    float q[KS][8];        // Q^ e^G rows
-    float pm[2][8];        // P rows (K = token)
-    float kd[TS][2][8];    // Kd^T rows (K = token)
+    Split8 w[KS];          // -W rows (A operand, K = d_k), pre-split
+    Split8 q[KS];          // Q^ e^G rows
+    Split8 pm[2];          // P rows (K = token)
+    Split8 kd[TS][2];      // Kd^T rows (K = token)
     float ut[4];           // U~ (result layout)
     float gc[TS][4];       // e^(G_C) of the state rows this lane updates
 };
+
+__device__ __forceinline__ Split8 load_split8(const uint16_t *hi, const uint16_t *lo, size_t off) {
+    Split8 v;
+    v.hi = *reinterpret_cast<const bf16x8 *>(hi + off);
+    v.lo = *reinterpret_cast<const bf16x8 *>(lo + off);
+    return v;
+}
 
 template <int DK, int DV>
 __device__ __forceinline__ void scan_load(const PrefillWs &ws, size_t gh, int wave, int lr, int lk, int j0,
                                           ScanOps<DK> &o) {
     constexpr int KS = DK / 32, TS = DK / 64;
-    const float *W = ws.W + gh * kChunk * DK + (16 * wave + lr) * DK + 8 * lk;
-    const float *Q = ws.Qg + gh * kChunk * DK + (16 * wave + lr) * DK + 8 * lk;
+    const size_t rw = gh * kChunk * DK + (16 * wave + lr) * DK + 8 * lk;
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
-        *reinterpret_cast<float4 *>(&o.w[k][0]) = *reinterpret_cast<const float4 *>(W + 32 * k);
-        *reinterpret_cast<float4 *>(&o.w[k][4]) = *reinterpret_cast<const float4 *>(W + 32 * k + 4);
-        *reinterpret_cast<float4 *>(&o.q[k][0]) = *reinterpret_cast<const float4 *>(Q + 32 * k);
-        *reinterpret_cast<float4 *>(&o.q[k][4]) = *reinterpret_cast<const float4 *>(Q + 32 * k + 4);
+        o.w[k] = load_split8(ws.Wn_hi, ws.Wn_lo, rw + 32 * k);
+        o.q[k] = load_split8(ws.Q_hi, ws.Q_lo, rw + 32 * k);
     }
-    const float *P = ws.P + gh * kChunk * kChunk + (16 * wave + lr) * kChunk + 8 * lk;
+    const size_t rp = gh * kChunk * kChunk + (16 * wave + lr) * kChunk + 8 * lk;
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        *reinterpret_cast<float4 *>(&o.pm[k][0]) = *reinterpret_cast<const float4 *>(P + 32 * k);
-        *reinterpret_cast<float4 *>(&o.pm[k][4]) = *reinterpret_cast<const float4 *>(P + 32 * k + 4);
-    }
+    for (int k = 0; k < 2; ++k) o.pm[k] = load_split8(ws.P_hi, ws.P_lo, rp + 32 * k);
 #pragma unroll
     for (int m = 0; m < TS; ++m) {
-        const float *K = ws.KdT + gh * DK * kChunk + (16 * (TS * wave + m) + lr) * kChunk + 8 * lk;
+        const size_t rk = gh * DK * kChunk + (16 * (TS * wave + m) + lr) * kChunk + 8 * lk;
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            *reinterpret_cast<float4 *>(&o.kd[m][k][0]) = *reinterpret_cast<const float4 *>(K + 32 * k);
-            *reinterpret_cast<float4 *>(&o.kd[m][k][4]) = *reinterpret_cast<const float4 *>(K + 32 * k + 4);
-        }
+        for (int k = 0; k < 2; ++k) o.kd[m][k] = load_split8(ws.K_hi, ws.K_lo, rk + 32 * k);
 #pragma unroll
         for (int r = 0; r < 4; ++r) o.gc[m][r] = ws.gC[gh * DK + 16 * (TS * wave + m) + 4 * lk + r];
     }
@@ -590,8 +677,8 @@ __global__ __launch_bounds__(256) void kda_prefill_scan_kernel(PrefillParams p, 
         zero3(ao);
 #pragma unroll
         for (int k = 0; k < KS; ++k) {
-            mma3s(split8(o.w[k], -1.0f), sb[k], au);
-            mma3s(split8(o.q[k]), sb[k], ao);
+            mma3s(o.w[k], sb[k], au);
+            mma3s(o.q[k], sb[k], ao);
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) U[16 * wave + 4 * lk + r][lr] = o.ut[r] + sum3(au, r);
@@ -606,7 +693,7 @@ __global__ __launch_bounds__(256) void kda_prefill_scan_kernel(PrefillParams p, 
         }
         // O += P U  (P rows beyond the chunk and above the diagonal are 0)
 #pragma unroll
-        for (int k = 0; k < 2; ++k) mma3s(split8(o.pm[k]), ub[k], ao);
+        for (int k = 0; k < 2; ++k) mma3s(o.pm[k], ub[k], ao);
 #pragma unroll
         for (int r = 0; r < 4; ++r) ypend[r] = sum3(ao, r);
         ypend_t0 = t0;
@@ -617,7 +704,7 @@ __global__ __launch_bounds__(256) void kda_prefill_scan_kernel(PrefillParams p, 
             Acc3 as;
             zero3(as);
 #pragma unroll
-            for (int k = 0; k < 2; ++k) mma3s(split8(o.kd[m][k]), ub[k], as);
+            for (int k = 0; k < 2; ++k) mma3s(o.kd[m][k], ub[k], as);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = 16 * (TS * wave + m) + 4 * lk + r;
@@ -698,11 +785,16 @@ static kda_status launch_prefill_typed(const PrefillParams &p, hipStream_t strea
     ws.vv = reinterpret_cast<float *>(base + l.vv);
     ws.la = reinterpret_cast<float *>(base + l.la);
     ws.beta = reinterpret_cast<float *>(base + l.beta);
-    ws.W = reinterpret_cast<float *>(base + l.W);
+    ws.kT = reinterpret_cast<float *>(base + l.kT);
+    ws.Wn_hi = reinterpret_cast<uint16_t *>(base + l.Wn_hi);
+    ws.Wn_lo = reinterpret_cast<uint16_t *>(base + l.Wn_lo);
+    ws.Q_hi = reinterpret_cast<uint16_t *>(base + l.Q_hi);
+    ws.Q_lo = reinterpret_cast<uint16_t *>(base + l.Q_lo);
+    ws.K_hi = reinterpret_cast<uint16_t *>(base + l.K_hi);
+    ws.K_lo = reinterpret_cast<uint16_t *>(base + l.K_lo);
+    ws.P_hi = reinterpret_cast<uint16_t *>(base + l.P_hi);
+    ws.P_lo = reinterpret_cast<uint16_t *>(base + l.P_lo);
     ws.Ut = reinterpret_cast<float *>(base + l.Ut);
-    ws.Qg = reinterpret_cast<float *>(base + l.Qg);
-    ws.KdT = reinterpret_cast<float *>(base + l.KdT);
-    ws.P = reinterpret_cast<float *>(base + l.P);
     ws.gC = reinterpret_cast<float *>(base + l.gC);
     ws.G_max = p.total_T / kChunk + p.N_seq;
 
