@@ -15,9 +15,9 @@
 //
 // Kernels, in stream order:
 //   meta   one workgroup: validates cu_seqlens, chunk offsets per sequence
-//   prep   one wave per (token, head): conv + SiLU, L2 norms, log2(alpha), beta
-//   intra  one workgroup per (chunk, head): prefix sums, A, P, the triangular
-//          solve for W and U~, the decayed Q and K factors
+//   intra  one workgroup per (chunk, head): conv + SiLU, L2 norms and gates of
+//          the chunk's tokens, prefix sums, A, P, the triangular solve for W
+//          and U~, the decayed Q and K factors
 //   scan   one workgroup per (sequence, head, 16 columns of d_v): the fp32 state
 //          carried from chunk to chunk (state columns are independent given the
 //          chunk factors), unnormalised outputs O written to y
@@ -36,9 +36,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 // lo = bf16(x - hi)), in the row-major layout the scan's operand loads read.
 struct PrefillWs {
     int32_t *meta;            // [0]: 1 if cu_seqlens is valid; [1 + s]: first chunk of s, s <= N
-    float *qh, *kh, *vv;      // [T, H, d]  fp32
-    float *la;                // [T, H, d_k]  log2(alpha)
-    float *beta;              // [T, H]
+    float *qh, *kh, *vv;      // [G, 64, H, d]  fp32, rows past a chunk's end unused
     float *kT;                // [G, H, d_k, 64]  k^ of each chunk, transposed
     uint16_t *Wn_hi, *Wn_lo;  // [G, H, 64, d_k]  -W
     uint16_t *Q_hi, *Q_lo;    // [G, H, 64, d_k]  Q^ e^G
@@ -50,23 +48,21 @@ struct PrefillWs {
 };
 
 struct WsLayout {
-    size_t meta, qh, kh, vv, la, beta, kT, Wn_hi, Wn_lo, Q_hi, Q_lo, K_hi, K_lo, P_hi, P_lo, Ut, gC, total;
+    size_t meta, qh, kh, vv, kT, Wn_hi, Wn_lo, Q_hi, Q_lo, K_hi, K_lo, P_hi, P_lo, Ut, gC, total;
 };
 
 static size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
 static WsLayout ws_layout(int H, int dk, int dv, int total_T, int N_seq) {
     const size_t G = (size_t)total_T / kChunk + (size_t)N_seq;
-    const size_t TH = (size_t)total_T * H, GH = G * H;
+    const size_t GH = G * H;
     WsLayout l{};
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes); return o; };
     l.meta = take(sizeof(int32_t) * (N_seq + 2));
-    l.qh = take(4 * TH * dk);
-    l.kh = take(4 * TH * dk);
-    l.vv = take(4 * TH * dv);
-    l.la = take(4 * TH * dk);
-    l.beta = take(4 * TH);
+    l.qh = take(4 * GH * kChunk * dk);
+    l.kh = take(4 * GH * kChunk * dk);
+    l.vv = take(4 * GH * kChunk * dv);
     l.kT = take(4 * GH * dk * kChunk);
     l.Wn_hi = take(2 * GH * kChunk * dk);
     l.Wn_lo = take(2 * GH * kChunk * dk);
@@ -122,74 +118,6 @@ __global__ void kda_prefill_meta_kernel(PrefillParams p, PrefillWs ws) {
 }
 
 // ---------------------------------------------------------------------------
-// prep: one wave per (token, head)
-// ---------------------------------------------------------------------------
-template <int DK, int DV, typename Tin>
-__global__ __launch_bounds__(256) void kda_prefill_prep_kernel(PrefillParams p, PrefillWs ws) {
-    constexpr int CH = 2 * DK + DV, EC = CH / kWave, EK = DK / kWave, EV = DV / kWave;
-    const int lane = threadIdx.x % kWave;
-    const int t = blockIdx.x * 4 + threadIdx.x / kWave;
-    const int h = blockIdx.y, H = p.H;
-    if (t >= p.total_T || ws.meta[0] != 1) return;
-    const int s = upper_index(p.cu_seqlens, p.N_seq + 1, t);   // cu[s] <= t < cu[s+1]
-    const int slot = p.slot_idx[s];
-    if (!slot_ok(slot, p.n_slots)) return;
-    const int pos = t - p.cu_seqlens[s];
-    const Tin *win = static_cast<const Tin *>(p.window) + ((size_t)slot * H + h) * 3 * CH;
-    float conv[EC];
-#pragma unroll
-    for (int e = 0; e < EC; ++e) {
-        const int c = lane + kWave * e;
-        const Tin *src;
-        int stride, off;
-        if (c < DK) { src = static_cast<const Tin *>(p.x_q); stride = DK; off = c; }
-        else if (c < 2 * DK) { src = static_cast<const Tin *>(p.x_k); stride = DK; off = c - DK; }
-        else { src = static_cast<const Tin *>(p.x_v); stride = DV; off = c - 2 * DK; }
-        const float4 w = *reinterpret_cast<const float4 *>(p.conv_wt + ((size_t)h * CH + c) * 4);
-        float x[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int q = pos - 3 + j;   // position of tap j's input in the sequence
-            x[j] = q >= 0 ? to_f32(src[((size_t)(t - 3 + j) * H + h) * stride + off])
-                          : to_f32(win[(q + 3) * CH + c]);
-        }
-        float acc = w.x * x[0];
-        acc = fmaf(w.y, x[1], acc);
-        acc = fmaf(w.z, x[2], acc);
-        acc = fmaf(w.w, x[3], acc);
-        conv[e] = p.silu ? acc * sigmoid(acc) : acc;
-    }
-    // channels c = lane + 64 e: e < EK are q, EK <= e < 2 EK are k, the rest v
-    float sq = 0.f, sk = 0.f;
-#pragma unroll
-    for (int e = 0; e < EK; ++e) {
-        sq = fmaf(conv[e], conv[e], sq);
-        sk = fmaf(conv[EK + e], conv[EK + e], sk);
-    }
-    sq = wave_sum(sq);
-    sk = wave_sum(sk);
-    const float rq = p.q_scale / sqrtf(sq + p.l2_eps);
-    const float rk = 1.0f / sqrtf(sk + p.l2_eps);
-    const size_t th = (size_t)t * H + h;
-    const Tin *g = static_cast<const Tin *>(p.g) + th * DK;
-    // the chunk-transposed copy of k^ (row i of chunk g holds its 64 tokens)
-    const size_t kt_base = ((size_t)(ws.meta[1 + s] + pos / kChunk) * H + h) * DK * kChunk + pos % kChunk;
-#pragma unroll
-    for (int e = 0; e < EK; ++e) {
-        const int i = lane + kWave * e;
-        ws.qh[th * DK + i] = conv[e] * rq;
-        ws.kh[th * DK + i] = conv[EK + e] * rk;
-        ws.kT[kt_base + (size_t)i * kChunk] = conv[EK + e] * rk;
-        // alpha below 2^-200 is 0 in fp32 either way; the floor keeps the
-        // prefix sums finite (g = +inf would give -inf - -inf = NaN later)
-        ws.la[th * DK + i] = fmaxf(-expf(p.A[h * DK + i]) * softplus(to_f32(g[i])) * kLog2e, -200.f);
-    }
-#pragma unroll
-    for (int e = 0; e < EV; ++e) ws.vv[th * DV + lane + kWave * e] = conv[2 * EK + e];
-    if (lane == 0) ws.beta[th] = sigmoid(to_f32(static_cast<const Tin *>(p.b)[th]));
-}
-
-// ---------------------------------------------------------------------------
 // intra: one workgroup (4 waves) per (chunk, head).  The Gram matrices A, P,
 // the triangular inverse T = (I + A)^-1 and [W | U~] = T [diag(beta) K^ e^G |
 // diag(beta) V] are formed here; every contraction runs on MFMA in bf16x3.
@@ -209,13 +137,135 @@ template <int DK, int DV>
 struct __align__(16) IntraLds {
     static constexpr int KW = DK + 1;   // padded rows: column reads hit distinct banks
     float G[kChunk][KW];                // log2-decay prefix sums
-    float A[kChunk][kChunk + 1];        // beta_t (K K^T * decay), strictly lower part used
-    float T[kChunk][kChunk + 4];        // (I + A)^-1
-    float Z[3][16][17];                 // block-inverse scratch
-    float D[4][16][17];                 // per-wave scratch of the direct tile path
+    union {
+        struct {
+            float A[kChunk][kChunk + 1];   // beta_t (K K^T * decay), strictly lower part used
+            float T[kChunk][kChunk + 4];   // (I + A)^-1
+            float Z[3][16][17];            // block-inverse scratch
+            float D[4][16][17];            // per-wave scratch of the direct tile path
+        };
+        float kt[DK][kChunk + 1];          // k^ of the chunk, transposed (first phase only)
+    };
     float beta[kChunk];
     int safe[4];
 };
+
+// NC consecutive input channels of one row, fetched in one load
+template <typename Tin, int NC> struct ChRaw;
+template <> struct ChRaw<uint16_t, 2> {
+    using T = uint32_t;
+    __device__ static float get(T r, int e) { return __uint_as_float(e ? (r & 0xffff0000u) : (r << 16)); }
+};
+template <> struct ChRaw<uint16_t, 1> {
+    using T = uint16_t;
+    __device__ static float get(T r, int) { return __uint_as_float((uint32_t)r << 16); }
+};
+template <> struct ChRaw<float, 2> {
+    using T = float2;
+    __device__ static float get(T r, int e) { return e ? r.y : r.x; }
+};
+template <> struct ChRaw<float, 1> {
+    using T = float;
+    __device__ static float get(T r, int) { return r; }
+};
+
+// Conv + SiLU over one of q, k, v for the n tokens of a chunk, one wave; the
+// lane owns channels NC*lane .. NC*lane + NC - 1.  MODE 0: q (L2 norm and q
+// scale), 1: k (L2 norm, and a transposed copy into kt, zero past n), 2: v.
+// The three inputs before the chunk come from the conv window at chunk 0,
+// else from the sequence itself.  All 64 rows go to out (layout [64, H, NC*64]
+// from the chunk's first row; rows past n hold values of no meaning).
+template <int NC, int MODE, typename Tin>
+__device__ __forceinline__ void prep_tensor(const PrefillParams &p, const Tin *x, const Tin *win, int choff,
+                                            int CH, int c, int t0, int n, int h, int lane, float *out,
+                                            float (*kt)[kChunk + 1]) {
+    using R = ChRaw<Tin, NC>;
+    using RT = typename R::T;
+    constexpr int D = NC * kWave;
+    const int H = p.H, cb = NC * lane;
+    float w[NC][4];
+#pragma unroll
+    for (int e = 0; e < NC; ++e) {
+        const float4 v = *reinterpret_cast<const float4 *>(p.conv_wt + ((size_t)h * CH + choff + cb + e) * 4);
+        w[e][0] = v.x; w[e][1] = v.y; w[e][2] = v.z; w[e][3] = v.w;
+    }
+    RT raw[kChunk + 3];   // rows -3 .. 63 of the chunk, all loads issued first
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        const Tin *src = c == 0 ? win + j * CH + choff + cb : x + ((size_t)(t0 - 3 + j) * H + h) * D + cb;
+        raw[j] = *reinterpret_cast<const RT *>(src);
+    }
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j) {
+        const int r = min(j, n - 1);   // rows past the chunk repeat its last row (never stored)
+        raw[3 + j] = *reinterpret_cast<const RT *>(x + ((size_t)(t0 + r) * H + h) * D + cb);
+    }
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j) {
+        float y[NC];
+#pragma unroll
+        for (int e = 0; e < NC; ++e) {
+            float acc = w[e][0] * R::get(raw[j], e);
+            acc = fmaf(w[e][1], R::get(raw[j + 1], e), acc);
+            acc = fmaf(w[e][2], R::get(raw[j + 2], e), acc);
+            acc = fmaf(w[e][3], R::get(raw[j + 3], e), acc);
+            y[e] = p.silu ? acc * sigmoid(acc) : acc;
+        }
+        if (MODE < 2) {
+            float ss = 0.f;
+#pragma unroll
+            for (int e = 0; e < NC; ++e) ss = fmaf(y[e], y[e], ss);
+            ss = wave_sum(ss);
+            const float sc = (MODE == 0 ? p.q_scale : 1.0f) / sqrtf(ss + p.l2_eps);
+#pragma unroll
+            for (int e = 0; e < NC; ++e) y[e] *= sc;
+        }
+        float *dst = out + ((size_t)j * H + h) * D + cb;
+        if (NC == 2) *reinterpret_cast<float2 *>(dst) = make_float2(y[0], y[NC - 1]);
+        else dst[0] = y[0];
+        if (MODE == 1) {
+#pragma unroll
+            for (int e = 0; e < NC; ++e) kt[cb + e][j] = j < n ? y[e] : 0.f;
+        }
+    }
+}
+
+// log2(alpha) of the chunk's tokens, its prefix sums over the chunk into G
+// (rows past n add nothing) and beta (0 past n); one wave.
+template <int NC, int DK, typename Tin>
+__device__ __forceinline__ void prep_gates(const PrefillParams &p, int t0, int n, int h, int lane,
+                                           float (*G)[DK + 1], float *beta) {
+    using R = ChRaw<Tin, NC>;
+    using RT = typename R::T;
+    const int H = p.H, cb = NC * lane;
+    const Tin *g = static_cast<const Tin *>(p.g);
+    RT raw[kChunk];
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j) {
+        const int r = min(j, n - 1);
+        raw[j] = *reinterpret_cast<const RT *>(g + ((size_t)(t0 + r) * H + h) * DK + cb);
+    }
+    const Tin bv = static_cast<const Tin *>(p.b)[(size_t)(t0 + min(lane, n - 1)) * H + h];
+    float ea[NC], acc[NC];
+#pragma unroll
+    for (int e = 0; e < NC; ++e) {
+        ea[e] = expf(p.A[h * DK + cb + e]);
+        acc[e] = 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j) {
+#pragma unroll
+        for (int e = 0; e < NC; ++e) {
+            // alpha below 2^-200 is 0 in fp32 either way; the floor keeps the
+            // prefix sums finite (g = +inf would give -inf - -inf = NaN later)
+            const float la = fmaxf(-ea[e] * softplus(R::get(raw[j], e)) * kLog2e, -200.f);
+            acc[e] += j < n ? la : 0.f;
+            G[j][cb + e] = acc[e];
+        }
+    }
+    beta[lane] = lane < n ? sigmoid(to_f32(bv)) : 0.f;
+}
+
 
 constexpr float kSafeSpan = 60.f;
 
@@ -239,7 +289,7 @@ __device__ __forceinline__ void load8(const float *src, bool valid, float *x) {
     x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
 }
 
-template <int DK, int DV>
+template <int DK, int DV, typename Tin>
 __global__ __launch_bounds__(256, 2) void kda_prefill_intra_kernel(PrefillParams p, PrefillWs ws) {
     constexpr int KS = DK / 32;
     __shared__ IntraLds<DK, DV> L;
@@ -250,34 +300,43 @@ __global__ __launch_bounds__(256, 2) void kda_prefill_intra_kernel(PrefillParams
     const int32_t *cs = ws.meta + 1;
     if (gidx >= cs[p.N_seq]) return;
     const int s = upper_index(cs, p.N_seq + 1, gidx);
-    if (!slot_ok(p.slot_idx[s], p.n_slots)) return;
+    const int slot = p.slot_idx[s];
+    if (!slot_ok(slot, p.n_slots)) return;
     const int c = gidx - cs[s];
     const int t0 = p.cu_seqlens[s] + c * kChunk;
     const int n = min(kChunk, p.cu_seqlens[s + 1] - t0);
     const size_t gh = (size_t)gidx * H + h;
-    const size_t row0 = (size_t)t0 * H + h;              // workspace row of token t0
+    const size_t row0 = (size_t)gidx * kChunk * H + h;   // workspace row of the chunk's first token
     const size_t rstride = (size_t)H;                    // rows between consecutive tokens
     auto kh_row = [&](int r) { return ws.kh + (row0 + r * rstride) * DK; };
     auto qh_row = [&](int r) { return ws.qh + (row0 + r * rstride) * DK; };
 
-    // 1. log2 alpha of the chunk into LDS (coalesced; rows >= n are zero),
-    //    then per-channel prefix sums: lane (channel, part) sums its run of
-    //    rows in registers, and the parts are chained through LDS
-    for (int e = tid; e < kChunk * DK / 4; e += 256) {
-        const int r = e / (DK / 4), i = 4 * (e % (DK / 4));
-        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (r < n) v = *reinterpret_cast<const float4 *>(ws.la + (row0 + r * rstride) * DK + i);
-        L.G[r][i] = v.x; L.G[r][i + 1] = v.y; L.G[r][i + 2] = v.z; L.G[r][i + 3] = v.w;
-    }
-    if (tid < kChunk) L.beta[tid] = tid < n ? ws.beta[row0 + tid * rstride] : 0.f;
-    constexpr int NPART = 256 / DK, RP = kChunk / NPART;
-    const int pch = tid % DK, part = tid / DK;
-    float run[RP];
-    __syncthreads();
+    // 1. the chunk's tokens: wave 0 q^, wave 1 k^, wave 2 v (to the
+    //    workspace, L2-resident for the steps below), wave 3 the decay prefix
+    //    sums and beta (LDS)
     {
-        float acc = 0.f;
-#pragma unroll
-        for (int j = 0; j < RP; ++j) { acc += L.G[part * RP + j][pch]; run[j] = acc; }
+        constexpr int CH = 2 * DK + DV;
+        const Tin *win = static_cast<const Tin *>(p.window) + ((size_t)slot * H + h) * 3 * CH;
+        const size_t cbase = (size_t)gidx * kChunk * H;
+        const Tin *xq = static_cast<const Tin *>(p.x_q), *xk = static_cast<const Tin *>(p.x_k);
+        const Tin *xv = static_cast<const Tin *>(p.x_v);
+        if (wave == 0)
+            prep_tensor<DK / 64, 0>(p, xq, win, 0, CH, c, t0, n, h, lane, ws.qh + cbase * DK, L.kt);
+        else if (wave == 1)
+            prep_tensor<DK / 64, 1>(p, xk, win, DK, CH, c, t0, n, h, lane, ws.kh + cbase * DK, L.kt);
+        else if (wave == 2)
+            prep_tensor<DV / 64, 2>(p, xv, win, 2 * DK, CH, c, t0, n, h, lane, ws.vv + cbase * DV, L.kt);
+        else
+            prep_gates<DK / 64, DK, Tin>(p, t0, n, h, lane, L.G, L.beta);
+    }
+    __syncthreads();
+    // the transposed k^ (zero past n) to the workspace: steps 4 and 6 read it
+    // by channel
+    float *const kT = ws.kT + gh * DK * kChunk;
+    for (int e = tid; e < DK * kChunk / 4; e += 256) {
+        const int i = e / (kChunk / 4), r0 = 4 * (e % (kChunk / 4));
+        *reinterpret_cast<float4 *>(kT + i * kChunk + r0) =
+            make_float4(L.kt[i][r0], L.kt[i][r0 + 1], L.kt[i][r0 + 2], L.kt[i][r0 + 3]);
     }
     // the V operand of step 7 is read now, so its latency hides behind steps 3-6
     constexpr int NU = DV / 64;                  // U~ column tiles per wave
@@ -293,20 +352,6 @@ __global__ __launch_bounds__(256, 2) void kda_prefill_intra_kernel(PrefillParams
                 vpre[m][k2][e] = sv < n ? ws.vv[(row0 + sv * rstride) * DV + col] : 0.f;
             }
     }
-    __syncthreads();   // every part has read its raw rows
-#pragma unroll
-    for (int j = 0; j < RP; ++j) L.G[part * RP + j][pch] = run[j];
-    __syncthreads();
-    {
-        float off = 0.f;   // totals of the earlier parts, in order
-        for (int q = 0; q < part; ++q) off += L.G[q * RP + RP - 1][pch];
-        __syncthreads();
-        if (part > 0) {
-#pragma unroll
-            for (int j = 0; j < RP; ++j) L.G[part * RP + j][pch] = run[j] + off;
-        }
-    }
-    __syncthreads();
     // 2. per 16-token block: may the diagonal tile use the scaled factors?
     {
         float span = 0.f;
@@ -419,12 +464,11 @@ __global__ __launch_bounds__(256, 2) void kda_prefill_intra_kernel(PrefillParams
         *reinterpret_cast<bf16x8 *>(ws.Q_hi + gh * kChunk * DK + r * DK + i0) = hv;
         *reinterpret_cast<bf16x8 *>(ws.Q_lo + gh * kChunk * DK + r * DK + i0) = lv;
     }
-    const float *kT = ws.kT + gh * DK * kChunk;
     for (int e8 = tid; e8 < kChunk * DK / 8; e8 += 256) {
         const int i = e8 / (kChunk / 8), r0 = 8 * (e8 % (kChunk / 8));
         const float gl = L.G[last][i];
         float kx[8];
-        load8(kT + i * kChunk + r0, true, kx);   // rows past n are masked below
+        load8(kT + i * kChunk + r0, true, kx);
         bf16x8 hv, lv;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -783,8 +827,6 @@ static kda_status launch_prefill_typed(const PrefillParams &p, hipStream_t strea
     ws.qh = reinterpret_cast<float *>(base + l.qh);
     ws.kh = reinterpret_cast<float *>(base + l.kh);
     ws.vv = reinterpret_cast<float *>(base + l.vv);
-    ws.la = reinterpret_cast<float *>(base + l.la);
-    ws.beta = reinterpret_cast<float *>(base + l.beta);
     ws.kT = reinterpret_cast<float *>(base + l.kT);
     ws.Wn_hi = reinterpret_cast<uint16_t *>(base + l.Wn_hi);
     ws.Wn_lo = reinterpret_cast<uint16_t *>(base + l.Wn_lo);
@@ -800,9 +842,7 @@ static kda_status launch_prefill_typed(const PrefillParams &p, hipStream_t strea
 
     hipLaunchKernelGGL(kda_prefill_meta_kernel, dim3(1), dim3(64), 0, stream, p, ws);
     if (p.total_T > 0) {
-        const dim3 tok_grid((unsigned)((p.total_T + 3) / 4), (unsigned)p.H);
-        hipLaunchKernelGGL((kda_prefill_prep_kernel<DK, DV, Tin>), tok_grid, dim3(256), 0, stream, p, ws);
-        hipLaunchKernelGGL((kda_prefill_intra_kernel<DK, DV>), dim3((unsigned)ws.G_max, (unsigned)p.H),
+        hipLaunchKernelGGL((kda_prefill_intra_kernel<DK, DV, Tin>), dim3((unsigned)ws.G_max, (unsigned)p.H),
                            dim3(256), 0, stream, p, ws);
     }
     hipLaunchKernelGGL((kda_prefill_scan_kernel<DK, DV, Tin>),
