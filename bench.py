@@ -53,12 +53,16 @@ def verify_bytes_per_seq_head(T=8, dk=128, dv=128, B=16, in_bytes=2):
             + (dk + ch * 4 + dv) * 4 / B)                     # params
 
 
+# the files that define the decode kernel and its launch: the counter
+# summary is stale once any of them changes
+DECODE_SOURCES = ("kda_recurrent.hip", "kda_device.h", "kda_internal.h")
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     d = os.path.join(ROOT, "linear_attention_recurrent_kda_amd", "csrc")
-    for f in sorted(os.listdir(d)):
-        if f.endswith((".hip", ".h")):
-            h.update(open(os.path.join(d, f), "rb").read())
+    for f in DECODE_SOURCES:
+        h.update(open(os.path.join(d, f), "rb").read())
     return h.hexdigest()[:16]
 
 
