@@ -36,8 +36,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 // lo = bf16(x - hi)), in the row-major layout the scan's operand loads read.
 struct PrefillWs {
     int32_t *meta;            // [0]: 1 if cu_seqlens is valid; [1 + s]: first chunk of s, s <= N
-    float *qh, *kh, *vv;      // [G, 64, H, d]  fp32, rows past a chunk's end unused
-    float *kT;                // [G, H, d_k, 64]  k^ of each chunk, transposed
+    float *vv;                // [G, 64, H, d_v]  conv'd v, rows past a chunk's end unused
     uint16_t *Wn_hi, *Wn_lo;  // [G, H, 64, d_k]  -W
     uint16_t *Q_hi, *Q_lo;    // [G, H, 64, d_k]  Q^ e^G
     uint16_t *K_hi, *K_lo;    // [G, H, d_k, 64]  (K^ e^(G_C - G))^T
@@ -48,7 +47,7 @@ struct PrefillWs {
 };
 
 struct WsLayout {
-    size_t meta, qh, kh, vv, kT, Wn_hi, Wn_lo, Q_hi, Q_lo, K_hi, K_lo, P_hi, P_lo, Ut, gC, total;
+    size_t meta, vv, Wn_hi, Wn_lo, Q_hi, Q_lo, K_hi, K_lo, P_hi, P_lo, Ut, gC, total;
 };
 
 static size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
@@ -60,10 +59,7 @@ static WsLayout ws_layout(int H, int dk, int dv, int total_T, int N_seq) {
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes); return o; };
     l.meta = take(sizeof(int32_t) * (N_seq + 2));
-    l.qh = take(4 * GH * kChunk * dk);
-    l.kh = take(4 * GH * kChunk * dk);
     l.vv = take(4 * GH * kChunk * dv);
-    l.kT = take(4 * GH * dk * kChunk);
     l.Wn_hi = take(2 * GH * kChunk * dk);
     l.Wn_lo = take(2 * GH * kChunk * dk);
     l.Q_hi = take(2 * GH * kChunk * dk);
@@ -118,9 +114,10 @@ __global__ void kda_prefill_meta_kernel(PrefillParams p, PrefillWs ws) {
 }
 
 // ---------------------------------------------------------------------------
-// intra: one workgroup (4 waves) per (chunk, head).  The Gram matrices A, P,
-// the triangular inverse T = (I + A)^-1 and [W | U~] = T [diag(beta) K^ e^G |
-// diag(beta) V] are formed here; every contraction runs on MFMA in bf16x3.
+// intra: one workgroup (8 waves) per (chunk, head).  The chunk's tokens are
+// first brought in (conv + SiLU, L2 norms, gates); then the Gram matrices A,
+// P, the triangular inverse T = (I + A)^-1 and [W | U~] = T [diag(beta) K^ e^G
+// | diag(beta) V] are formed; every contraction runs on MFMA in bf16x3.
 //
 // Gram tiles are 16 x 16 token blocks.  For a t-block starting at token r,
 // e^(G_t - G_s) = e^(G_t - G_r) e^(G_r - G_s): the first factor is <= 1 for
@@ -130,25 +127,57 @@ __global__ void kda_prefill_meta_kernel(PrefillParams p, PrefillWs ws) {
 // (checked per block), otherwise the tile is summed directly with one
 // exponential per term.
 //
-// q^ and k^ are read from the workspace (they stay in L2 across the tiles);
-// LDS holds only the decay prefix sums, A and T, so two workgroups share a CU.
+// LDS holds q^, k^ (rows, zero past the chunk's end), the decay prefix sums,
+// A and T: about 143 KiB at d_k = 128, one workgroup per CU.  Only v goes
+// through the workspace (L2).
 // ---------------------------------------------------------------------------
+constexpr int kIntraThreads = 512;
+constexpr int kIntraWaves = kIntraThreads / kWave;
+
 template <int DK, int DV>
 struct __align__(16) IntraLds {
-    static constexpr int KW = DK + 1;   // padded rows: column reads hit distinct banks
+    static constexpr int KW = DK + 1;   // odd pitch: column reads hit distinct banks
+    static constexpr int RW = DK + 4;   // 16-byte rows for vector reads
     float G[kChunk][KW];                // log2-decay prefix sums
-    union {
-        struct {
-            float A[kChunk][kChunk + 1];   // beta_t (K K^T * decay), strictly lower part used
-            float T[kChunk][kChunk + 4];   // (I + A)^-1
-            float Z[3][16][17];            // block-inverse scratch
-            float D[4][16][17];            // per-wave scratch of the direct tile path
-        };
-        float kt[DK][kChunk + 1];          // k^ of the chunk, transposed (first phase only)
-    };
+    float Q[kChunk][RW];                // q^
+    float K[kChunk][RW];                // k^
+    float A[kChunk][kChunk + 1];        // beta_t (K K^T * decay), strictly lower part used
+    float T[kChunk][kChunk + 4];        // (I + A)^-1
+    float Z[3][16][17];                 // block-inverse scratch
+    float D[kIntraWaves][16][17];       // per-wave scratch of the direct tile path
     float beta[kChunk];
     int safe[4];
 };
+
+// Sum over the 64 lanes of a wave (all lanes active), every lane receiving
+// the same value: DPP adds inside each row of 16 lanes (pair, quad, half-row
+// and row mirrors), row broadcasts carry the row sums up to lane 63, which is
+// read back as a scalar.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_add(float v) {
+    const int x = __builtin_bit_cast(int, v);
+    return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, x, CTRL, ROWS, 0xF, false));
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+    v = dpp_add<0xB1, 0xF>(v);    // quad_perm [1,0,3,2]
+    v = dpp_add<0x4E, 0xF>(v);    // quad_perm [2,3,0,1]
+    v = dpp_add<0x141, 0xF>(v);   // row_half_mirror
+    v = dpp_add<0x140, 0xF>(v);   // row_mirror
+    v = dpp_add<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
+    v = dpp_add<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+// Hardware exp2 / log2 / reciprocal forms for the per-token preparation
+// (about 1 ulp each; the chunk algebra's bf16x3 contractions are ~1e-5).
+__device__ __forceinline__ float silu_hw(float x) {
+    return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x * kLog2e));
+}
+// log2(alpha) = -e^A softplus(g) / ln 2, softplus(g) = max(g, 0) + ln(1 + e^-|g|)
+__device__ __forceinline__ float log2_alpha_hw(float ea, float g) {
+    const float sp2 = fmaxf(g, 0.f) * kLog2e + __builtin_amdgcn_logf(1.0f + __builtin_amdgcn_exp2f(-fabsf(g) * kLog2e));
+    return -ea * sp2;
+}
 
 // NC consecutive input channels of one row, fetched in one load
 template <typename Tin, int NC> struct ChRaw;
@@ -169,19 +198,18 @@ template <> struct ChRaw<float, 1> {
     __device__ static float get(T r, int) { return r; }
 };
 
-// Conv + SiLU over one of q, k, v for the n tokens of a chunk, one wave; the
-// lane owns channels NC*lane .. NC*lane + NC - 1.  MODE 0: q (L2 norm and q
-// scale), 1: k (L2 norm, and a transposed copy into kt, zero past n), 2: v.
-// The three inputs before the chunk come from the conv window at chunk 0,
-// else from the sequence itself.  All 64 rows go to out (layout [64, H, NC*64]
-// from the chunk's first row; rows past n hold values of no meaning).
-template <int NC, int MODE, typename Tin>
-__device__ __forceinline__ void prep_tensor(const PrefillParams &p, const Tin *x, const Tin *win, int choff,
-                                            int CH, int c, int t0, int n, int h, int lane, float *out,
-                                            float (*kt)[kChunk + 1]) {
+// Conv + SiLU over one of q, k, v for rows 32*HALF .. 32*HALF + 31 of a
+// chunk, one wave; the lane owns channels NC*lane .. NC*lane + NC - 1.
+// MODE 0: q (L2 norm and q scale), 1: k (L2 norm), both into LDS rows (zero
+// past n); MODE 2: v, to the chunk-padded workspace rows (all 64 rows are
+// written; rows past n hold values of no meaning).  The three inputs before
+// the chunk come from the conv window at chunk 0, else from the sequence.
+template <int NC, int MODE, int HALF, typename Tin>
+__device__ __forceinline__ void prep_rows(const PrefillParams &p, const Tin *x, const Tin *win, int choff, int CH,
+                                          int c, int t0, int n, int h, int lane, float *out, size_t ostride) {
     using R = ChRaw<Tin, NC>;
     using RT = typename R::T;
-    constexpr int D = NC * kWave;
+    constexpr int D = NC * kWave, NR = kChunk / 2, R0 = NR * HALF;
     const int H = p.H, cb = NC * lane;
     float w[NC][4];
 #pragma unroll
@@ -189,19 +217,22 @@ __device__ __forceinline__ void prep_tensor(const PrefillParams &p, const Tin *x
         const float4 v = *reinterpret_cast<const float4 *>(p.conv_wt + ((size_t)h * CH + choff + cb + e) * 4);
         w[e][0] = v.x; w[e][1] = v.y; w[e][2] = v.z; w[e][3] = v.w;
     }
-    RT raw[kChunk + 3];   // rows -3 .. 63 of the chunk, all loads issued first
+    RT raw[NR + 3];   // rows R0 - 3 .. R0 + 31, all loads issued first
 #pragma unroll
-    for (int j = 0; j < 3; ++j) {
-        const Tin *src = c == 0 ? win + j * CH + choff + cb : x + ((size_t)(t0 - 3 + j) * H + h) * D + cb;
+    for (int j = 0; j < NR + 3; ++j) {
+        const int q = R0 - 3 + j;
+        const Tin *src;
+        if (HALF == 0 && j < 3) {
+            src = c == 0 ? win + j * CH + choff + cb : x + ((size_t)(t0 + q) * H + h) * D + cb;
+        } else {
+            // rows past the chunk repeat its last row
+            src = x + ((size_t)(t0 + min(q, n - 1)) * H + h) * D + cb;
+        }
         raw[j] = *reinterpret_cast<const RT *>(src);
     }
 #pragma unroll
-    for (int j = 0; j < kChunk; ++j) {
-        const int r = min(j, n - 1);   // rows past the chunk repeat its last row (never stored)
-        raw[3 + j] = *reinterpret_cast<const RT *>(x + ((size_t)(t0 + r) * H + h) * D + cb);
-    }
-#pragma unroll
-    for (int j = 0; j < kChunk; ++j) {
+    for (int j = 0; j < NR; ++j) {
+        const int row = R0 + j;
         float y[NC];
 #pragma unroll
         for (int e = 0; e < NC; ++e) {
@@ -209,63 +240,44 @@ __device__ __forceinline__ void prep_tensor(const PrefillParams &p, const Tin *x
             acc = fmaf(w[e][1], R::get(raw[j + 1], e), acc);
             acc = fmaf(w[e][2], R::get(raw[j + 2], e), acc);
             acc = fmaf(w[e][3], R::get(raw[j + 3], e), acc);
-            y[e] = p.silu ? acc * sigmoid(acc) : acc;
+            y[e] = p.silu ? silu_hw(acc) : acc;
         }
         if (MODE < 2) {
             float ss = 0.f;
 #pragma unroll
             for (int e = 0; e < NC; ++e) ss = fmaf(y[e], y[e], ss);
-            ss = wave_sum(ss);
-            const float sc = (MODE == 0 ? p.q_scale : 1.0f) / sqrtf(ss + p.l2_eps);
+            ss = wave_sum_dpp(ss);
+            const float sc = row < n ? (MODE == 0 ? p.q_scale : 1.0f) * __builtin_amdgcn_rsqf(ss + p.l2_eps) : 0.f;
 #pragma unroll
             for (int e = 0; e < NC; ++e) y[e] *= sc;
         }
-        float *dst = out + ((size_t)j * H + h) * D + cb;
+        float *dst = out + row * ostride + cb;
         if (NC == 2) *reinterpret_cast<float2 *>(dst) = make_float2(y[0], y[NC - 1]);
         else dst[0] = y[0];
-        if (MODE == 1) {
-#pragma unroll
-            for (int e = 0; e < NC; ++e) kt[cb + e][j] = j < n ? y[e] : 0.f;
-        }
     }
 }
 
-// log2(alpha) of the chunk's tokens, its prefix sums over the chunk into G
-// (rows past n add nothing) and beta (0 past n); one wave.
-template <int NC, int DK, typename Tin>
-__device__ __forceinline__ void prep_gates(const PrefillParams &p, int t0, int n, int h, int lane,
-                                           float (*G)[DK + 1], float *beta) {
-    using R = ChRaw<Tin, NC>;
-    using RT = typename R::T;
-    const int H = p.H, cb = NC * lane;
+// log2(alpha) of the chunk's tokens for channels ch0 .. ch0 + 63 and its
+// prefix sums over the chunk into G (rows past n add nothing); one wave.
+template <int DK, typename Tin>
+__device__ __forceinline__ void prep_gates(const PrefillParams &p, int t0, int n, int h, int lane, int ch0,
+                                           float (*G)[DK + 1]) {
+    const int H = p.H, ch = ch0 + lane;
     const Tin *g = static_cast<const Tin *>(p.g);
-    RT raw[kChunk];
+    Tin raw[kChunk];
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j) raw[j] = g[((size_t)(t0 + min(j, n - 1)) * H + h) * DK + ch];
+    const float ea = expf(p.A[h * DK + ch]);
+    float acc = 0.f;
 #pragma unroll
     for (int j = 0; j < kChunk; ++j) {
-        const int r = min(j, n - 1);
-        raw[j] = *reinterpret_cast<const RT *>(g + ((size_t)(t0 + r) * H + h) * DK + cb);
+        // alpha below 2^-200 is 0 in fp32 either way; the floor keeps the
+        // prefix sums finite (g = +inf would give -inf - -inf = NaN later)
+        const float la = fmaxf(log2_alpha_hw(ea, to_f32(raw[j])), -200.f);
+        acc += j < n ? la : 0.f;
+        G[j][ch] = acc;
     }
-    const Tin bv = static_cast<const Tin *>(p.b)[(size_t)(t0 + min(lane, n - 1)) * H + h];
-    float ea[NC], acc[NC];
-#pragma unroll
-    for (int e = 0; e < NC; ++e) {
-        ea[e] = expf(p.A[h * DK + cb + e]);
-        acc[e] = 0.f;
-    }
-#pragma unroll
-    for (int j = 0; j < kChunk; ++j) {
-#pragma unroll
-        for (int e = 0; e < NC; ++e) {
-            // alpha below 2^-200 is 0 in fp32 either way; the floor keeps the
-            // prefix sums finite (g = +inf would give -inf - -inf = NaN later)
-            const float la = fmaxf(-ea[e] * softplus(R::get(raw[j], e)) * kLog2e, -200.f);
-            acc[e] += j < n ? la : 0.f;
-            G[j][cb + e] = acc[e];
-        }
-    }
-    beta[lane] = lane < n ? sigmoid(to_f32(bv)) : 0.f;
 }
-
 
 constexpr float kSafeSpan = 60.f;
 
@@ -277,20 +289,16 @@ __device__ __forceinline__ void split_bits(float x, uint16_t &hi, uint16_t &lo) 
     lo = __builtin_bit_cast(uint16_t, l);
 }
 
-// 8 consecutive fp32 values of a workspace row (16-byte aligned), or zeros
-// for a row past the end of the chunk (it may lie past the array)
-__device__ __forceinline__ void load8(const float *src, bool valid, float *x) {
-    float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
-    if (valid) {
-        a = *reinterpret_cast<const float4 *>(src);
-        b = *reinterpret_cast<const float4 *>(src + 4);
-    }
+// 8 consecutive fp32 values of an LDS row (16-byte aligned)
+__device__ __forceinline__ void lds8(const float *src, float *x) {
+    const float4 a = *reinterpret_cast<const float4 *>(src);
+    const float4 b = *reinterpret_cast<const float4 *>(src + 4);
     x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
     x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
 }
 
 template <int DK, int DV, typename Tin>
-__global__ __launch_bounds__(256, 2) void kda_prefill_intra_kernel(PrefillParams p, PrefillWs ws) {
+__global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(PrefillParams p, PrefillWs ws) {
     constexpr int KS = DK / 32;
     __shared__ IntraLds<DK, DV> L;
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
@@ -308,52 +316,58 @@ __global__ __launch_bounds__(256, 2) void kda_prefill_intra_kernel(PrefillParams
     const size_t gh = (size_t)gidx * H + h;
     const size_t row0 = (size_t)gidx * kChunk * H + h;   // workspace row of the chunk's first token
     const size_t rstride = (size_t)H;                    // rows between consecutive tokens
-    auto kh_row = [&](int r) { return ws.kh + (row0 + r * rstride) * DK; };
-    auto qh_row = [&](int r) { return ws.qh + (row0 + r * rstride) * DK; };
 
-    // 1. the chunk's tokens: wave 0 q^, wave 1 k^, wave 2 v (to the
-    //    workspace, L2-resident for the steps below), wave 3 the decay prefix
-    //    sums and beta (LDS)
+    // 1. the chunk's tokens: waves 0-1 q^ and 2-3 k^ (LDS), 4-5 v (workspace),
+    //    a row half each; waves 6-7 the decay prefix sums (64 channels each)
+    //    and beta
     {
-        constexpr int CH = 2 * DK + DV;
+        constexpr int CH = 2 * DK + DV, RW = IntraLds<DK, DV>::RW;
         const Tin *win = static_cast<const Tin *>(p.window) + ((size_t)slot * H + h) * 3 * CH;
-        const size_t cbase = (size_t)gidx * kChunk * H;
         const Tin *xq = static_cast<const Tin *>(p.x_q), *xk = static_cast<const Tin *>(p.x_k);
         const Tin *xv = static_cast<const Tin *>(p.x_v);
-        if (wave == 0)
-            prep_tensor<DK / 64, 0>(p, xq, win, 0, CH, c, t0, n, h, lane, ws.qh + cbase * DK, L.kt);
-        else if (wave == 1)
-            prep_tensor<DK / 64, 1>(p, xk, win, DK, CH, c, t0, n, h, lane, ws.kh + cbase * DK, L.kt);
-        else if (wave == 2)
-            prep_tensor<DV / 64, 2>(p, xv, win, 2 * DK, CH, c, t0, n, h, lane, ws.vv + cbase * DV, L.kt);
-        else
-            prep_gates<DK / 64, DK, Tin>(p, t0, n, h, lane, L.G, L.beta);
+        float *vrow = ws.vv + row0 * DV;   // the chunk's first row of this head
+        switch (wave) {
+        case 0: prep_rows<DK / 64, 0, 0>(p, xq, win, 0, CH, c, t0, n, h, lane, &L.Q[0][0], RW); break;
+        case 1: prep_rows<DK / 64, 0, 1>(p, xq, win, 0, CH, c, t0, n, h, lane, &L.Q[0][0], RW); break;
+        case 2: prep_rows<DK / 64, 1, 0>(p, xk, win, DK, CH, c, t0, n, h, lane, &L.K[0][0], RW); break;
+        case 3: prep_rows<DK / 64, 1, 1>(p, xk, win, DK, CH, c, t0, n, h, lane, &L.K[0][0], RW); break;
+        case 4:
+            prep_rows<DV / 64, 2, 0>(p, xv, win, 2 * DK, CH, c, t0, n, h, lane, vrow, rstride * DV);
+            break;
+        case 5:
+            prep_rows<DV / 64, 2, 1>(p, xv, win, 2 * DK, CH, c, t0, n, h, lane, vrow, rstride * DV);
+            break;
+        default: {
+            const int gw = wave - 6;
+            if (64 * gw < DK) prep_gates<DK, Tin>(p, t0, n, h, lane, 64 * gw, L.G);
+            if (gw == 1) {
+                const Tin bv = static_cast<const Tin *>(p.b)[(size_t)(t0 + min(lane, n - 1)) * H + h];
+                L.beta[lane] = lane < n ? sigmoid(to_f32(bv)) : 0.f;
+            }
+        }
+        }
     }
     __syncthreads();
-    // the transposed k^ (zero past n) to the workspace: steps 4 and 6 read it
-    // by channel
-    float *const kT = ws.kT + gh * DK * kChunk;
-    for (int e = tid; e < DK * kChunk / 4; e += 256) {
-        const int i = e / (kChunk / 4), r0 = 4 * (e % (kChunk / 4));
-        *reinterpret_cast<float4 *>(kT + i * kChunk + r0) =
-            make_float4(L.kt[i][r0], L.kt[i][r0 + 1], L.kt[i][r0 + 2], L.kt[i][r0 + 3]);
-    }
-    // the V operand of step 7 is read now, so its latency hides behind steps 3-6
-    constexpr int NU = DV / 64;                  // U~ column tiles per wave
-    float vpre[NU][2][8];
+
+    // the V operand of step 6 is read now, so its latency hides behind steps 2-5
+    constexpr int NCT = (DK + DV) / 16;          // column tiles of [W | U~]
+    float vpre[2][2][8];
 #pragma unroll
-    for (int m = 0; m < NU; ++m) {
-        const int col = 16 * (wave + 4 * (DK / 64 + m)) + lr - DK;
+    for (int ci = 0; ci < 2; ++ci) {
+        const int ct = wave + kIntraWaves * ci;
+        const int col = 16 * ct + lr - DK;
+        if (ct < DK / 16 || ct >= NCT) continue;   // wave-uniform
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int sv = 32 * k2 + 8 * lk + e;
-                vpre[m][k2][e] = sv < n ? ws.vv[(row0 + sv * rstride) * DV + col] : 0.f;
+                vpre[ci][k2][e] = ws.vv[(row0 + sv * rstride) * DV + col];
             }
     }
+
     // 2. per 16-token block: may the diagonal tile use the scaled factors?
-    {
+    if (wave < 4) {
         float span = 0.f;
         for (int i = lane; i < DK; i += kWave) span = fmaxf(span, L.G[16 * wave][i] - L.G[16 * wave + 15][i]);
 #pragma unroll
@@ -363,10 +377,11 @@ __global__ __launch_bounds__(256, 2) void kda_prefill_intra_kernel(PrefillParams
     __syncthreads();
 
     // 3. A and P in 16 x 16 tiles; tile (bt, bs) covers t in block bt, s in
-    //    block bs.  The 10 tiles on or below the diagonal go 3,3,2,2 to the
-    //    waves; the 6 above it (P = 0 there, A is never read there) 2,2,1,1.
+    //    block bs.  The 10 tiles on or below the diagonal come first (two
+    //    waves take two of them); the 6 above it (P = 0 there, A is never
+    //    read there) go to the other waves.
     uint16_t *Ph = ws.P_hi + gh * kChunk * kChunk, *Pl = ws.P_lo + gh * kChunk * kChunk;
-    for (int tile = wave; tile < 16; tile += 4) {
+    for (int tile = wave; tile < 16; tile += kIntraWaves) {
         const int lbt[16] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3, 0, 0, 0, 1, 1, 2};
         const int lbs[16] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3, 1, 2, 3, 2, 3, 3};
         const int bt = lbt[tile], bs = lbs[tile];
@@ -383,45 +398,35 @@ __global__ __launch_bounds__(256, 2) void kda_prefill_intra_kernel(PrefillParams
         const int r = 16 * bt;
         if (bs < bt || L.safe[bt]) {
             const int t = 16 * bt + lr, sr = 16 * bs + lr;
-            const float *kt = kh_row(t), *qt = qh_row(t), *ks = kh_row(sr);
-            float ka[KS][8], qa[KS][8], kb[KS][8];
-#pragma unroll
-            for (int kk = 0; kk < KS; ++kk) {   // all operand loads first
-                const int c0 = 32 * kk + 8 * lk;
-                load8(kt + c0, t < n, ka[kk]);
-                load8(qt + c0, t < n, qa[kk]);
-                load8(ks + c0, sr < n, kb[kk]);
-            }
 #pragma unroll
             for (int kk = 0; kk < KS; ++kk) {
                 const int c0 = 32 * kk + 8 * lk;
+                float ka[8], qa[8], kb[8];
+                lds8(&L.K[t][c0], ka);
+                lds8(&L.Q[t][c0], qa);
+                lds8(&L.K[sr][c0], kb);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const float gr = L.G[r][c0 + e];
                     const float et = exp2f(L.G[t][c0 + e] - gr);
-                    ka[kk][e] *= et;
-                    qa[kk][e] *= et;
-                    kb[kk][e] *= exp2f(gr - L.G[sr][c0 + e]);
+                    ka[e] *= et;
+                    qa[e] *= et;
+                    kb[e] *= exp2f(gr - L.G[sr][c0 + e]);
                 }
-                const Split8 b = split8(kb[kk]);
-                aA = mma3(split8(ka[kk]), b, aA);
-                aP = mma3(split8(qa[kk]), b, aP);
+                const Split8 b = split8(kb);
+                aA = mma3(split8(ka), b, aA);
+                aP = mma3(split8(qa), b, aP);
             }
         } else {
             // direct: lane owns row t = r + lr and columns s = r + 4 lk + j
             float da[4] = {0.f, 0.f, 0.f, 0.f}, dp[4] = {0.f, 0.f, 0.f, 0.f};
             const int t = r + lr;
-            const float *kt = kh_row(t), *qt = qh_row(t);
             for (int ch = 0; ch < DK; ++ch) {
-                float kv = 0.f, qv = 0.f;
-                if (t < n) { kv = kt[ch]; qv = qt[ch]; }
-                const float gt = L.G[t][ch];
+                const float kv = L.K[t][ch], qv = L.Q[t][ch], gt = L.G[t][ch];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int sv = r + 4 * lk + j;
-                    float ks = 0.f;
-                    if (sv < n) ks = kh_row(sv)[ch];
-                    const float e = exp2f(fminf(gt - L.G[sv][ch], 0.f)) * ks;
+                    const float e = exp2f(fminf(gt - L.G[sv][ch], 0.f)) * L.K[sv][ch];
                     da[j] = fmaf(kv, e, da[j]);
                     dp[j] = fmaf(qv, e, dp[j]);
                 }
@@ -449,10 +454,10 @@ __global__ __launch_bounds__(256, 2) void kda_prefill_intra_kernel(PrefillParams
     }
     // 4. decayed factors for the scan: Q^ e^G (rows), (K^ e^(G_C - G))^T, e^(G_C)
     const int last = max(n - 1, 0);
-    for (int e8 = tid; e8 < kChunk * DK / 8; e8 += 256) {
+    for (int e8 = tid; e8 < kChunk * DK / 8; e8 += kIntraThreads) {
         const int r = e8 / (DK / 8), i0 = 8 * (e8 % (DK / 8));
         float x[8];
-        load8(qh_row(r) + i0, r < n, x);
+        lds8(&L.Q[r][i0], x);
         bf16x8 hv, lv;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -464,17 +469,15 @@ __global__ __launch_bounds__(256, 2) void kda_prefill_intra_kernel(PrefillParams
         *reinterpret_cast<bf16x8 *>(ws.Q_hi + gh * kChunk * DK + r * DK + i0) = hv;
         *reinterpret_cast<bf16x8 *>(ws.Q_lo + gh * kChunk * DK + r * DK + i0) = lv;
     }
-    for (int e8 = tid; e8 < kChunk * DK / 8; e8 += 256) {
-        const int i = e8 / (kChunk / 8), r0 = 8 * (e8 % (kChunk / 8));
+    for (int e8 = tid; e8 < kChunk * DK / 8; e8 += kIntraThreads) {
+        const int i = e8 % DK, r0 = 8 * (e8 / DK);   // lanes along channels: column reads spread over banks
         const float gl = L.G[last][i];
-        float kx[8];
-        load8(kT + i * kChunk + r0, true, kx);
         bf16x8 hv, lv;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int r = r0 + e;
-            float v = 0.f;
-            if (r < n) v = kx[e] * exp2f(fminf(gl - L.G[r][i], 0.f));
+            // k^ rows past n are zero
+            const float v = L.K[r][i] * exp2f(fminf(gl - L.G[r][i], 0.f));
             const __bf16 hb = (__bf16)v;
             hv[e] = hb;
             lv[e] = (__bf16)(v - (float)hb);
@@ -485,7 +488,7 @@ __global__ __launch_bounds__(256, 2) void kda_prefill_intra_kernel(PrefillParams
     if (tid < DK) ws.gC[gh * DK + tid] = exp2f(L.G[last][tid]);
 
     // 5. T = (I + A)^-1 by 16 x 16 blocks
-    for (int e = tid; e < kChunk * kChunk; e += 256) L.T[e / kChunk][e % kChunk] = 0.f;
+    for (int e = tid; e < kChunk * kChunk; e += kIntraThreads) L.T[e / kChunk][e % kChunk] = 0.f;
     __syncthreads();
     if (tid < 64) {   // diagonal blocks: column j of (I + A_bb)^-1
         const int b = tid / 16, j = tid % 16, o = 16 * b;
@@ -502,7 +505,7 @@ __global__ __launch_bounds__(256, 2) void kda_prefill_intra_kernel(PrefillParams
     __syncthreads();
     for (int b = 1; b < 4; ++b) {
         // Z_b' = sum_{b' <= m < b} A_bm T_mb'  for every b' < b
-        for (int e = tid; e < b * 256; e += 256) {
+        for (int e = tid; e < b * 256; e += kIntraThreads) {
             const int bp = e / 256, i = (e / 16) % 16, j = e % 16;
             float acc = 0.f;
             for (int m = 16 * bp; m < 16 * b; ++m) acc = fmaf(L.A[16 * b + i][m], L.T[m][16 * bp + j], acc);
@@ -510,7 +513,7 @@ __global__ __launch_bounds__(256, 2) void kda_prefill_intra_kernel(PrefillParams
         }
         __syncthreads();
         // T_bb' = -T_bb Z_b'
-        for (int e = tid; e < b * 256; e += 256) {
+        for (int e = tid; e < b * 256; e += kIntraThreads) {
             const int bp = e / 256, i = (e / 16) % 16, j = e % 16;
             float acc = 0.f;
 #pragma unroll
@@ -532,22 +535,20 @@ __global__ __launch_bounds__(256, 2) void kda_prefill_intra_kernel(PrefillParams
             for (int e = 0; e < 8; ++e) x[e] = L.T[16 * rt + lr][32 * k2 + 8 * lk + e];
             ta[rt][k2] = split8(x);
         }
-    constexpr int NCT = (DK + DV) / 16;
 #pragma unroll
-    for (int ci = 0; ci < NCT / 4; ++ci) {
-        const int ct = wave + 4 * ci;
+    for (int ci = 0; ci < 2; ++ci) {
+        const int ct = wave + kIntraWaves * ci;
+        if (ct >= NCT) continue;                   // wave-uniform
         const int col = 16 * ct + lr;
-        const bool isw = ci < DK / 64;             // wave-uniform
+        const bool isw = ct < DK / 16;             // wave-uniform
         Split8 rb[2];
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
             float x[8];
-            if (isw) load8(kT + col * kChunk + 32 * k2 + 8 * lk, true, x);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int sv = 32 * k2 + 8 * lk + e;
-                if (isw) x[e] = sv < n ? L.beta[sv] * x[e] * exp2f(L.G[sv][col]) : 0.f;
-                else x[e] = L.beta[sv] * vpre[ci - DK / 64][k2][e];
+                x[e] = isw ? L.beta[sv] * L.K[sv][col] * exp2f(L.G[sv][col]) : L.beta[sv] * vpre[ci][k2][e];
             }
             rb[k2] = split8(x);
         }
@@ -824,10 +825,7 @@ static kda_status launch_prefill_typed(const PrefillParams &p, hipStream_t strea
     unsigned char *base = static_cast<unsigned char *>(p.workspace);
     PrefillWs ws{};
     ws.meta = reinterpret_cast<int32_t *>(base + l.meta);
-    ws.qh = reinterpret_cast<float *>(base + l.qh);
-    ws.kh = reinterpret_cast<float *>(base + l.kh);
     ws.vv = reinterpret_cast<float *>(base + l.vv);
-    ws.kT = reinterpret_cast<float *>(base + l.kT);
     ws.Wn_hi = reinterpret_cast<uint16_t *>(base + l.Wn_hi);
     ws.Wn_lo = reinterpret_cast<uint16_t *>(base + l.Wn_lo);
     ws.Q_hi = reinterpret_cast<uint16_t *>(base + l.Q_hi);
@@ -843,7 +841,7 @@ static kda_status launch_prefill_typed(const PrefillParams &p, hipStream_t strea
     hipLaunchKernelGGL(kda_prefill_meta_kernel, dim3(1), dim3(64), 0, stream, p, ws);
     if (p.total_T > 0) {
         hipLaunchKernelGGL((kda_prefill_intra_kernel<DK, DV, Tin>), dim3((unsigned)ws.G_max, (unsigned)p.H),
-                           dim3(256), 0, stream, p, ws);
+                           dim3(kIntraThreads), 0, stream, p, ws);
     }
     hipLaunchKernelGGL((kda_prefill_scan_kernel<DK, DV, Tin>),
                        dim3((unsigned)p.N_seq, (unsigned)p.H, (unsigned)(DV / kColBlock)), dim3(256), 0,
