@@ -572,12 +572,17 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
 }
 
 // ---------------------------------------------------------------------------
-// scan: one workgroup (4 waves) per (sequence, head, 16 state columns).
-// Per chunk, wave w owns rows 16w..16w+15 of the chunk and state row tiles
-// TS*w .. TS*w+TS-1; all products run on MFMA in bf16x3 with fp32
-// accumulation.  The next chunk's operands are loaded while the current one
-// is computed (two register buffers).
+// scan: one workgroup per (sequence, head, 16 state columns), two teams of 4
+// waves.  Team 0 computes the even chunks and team 1 the odd ones; while one
+// team computes a chunk, the other loads the operands of the next one into
+// its registers, so the operand traffic (bound by the L1's outstanding-miss
+// capacity) runs under the other team's MFMA work.  Inside a team, wave w
+// owns rows 16w..16w+15 of the chunk and state row tiles TS*w .. TS*w+TS-1;
+// all products run on MFMA in bf16x3 with fp32 accumulation.  The state is
+// handed from team to team through LDS (two buffers).
 // ---------------------------------------------------------------------------
+constexpr int kScanThreads = 512;
+
 template <int DK>
 struct ScanOps {
     static constexpr int KS = DK / 32, TS = DK / 64;
@@ -596,37 +601,46 @@ __device__ __forceinline__ Split8 load_split8(const uint16_t *hi, const uint16_t
     return v;
 }
 
-template <int DK, int DV>
-__device__ __forceinline__ void scan_load(const PrefillWs &ws, size_t gh, int wave, int lr, int lk, int j0,
-                                          ScanOps<DK> &o) {
-    constexpr int KS = DK / 32, TS = DK / 64;
-    const size_t rw = gh * kChunk * DK + (16 * wave + lr) * DK + 8 * lk;
+// first half of a chunk's operands: the d_k-contraction rows (-W, Q^ e^G)
+template <int DK>
+__device__ __forceinline__ void scan_load_a(const PrefillWs &ws, size_t gh, int w4, int lr, int lk, ScanOps<DK> &o) {
+    constexpr int KS = DK / 32;
+    const size_t rw = gh * kChunk * DK + (16 * w4 + lr) * DK + 8 * lk;
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
         o.w[k] = load_split8(ws.Wn_hi, ws.Wn_lo, rw + 32 * k);
         o.q[k] = load_split8(ws.Q_hi, ws.Q_lo, rw + 32 * k);
     }
-    const size_t rp = gh * kChunk * kChunk + (16 * wave + lr) * kChunk + 8 * lk;
+}
+
+// second half: P, Kd^T, U~ and e^(G_C)
+template <int DK, int DV>
+__device__ __forceinline__ void scan_load_b(const PrefillWs &ws, size_t gh, int w4, int lr, int lk, int j0,
+                                            ScanOps<DK> &o) {
+    constexpr int TS = DK / 64;
+    const size_t rp = gh * kChunk * kChunk + (16 * w4 + lr) * kChunk + 8 * lk;
 #pragma unroll
     for (int k = 0; k < 2; ++k) o.pm[k] = load_split8(ws.P_hi, ws.P_lo, rp + 32 * k);
 #pragma unroll
     for (int m = 0; m < TS; ++m) {
-        const size_t rk = gh * DK * kChunk + (16 * (TS * wave + m) + lr) * kChunk + 8 * lk;
+        const size_t rk = gh * DK * kChunk + (16 * (TS * w4 + m) + lr) * kChunk + 8 * lk;
 #pragma unroll
         for (int k = 0; k < 2; ++k) o.kd[m][k] = load_split8(ws.K_hi, ws.K_lo, rk + 32 * k);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o.gc[m][r] = ws.gC[gh * DK + 16 * (TS * wave + m) + 4 * lk + r];
+        for (int r = 0; r < 4; ++r) o.gc[m][r] = ws.gC[gh * DK + 16 * (TS * w4 + m) + 4 * lk + r];
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) o.ut[r] = ws.Ut[gh * kChunk * DV + (16 * wave + 4 * lk + r) * DV + j0 + lr];
+    for (int r = 0; r < 4; ++r) o.ut[r] = ws.Ut[gh * kChunk * DV + (16 * w4 + 4 * lk + r) * DV + j0 + lr];
 }
 
 template <int DK, int DV, typename Tin>
-__global__ __launch_bounds__(256) void kda_prefill_scan_kernel(PrefillParams p, PrefillWs ws) {
+__global__ __launch_bounds__(kScanThreads) void kda_prefill_scan_kernel(PrefillParams p, PrefillWs ws) {
     constexpr int CB = kColBlock, CH = 2 * DK + DV, KS = DK / 32, TS = DK / 64;
+    static_assert(CH <= kScanThreads, "one thread per conv channel");
     __shared__ __align__(16) float S[2][DK][CB];
     __shared__ __align__(16) float U[kChunk][CB];
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int team = wave / 4, w4 = wave % 4;
     const int lr = lane % 16, lk = lane / 16;
     const int s = blockIdx.x, h = blockIdx.y, j0 = blockIdx.z * CB, H = p.H;
     if (ws.meta[0] != 1) return;
@@ -640,11 +654,9 @@ __global__ __launch_bounds__(256) void kda_prefill_scan_kernel(PrefillParams p, 
     // the previous window when len < 3); read everything, then write
     if (blockIdx.z == 0) {
         Tin *win = static_cast<Tin *>(p.window) + ((size_t)slot * H + h) * 3 * CH;
-        Tin nv[2][3];
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-            const int ch = tid + 256 * k2;
-            if (ch >= CH) continue;
+        const int ch = tid;
+        Tin nv[3];
+        if (ch < CH) {
             const Tin *src;
             int stride, off;
             if (ch < DK) { src = static_cast<const Tin *>(p.x_q); stride = DK; off = ch; }
@@ -653,33 +665,20 @@ __global__ __launch_bounds__(256) void kda_prefill_scan_kernel(PrefillParams p, 
 #pragma unroll
             for (int j = 0; j < 3; ++j) {
                 const int q = len + j - 3;   // sequence position of new row j
-                nv[k2][j] = q >= 0 ? src[((size_t)(p.cu_seqlens[s] + q) * H + h) * stride + off]
-                                   : win[(q + 3) * CH + ch];
+                nv[j] = q >= 0 ? src[((size_t)(p.cu_seqlens[s] + q) * H + h) * stride + off]
+                               : win[(q + 3) * CH + ch];
             }
         }
         __syncthreads();
+        if (ch < CH) {
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-            const int ch = tid + 256 * k2;
-            if (ch >= CH) continue;
-#pragma unroll
-            for (int j = 0; j < 3; ++j) win[j * CH + ch] = nv[k2][j];
+            for (int j = 0; j < 3; ++j) win[j * CH + ch] = nv[j];
         }
     }
 
     float *Sg = p.state + ((size_t)slot * H + h) * DK * DV;
-    for (int e = tid; e < DK * CB; e += 256) S[0][e / CB][e % CB] = Sg[(e / CB) * DV + j0 + e % CB];
-    __syncthreads();
+    for (int e = tid; e < DK * CB; e += kScanThreads) S[0][e / CB][e % CB] = Sg[(e / CB) * DV + j0 + e % CB];
 
-    auto load_sb = [&](int buf, Split8 (&sb)[KS]) {
-#pragma unroll
-        for (int k = 0; k < KS; ++k) {
-            float x[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = S[buf][32 * k + 8 * lk + e][lr];
-            sb[k] = split8(x);
-        }
-    };
     // bf16x3 product with the three partial products in separate
     // accumulators (short dependency chains), summed at the end
     struct Acc3 {
@@ -697,88 +696,82 @@ __global__ __launch_bounds__(256) void kda_prefill_scan_kernel(PrefillParams p, 
     };
     auto sum3 = [](const Acc3 &a, int r) { return a.hh[r] + (a.hl[r] + a.lh[r]); };
 
-    // sequence bounds in registers: a load inside the chunk loop would have
-    // to wait behind the prefetch of the next chunk
     const int seq_t0 = p.cu_seqlens[s], seq_t1 = p.cu_seqlens[s + 1];
-    float ypend[4];          // outputs of the previous chunk, stored one step late
-    int ypend_t0 = 0, ypend_n = 0;
-    auto flush_y = [&]() {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = 16 * wave + 4 * lk + r;
-            if (t < ypend_n) p.y[((size_t)(ypend_t0 + t) * H + h) * DV + j0 + lr] = ypend[r];
-        }
-    };
-
-    // chunk c reads the state from S[c & 1] and writes the next one to
-    // S[(c + 1) & 1]; two barriers per chunk
-    auto chunk_step = [&](int c, const ScanOps<DK> &o, Split8 (&sb)[KS]) {
+    ScanOps<DK> ops;
+    if (team == 0 && nch > 0) {
+        scan_load_a<DK>(ws, (size_t)g0 * H + h, w4, lr, lk, ops);
+        scan_load_b<DK, DV>(ws, (size_t)g0 * H + h, w4, lr, lk, j0, ops);
+    }
+    __syncthreads();
+    Acc3 ao;
+    for (int c = 0; c < nch; ++c) {
         const int cur = c & 1;
-        const int t0 = seq_t0 + c * kChunk;
-        const int n = min(kChunk, seq_t1 - t0);
-        // U = U~ - W S ; O = Q^e^G S
-        Acc3 au, ao;
-        zero3(au);
-        zero3(ao);
+        const bool mine = cur == team;            // wave-uniform
+        const size_t gnext = (size_t)(g0 + c + 1) * H + h;
+        // segment 1: U = U~ - W S and O = Q^e^G S  |  the other team loads
+        if (mine) {
+            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this chunk's operands have landed
+            Split8 sb[KS];
 #pragma unroll
-        for (int k = 0; k < KS; ++k) {
-            mma3s(o.w[k], sb[k], au);
-            mma3s(o.q[k], sb[k], ao);
+            for (int k = 0; k < KS; ++k) {
+                float x[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = S[cur][32 * k + 8 * lk + e][lr];
+                sb[k] = split8(x);
+            }
+            Acc3 au;
+            zero3(au);
+            zero3(ao);
+#pragma unroll
+            for (int k = 0; k < KS; ++k) {
+                mma3s(ops.w[k], sb[k], au);
+                mma3s(ops.q[k], sb[k], ao);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) U[16 * w4 + 4 * lk + r][lr] = ops.ut[r] + sum3(au, r);
+        } else if (c + 1 < nch) {
+            scan_load_a<DK>(ws, gnext, w4, lr, lk, ops);
         }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) U[16 * wave + 4 * lk + r][lr] = o.ut[r] + sum3(au, r);
         __syncthreads();
-        Split8 ub[2];
+        // segment 2: O += P U, S' = diag(e^G_C) S + Kd^T U  |  the other team loads
+        if (mine) {
+            const int t0 = seq_t0 + c * kChunk;
+            const int n = min(kChunk, seq_t1 - t0);
+            Split8 ub[2];
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            float x[8];
+            for (int k = 0; k < 2; ++k) {
+                float x[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = U[32 * k + 8 * lk + e][lr];
-            ub[k] = split8(x);
-        }
-        // O += P U  (P rows beyond the chunk and above the diagonal are 0)
+                for (int e = 0; e < 8; ++e) x[e] = U[32 * k + 8 * lk + e][lr];
+                ub[k] = split8(x);
+            }
+            // P rows beyond the chunk and above the diagonal are 0
 #pragma unroll
-        for (int k = 0; k < 2; ++k) mma3s(o.pm[k], ub[k], ao);
+            for (int k = 0; k < 2; ++k) mma3s(ops.pm[k], ub[k], ao);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) ypend[r] = sum3(ao, r);
-        ypend_t0 = t0;
-        ypend_n = n;
-        // S' = diag(e^G_C) S + Kd^T U  into the other buffer
+            for (int m = 0; m < TS; ++m) {
+                Acc3 as;
+                zero3(as);
 #pragma unroll
-        for (int m = 0; m < TS; ++m) {
-            Acc3 as;
-            zero3(as);
+                for (int k = 0; k < 2; ++k) mma3s(ops.kd[m][k], ub[k], as);
 #pragma unroll
-            for (int k = 0; k < 2; ++k) mma3s(o.kd[m][k], ub[k], as);
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * (TS * w4 + m) + 4 * lk + r;
+                    S[cur ^ 1][row][lr] = ops.gc[m][r] * S[cur][row][lr] + sum3(as, r);
+                }
+            }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int row = 16 * (TS * wave + m) + 4 * lk + r;
-                S[cur ^ 1][row][lr] = o.gc[m][r] * S[cur][row][lr] + sum3(as, r);
+                const int t = 16 * w4 + 4 * lk + r;
+                if (t < n) p.y[((size_t)(t0 + t) * H + h) * DV + j0 + lr] = sum3(ao, r);
             }
+        } else if (c + 1 < nch) {
+            scan_load_b<DK, DV>(ws, gnext, w4, lr, lk, j0, ops);
         }
         __syncthreads();
-        load_sb(cur ^ 1, sb);
-    };
-
-    Split8 sb[KS];
-    load_sb(0, sb);
-    ScanOps<DK> cur, nxt;
-    if (nch > 0) scan_load<DK, DV>(ws, (size_t)g0 * H + h, wave, lr, lk, j0, cur);
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the loop starts with nothing in flight
-    for (int c = 0; c < nch; ++c) {
-        // the next chunk's operands load while this chunk computes
-        if (c + 1 < nch) scan_load<DK, DV>(ws, (size_t)(g0 + c + 1) * H + h, wave, lr, lk, j0, nxt);
-        flush_y();
-        chunk_step(c, cur, sb);
-        // all of them (and the output stores issued above) have landed by
-        // now; an explicit vmcnt(0) tells the compiler so, instead of
-        // conservative waits inside the next step
-        __builtin_amdgcn_s_waitcnt(0x0F70);
-        cur = nxt;
     }
-    flush_y();
     const int fin = nch & 1;
-    for (int e = tid; e < DK * CB; e += 256) Sg[(e / CB) * DV + j0 + e % CB] = S[fin][e / CB][e % CB];
+    for (int e = tid; e < DK * CB; e += kScanThreads) Sg[(e / CB) * DV + j0 + e % CB] = S[fin][e / CB][e % CB];
 }
 
 // ---------------------------------------------------------------------------
@@ -844,7 +837,7 @@ static kda_status launch_prefill_typed(const PrefillParams &p, hipStream_t strea
                            dim3(kIntraThreads), 0, stream, p, ws);
     }
     hipLaunchKernelGGL((kda_prefill_scan_kernel<DK, DV, Tin>),
-                       dim3((unsigned)p.N_seq, (unsigned)p.H, (unsigned)(DV / kColBlock)), dim3(256), 0,
+                       dim3((unsigned)p.N_seq, (unsigned)p.H, (unsigned)(DV / kColBlock)), dim3(kScanThreads), 0,
                        stream, p, ws);
     if (p.total_T > 0) {
         const dim3 tok_grid((unsigned)((p.total_T + 3) / 4), (unsigned)p.H);
