@@ -30,6 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK = 2.5e15   # MI355X dense bf16 MFMA, flop/s
 METRIC = "KDA decode state updates/s (token·heads/s) + achieved HBM GB/s at B=64"
 
 # algorithmic bytes per (token, head) of one decode step at H=32, d_k=d_v=128,
@@ -73,6 +74,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="run only the chunked-prefill measurement (32768 tokens, H=32) and print it; "
+                         "for profiling that path")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the timed region, run one plain copy of this many MiB "
                          "(a known-size kernel for calibrating memory counters)")
@@ -92,6 +96,10 @@ def main():
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.prefill_only:
+        print(json.dumps({"chunk_prefill_t32k": prefill_extra(torch, api, synth, torch.cuda.current_stream())}),
+              flush=True)
+        return
     cfg = synth.WORKLOADS["decode_b64"]
     B, H, dk, dv, n_slots = cfg["B"], cfg["H"], cfg["d_k"], cfg["d_v"], cfg["n_slots"]
     K, W = args.steps, args.warmup
@@ -286,6 +294,30 @@ def extras(torch, api, synth, layer, cache, step_inputs, y, slots, B, H, dk, dv,
     return ex
 
 
+def prefill_mfma_per_chunk_head(dk, dv, col_block=16):
+    """v_mfma_f32_16x16x32_bf16 instructions the chunked prefill issues per
+    (chunk, head); bf16x3 makes three of them per fp32 16x16x32 product.
+    intra: the 10 Gram tiles on or below the diagonal, A and P, d_k/32 steps
+    each; [W | U~] = T R over (d_k + d_v)/16 column tiles, 1+1+2+2 steps over
+    the four lower-triangular row tiles of T; the off-diagonal blocks of T
+    itself, 13 steps (Z = A T then -T_bb Z for the six blocks below the
+    diagonal, K = 16, 32 or 48 padded to steps of 32).  scan, per block of 16 state
+    columns: W S and Q S (d_k/32 steps for each of 4 row tiles), P U (2 steps
+    x 4 row tiles), Kd^T U (2 steps x d_k/16 row tiles)."""
+    ks = dk // 32
+    intra = 3 * (10 * 2 * ks + (dk + dv) // 16 * 6 + 13)
+    scan = 3 * (dv // col_block) * (4 * 2 * ks + 4 * 2 + (dk // 16) * 2)
+    return intra + scan
+
+
+def prefill_algorithmic_flops_per_chunk_head(dk, dv, C=64):
+    """Dense flops of the chunk algebra, each contraction counted once: A and
+    P (C x C x d_k), T = (I + A)^-1 (~C^3/3 multiply-adds), [W | U~]
+    (C x C x (d_k + d_v)), W S and Q S (C x d_k x d_v), P U (C x C x d_v),
+    Kd^T U (d_k x C x d_v)."""
+    return 2 * (2 * C * C * dk + C ** 3 / 3 + C * C * (dk + dv) + 2 * C * dk * dv + C * C * dv + dk * C * dv)
+
+
 def prefill_extra(torch, api, synth, stream):
     cfg = synth.WORKLOADS["prefill_t32k"]
     H, dk, dv, T = cfg["H"], cfg["d_k"], cfg["d_v"], cfg["T"]
@@ -312,8 +344,14 @@ def prefill_extra(torch, api, synth, stream):
     out_b = T * H * dv * 4
     st_b = 2 * H * dk * dv * 4
     tot = in_b + out_b + st_b
+    chunk_heads = (T + 63) // 64 * H
+    mfma_flops = prefill_mfma_per_chunk_head(dk, dv) * 16 * 16 * 32 * 2 * chunk_heads
+    alg_flops = prefill_algorithmic_flops_per_chunk_head(dk, dv) * chunk_heads
     return {"us_per_call": s * 1e6, "tokens_per_s": T / s, "token_heads_per_s": T * H / s,
             "algorithmic_gbs": tot / s / 1e9, "frac_of_8tbs": tot / s / 8e12,
+            "mfma_flops_issued": mfma_flops, "mfma_tflops": mfma_flops / s / 1e12,
+            "mfma_util_of_bf16_dense_peak": mfma_flops / s / MFMA_BF16_PEAK,
+            "algorithmic_tflops": alg_flops / s / 1e12,
             "workspace_bytes": ws_n}
 
 

@@ -487,7 +487,9 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
     }
     if (tid < DK) ws.gC[gh * DK + tid] = exp2f(L.G[last][tid]);
 
-    // 5. T = (I + A)^-1 by 16 x 16 blocks
+    // 5. T = (I + A)^-1 by 16 x 16 blocks: the diagonal blocks by forward
+    //    substitution, then block row b = 1, 2, 3 from
+    //    T_bb' = -T_bb sum_{b' <= m < b} A_bm T_mb'  (one wave per b' < b, MFMA)
     for (int e = tid; e < kChunk * kChunk; e += kIntraThreads) L.T[e / kChunk][e % kChunk] = 0.f;
     __syncthreads();
     if (tid < 64) {   // diagonal blocks: column j of (I + A_bb)^-1
@@ -504,21 +506,34 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
     }
     __syncthreads();
     for (int b = 1; b < 4; ++b) {
-        // Z_b' = sum_{b' <= m < b} A_bm T_mb'  for every b' < b
-        for (int e = tid; e < b * 256; e += kIntraThreads) {
-            const int bp = e / 256, i = (e / 16) % 16, j = e % 16;
-            float acc = 0.f;
-            for (int m = 16 * bp; m < 16 * b; ++m) acc = fmaf(L.A[16 * b + i][m], L.T[m][16 * bp + j], acc);
-            L.Z[bp][i][j] = acc;
-        }
-        __syncthreads();
-        // T_bb' = -T_bb Z_b'
-        for (int e = tid; e < b * 256; e += kIntraThreads) {
-            const int bp = e / 256, i = (e / 16) % 16, j = e % 16;
-            float acc = 0.f;
+        if (wave < b) {
+            const int bp = wave, K = 16 * (b - bp);
+            // Z = A[block b, columns 16 b' .. 16 b) T[rows 16 b' .. 16 b, block b']
+            f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            for (int k0 = 0; k0 < K; k0 += 32) {
+                float xa[8], xb[8];
 #pragma unroll
-            for (int m = 0; m < 16; ++m) acc = fmaf(L.T[16 * b + i][16 * b + m], L.Z[bp][m][j], acc);
-            L.T[16 * b + i][16 * bp + j] = -acc;
+                for (int e = 0; e < 8; ++e) {
+                    const int kk = k0 + 8 * lk + e;
+                    xa[e] = kk < K ? L.A[16 * b + lr][16 * bp + kk] : 0.f;
+                    xb[e] = kk < K ? L.T[16 * bp + kk][16 * bp + lr] : 0.f;
+                }
+                z = mma3(split8(xa), split8(xb), z);
+            }
+            // result layout to operand layout through this wave's scratch
+#pragma unroll
+            for (int r = 0; r < 4; ++r) L.Z[bp][4 * lk + r][lr] = z[r];
+            __builtin_amdgcn_wave_barrier();
+            float xa[8], xb[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int kk = 8 * lk + e;
+                xa[e] = kk < 16 ? L.T[16 * b + lr][16 * b + kk] : 0.f;
+                xb[e] = kk < 16 ? L.Z[bp][kk][lr] : 0.f;
+            }
+            const f32x4 t = mma3(split8(xa), split8(xb), f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+            for (int r = 0; r < 4; ++r) L.T[16 * b + 4 * lk + r][16 * bp + lr] = -t[r];
         }
         __syncthreads();
     }
