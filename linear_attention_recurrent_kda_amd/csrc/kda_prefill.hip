@@ -790,37 +790,69 @@ __global__ __launch_bounds__(kScanThreads) void kda_prefill_scan_kernel(PrefillP
 }
 
 // ---------------------------------------------------------------------------
-// norm: one wave per (token, head): y = O / sqrt(mean(O^2) + eps) * w * sigmoid(z)
+// norm: y = O / sqrt(mean(O^2) + eps) * w * sigmoid(z) over rows r = t*H + h
+// of y (contiguous).  A lane holds 4 consecutive columns, a row spans d_v/4
+// lanes (a wave covers 2 rows at d_v = 128, 4 at d_v = 64); a workgroup
+// walks kNormRows consecutive rows.
 // ---------------------------------------------------------------------------
-template <int DK, int DV, typename Tin>
+constexpr int kNormRows = 64;
+
+// 4 consecutive inputs (8- or 16-byte aligned) as fp32
+__device__ __forceinline__ void load4(const uint16_t *src, float *x) {
+    const uint2 v = *reinterpret_cast<const uint2 *>(src);
+    x[0] = __uint_as_float(v.x << 16);
+    x[1] = __uint_as_float(v.x & 0xffff0000u);
+    x[2] = __uint_as_float(v.y << 16);
+    x[3] = __uint_as_float(v.y & 0xffff0000u);
+}
+__device__ __forceinline__ void load4(const float *src, float *x) {
+    const float4 v = *reinterpret_cast<const float4 *>(src);
+    x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+}
+
+template <int DV, typename Tin>
 __global__ __launch_bounds__(256) void kda_prefill_norm_kernel(PrefillParams p, PrefillWs ws) {
-    constexpr int EV = DV / kWave;
-    const int lane = threadIdx.x % kWave;
-    const int t = blockIdx.x * 4 + threadIdx.x / kWave;
-    const int h = blockIdx.y, H = p.H;
-    if (t >= p.total_T) return;
-    float *yr = p.y + ((size_t)t * H + h) * DV;
-    bool live = ws.meta[0] == 1;
-    if (live) {
-        const int s = upper_index(p.cu_seqlens, p.N_seq + 1, t);
-        live = slot_ok(p.slot_idx[s], p.n_slots);
-    }
-    if (!live) {
-#pragma unroll
-        for (int e = 0; e < EV; ++e) yr[lane + kWave * e] = 0.f;
-        return;
-    }
-    float o[EV];
-    float ss = 0.f;
-#pragma unroll
-    for (int e = 0; e < EV; ++e) { o[e] = yr[lane + kWave * e]; ss = fmaf(o[e], o[e], ss); }
-    ss = wave_sum(ss);
-    const float r = 1.0f / sqrtf(ss * (1.0f / DV) + p.rms_eps);
-    const Tin *z = static_cast<const Tin *>(p.z) + ((size_t)t * H + h) * DV;
-#pragma unroll
-    for (int e = 0; e < EV; ++e) {
-        const int j = lane + kWave * e;
-        yr[j] = o[e] * r * (p.norm_w[h * DV + j] * sigmoid(to_f32(z[j])));
+    constexpr int LPR = DV / 4, RPW = kWave / LPR, RPB = 4 * RPW;   // lanes per row, rows per wave / block pass
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int H = p.H, c0 = 4 * (lane % LPR);
+    const size_t nrows = (size_t)p.total_T * H;
+    const bool valid = ws.meta[0] == 1;
+#pragma unroll 2
+    for (int pass = 0; pass < kNormRows / RPB; ++pass) {
+        const size_t r = (size_t)blockIdx.x * kNormRows + pass * RPB + wave * RPW + lane / LPR;
+        const bool in = r < nrows;
+        const size_t rr = in ? r : 0;
+        const int t = (int)(rr / H), h = (int)(rr % H);
+        bool live = in && valid;
+        if (live) live = slot_ok(p.slot_idx[upper_index(p.cu_seqlens, p.N_seq + 1, t)], p.n_slots);
+        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (in) o = *reinterpret_cast<const float4 *>(p.y + rr * DV + c0);
+        float ss = o.x * o.x;
+        ss = fmaf(o.y, o.y, ss);
+        ss = fmaf(o.z, o.z, ss);
+        ss = fmaf(o.w, o.w, ss);
+        // row sums: DPP inside each 16-lane row, then (d_v = 128) across row pairs
+        ss = dpp_add<0xB1, 0xF>(ss);
+        ss = dpp_add<0x4E, 0xF>(ss);
+        ss = dpp_add<0x141, 0xF>(ss);
+        ss = dpp_add<0x140, 0xF>(ss);
+        if (LPR == 32) {
+            ss = dpp_add<0x142, 0xA>(ss);   // rows 1, 3 += rows 0, 2
+            const float s_lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ss), 31));
+            const float s_hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ss), 63));
+            ss = lane < 32 ? s_lo : s_hi;
+        }
+        const float rn = 1.0f / sqrtf(ss * (1.0f / DV) + p.rms_eps);
+        float zf[4];
+        load4(static_cast<const Tin *>(p.z) + rr * DV + c0, zf);
+        const float4 w = *reinterpret_cast<const float4 *>(p.norm_w + h * DV + c0);
+        float4 out;
+        out.x = o.x * rn * (w.x * sigmoid(zf[0]));
+        out.y = o.y * rn * (w.y * sigmoid(zf[1]));
+        out.z = o.z * rn * (w.z * sigmoid(zf[2]));
+        out.w = o.w * rn * (w.w * sigmoid(zf[3]));
+        if (!live) out = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (in) *reinterpret_cast<float4 *>(p.y + rr * DV + c0) = out;
     }
 }
 
@@ -855,8 +887,9 @@ static kda_status launch_prefill_typed(const PrefillParams &p, hipStream_t strea
                        dim3((unsigned)p.N_seq, (unsigned)p.H, (unsigned)(DV / kColBlock)), dim3(kScanThreads), 0,
                        stream, p, ws);
     if (p.total_T > 0) {
-        const dim3 tok_grid((unsigned)((p.total_T + 3) / 4), (unsigned)p.H);
-        hipLaunchKernelGGL((kda_prefill_norm_kernel<DK, DV, Tin>), tok_grid, dim3(256), 0, stream, p, ws);
+        const size_t rows = (size_t)p.total_T * p.H;
+        hipLaunchKernelGGL((kda_prefill_norm_kernel<DV, Tin>), dim3((unsigned)((rows + kNormRows - 1) / kNormRows)),
+                           dim3(256), 0, stream, p, ws);
     }
     return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
