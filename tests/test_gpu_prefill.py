@@ -84,6 +84,26 @@ def test_other_head_sizes(dk, dv, dtype):
     assert state_rel_err(host(cache.state[1:2]), o["state"]) < 1e-4
 
 
+def test_strong_decay_direct_diagonal_tiles():
+    """Decay strong enough that some 16-token blocks span more than 2^60 of
+    decay (their diagonal Gram tiles take the direct path), mixed with weak
+    blocks, and one token whose decay hits the log2(alpha) floor."""
+    g = synth.rng(960)
+    H, dk, dv, T = 2, 128, 128, 200
+    params = synth.layer_params(g, H, dk, dv)
+    dl, ol = layer_pair(params)
+    inp = synth.token_inputs(g, (T,), H, dk, dv, "f32")
+    pos = np.arange(T) % 64
+    strong = ((pos // 16) % 2 == 1)[:, None, None]          # blocks 1 and 3 of every chunk
+    inp["g"] = np.where(strong, inp["g"] + 8.0, inp["g"]).astype(np.float32)
+    inp["g"][77] = 1000.0
+    cache = new_cache(1, H, dk, dv, "f32")
+    y, _ = run_prefill(dl, cache, [0], [T], inp, "f32")
+    o = oracle_seq(ol, np.zeros((H, dk, dv)), np.zeros((H, 3, 2 * dk + dv)), inp, 0, T)
+    check_tokens(y, o["y"][0])
+    assert state_rel_err(host(cache.state), o["state"]) < 1e-4
+
+
 def test_packed_sequences_with_padding():
     """Four packed sequences (lengths 70, 0, 2, 129) with their own start
     states and windows, one padding row (-1), slots in permuted order."""
