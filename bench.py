@@ -288,6 +288,11 @@ def extras(torch, api, synth, layer, cache, step_inputs, y, slots, B, H, dk, dv,
     cb = Bv * H * (dk * dv * 4 + 3 * (2 * dk + dv) * 2) * 2
     ex["spec_verify_b16_t8"] = {"us_per_call": sv * 1e6, "token_heads_per_s": Bv * T * H / sv,
                                 "algorithmic_gbs": vb / sv / 1e9, "frac_of_8tbs": vb / sv / 8e12}
+    # the snapshots are written once and read at most once (by the commit):
+    # the same call with non-temporal state traffic
+    svs = timed(torch, stream, lambda: api.kda_spec_verify(sl_layer, cache, live, rest, vinp, yv), 20)
+    ex["spec_verify_b16_t8_stream"] = {"us_per_call": svs * 1e6, "token_heads_per_s": Bv * T * H / svs,
+                                       "algorithmic_gbs": vb / svs / 1e9, "frac_of_8tbs": vb / svs / 8e12}
     ex["spec_commit_b16"] = {"us_per_call": sc * 1e6, "mean_accepted": Lm,
                              "algorithmic_gbs": cb / sc / 1e9}
     ex["chunk_prefill_t32k"] = prefill_extra(torch, api, synth, stream)
