@@ -269,6 +269,15 @@ def extras(torch, api, synth, layer, cache, step_inputs, y, slots, B, H, dk, dv,
     s = timed(torch, stream, lambda: api.kda_copy_probe(dst, src), 10)
     ex["copy_probe_1gib"] = {"gbs": 2 * n * 4 / s / 1e9, "us": s * 1e6}
     del src, dst
+    # the same copy over 128 MiB each way, repeated: the size of the decode's
+    # state traffic per step, resident in the 256 MB Infinity Cache like the
+    # hot decode's state
+    n = 1 << 25
+    src = torch.empty(n, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    dst = torch.empty_like(src)
+    s = timed(torch, stream, lambda: api.kda_copy_probe(dst, src), 50)
+    ex["copy_probe_128mib_hot"] = {"gbs": 2 * n * 4 / s / 1e9, "us": s * 1e6}
+    del src, dst
     # spec-verify B=16 x T=8 and commit
     cfg = synth.WORKLOADS["spec_verify_b16_t8"]
     Bv, T = cfg["B"], cfg["T"]
