@@ -626,6 +626,9 @@ __device__ __forceinline__ void scan_load_a(const PrefillWs &ws, size_t gh, int 
         o.w[k] = load_split8(ws.Wn_hi, ws.Wn_lo, rw + 32 * k);
         o.q[k] = load_split8(ws.Q_hi, ws.Q_lo, rw + 32 * k);
     }
+    const size_t rp = gh * kChunk * kChunk + (16 * w4 + lr) * kChunk + 8 * lk;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) o.pm[k] = load_split8(ws.P_hi, ws.P_lo, rp + 32 * k);
 }
 
 // second half: P, Kd^T, U~ and e^(G_C)
@@ -633,9 +636,6 @@ template <int DK, int DV>
 __device__ __forceinline__ void scan_load_b(const PrefillWs &ws, size_t gh, int w4, int lr, int lk, int j0,
                                             ScanOps<DK> &o) {
     constexpr int TS = DK / 64;
-    const size_t rp = gh * kChunk * kChunk + (16 * w4 + lr) * kChunk + 8 * lk;
-#pragma unroll
-    for (int k = 0; k < 2; ++k) o.pm[k] = load_split8(ws.P_hi, ws.P_lo, rp + 32 * k);
 #pragma unroll
     for (int m = 0; m < TS; ++m) {
         const size_t rk = gh * DK * kChunk + (16 * (TS * w4 + m) + lr) * kChunk + 8 * lk;
