@@ -21,7 +21,7 @@
 //   scan   one workgroup per (sequence, head, 16 columns of d_v): the fp32 state
 //          carried from chunk to chunk (state columns are independent given the
 //          chunk factors), unnormalised outputs O written to y
-//   norm   one wave per (token, head): RMSNorm over d_v, weight, sigmoid gate
+//   norm   RMSNorm over d_v, weight, sigmoid gate on the rows of y
 #include "kda_device.h"
 #include "kda_internal.h"
 
