@@ -133,6 +133,43 @@ def test_packed_sequences_with_padding():
     assert np.array_equal(host(cache.state[[3, 5]]), s_before[[3, 5]])
 
 
+def test_many_sequences_mixed_lengths():
+    """41 packed sequences with seeded lengths from 0 to 200 (chunk-aligned,
+    one-token and empty ones included), three padding rows, slots in random
+    order: every output, final state and window against the oracle."""
+    g = synth.rng(975)
+    H, dk, dv = 2, 64, 64
+    params = synth.layer_params(g, H, dk, dv)
+    dl, ol = layer_pair(params)
+    lens = [int(x) for x in g.integers(0, 201, size=41)]
+    lens[:6] = [0, 1, 64, 128, 3, 65]
+    n_slots = 48
+    slots = [int(x) for x in g.permutation(n_slots)[:41]]
+    for i in (7, 19, 33):
+        slots[i] = -1
+    total = sum(lens)
+    inp = synth.token_inputs(g, (total,), H, dk, dv, "bf16")
+    cache = new_cache(n_slots, H, dk, dv, "bf16", fill_seed=4)
+    s_before = host(cache.state)
+    w_before = host(cache.conv_state)
+    y, cu = run_prefill(dl, cache, slots, lens, inp, "bf16")
+    assert cache.err_flag.item() == 0
+    worst = 0.0
+    for i, (sl, ln) in enumerate(zip(slots, lens)):
+        a, b = cu[i], cu[i + 1]
+        if sl < 0:
+            assert np.all(y[a:b] == 0.0)
+            continue
+        o = oracle_seq(ol, s_before[sl], w_before[sl], inp, a, b)
+        if ln:
+            errs = [parity_error(y[t], o["y"][0][t - a]) for t in range(a, b)]
+            worst = max(worst, max(errs))
+        assert state_rel_err(host(cache.state[sl:sl + 1]), o["state"]) < 1e-4
+        assert np.array_equal(host(cache.conv_state[sl:sl + 1]), o["window"])
+    print(f"  prefill parity over {len(lens)} sequences: worst max|d|/RMS = {worst:.3e}", flush=True)
+    assert worst <= TOL
+
+
 def test_prefill_then_decode_continues_the_sequence():
     g = synth.rng(980)
     H, dk, dv, T, D = 4, 128, 128, 100, 20
