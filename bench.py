@@ -316,11 +316,12 @@ def prefill_mfma_per_chunk_head(dk, dv, col_block=16):
     the four lower-triangular row tiles of T; the off-diagonal blocks of T
     itself, 13 steps (Z = A T then -T_bb Z for the six blocks below the
     diagonal, K = 16, 32 or 48 padded to steps of 32).  scan, per block of 16 state
-    columns: W S and Q S (d_k/32 steps for each of 4 row tiles), P U (2 steps
-    x 4 row tiles), Kd^T U (2 steps x d_k/16 row tiles)."""
+    columns: W S and Q S (d_k/32 steps for each of 4 row tiles), P U (1, 1, 2
+    and 2 steps for the 4 row tiles: P is lower triangular), Kd^T U (2 steps x
+    d_k/16 row tiles)."""
     ks = dk // 32
     intra = 3 * (10 * 2 * ks + (dk + dv) // 16 * 6 + 13)
-    scan = 3 * (dv // col_block) * (4 * 2 * ks + 4 * 2 + (dk // 16) * 2)
+    scan = 3 * (dv // col_block) * (4 * 2 * ks + 6 + (dk // 16) * 2)
     return intra + scan
 
 

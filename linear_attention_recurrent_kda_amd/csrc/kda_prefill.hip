@@ -617,6 +617,7 @@ __device__ __forceinline__ Split8 load_split8(const uint16_t *hi, const uint16_t
 }
 
 // first half of a chunk's operands: the d_k-contraction rows (-W, Q^ e^G)
+// and the P rows
 template <int DK>
 __device__ __forceinline__ void scan_load_a(const PrefillWs &ws, size_t gh, int w4, int lr, int lk, ScanOps<DK> &o) {
     constexpr int KS = DK / 32;
@@ -628,10 +629,11 @@ __device__ __forceinline__ void scan_load_a(const PrefillWs &ws, size_t gh, int 
     }
     const size_t rp = gh * kChunk * kChunk + (16 * w4 + lr) * kChunk + 8 * lk;
 #pragma unroll
-    for (int k = 0; k < 2; ++k) o.pm[k] = load_split8(ws.P_hi, ws.P_lo, rp + 32 * k);
+    for (int k = 0; k < 2; ++k)   // rows below 32 have P = 0 in tokens 32..63
+        if (w4 >= 2 || k == 0) o.pm[k] = load_split8(ws.P_hi, ws.P_lo, rp + 32 * k);
 }
 
-// second half: P, Kd^T, U~ and e^(G_C)
+// second half: Kd^T, U~ and e^(G_C)
 template <int DK, int DV>
 __device__ __forceinline__ void scan_load_b(const PrefillWs &ws, size_t gh, int w4, int lr, int lk, int j0,
                                             ScanOps<DK> &o) {
@@ -762,7 +764,8 @@ __global__ __launch_bounds__(kScanThreads) void kda_prefill_scan_kernel(PrefillP
             }
             // P rows beyond the chunk and above the diagonal are 0
 #pragma unroll
-            for (int k = 0; k < 2; ++k) mma3s(ops.pm[k], ub[k], ao);
+            for (int k = 0; k < 2; ++k)
+                if (w4 >= 2 || k == 0) mma3s(ops.pm[k], ub[k], ao);
 #pragma unroll
             for (int m = 0; m < TS; ++m) {
                 Acc3 as;
