@@ -33,18 +33,28 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 // Device pointers into the caller's workspace.  The per-chunk factors the
 // scan multiplies on MFMA are stored pre-split as bf16 pairs (hi = bf16(x),
-// lo = bf16(x - hi)), in the row-major layout the scan's operand loads read.
+// lo = bf16(x - hi)), each matrix in MFMA operand order (opnd_off below).
 struct PrefillWs {
     int32_t *meta;            // [0]: 1 if cu_seqlens is valid; [1 + s]: first chunk of s, s <= N
     float *vv;                // [G, 64, H, d_v]  conv'd v, rows past a chunk's end unused
-    uint16_t *Wn_hi, *Wn_lo;  // [G, H, 64, d_k]  -W
-    uint16_t *Q_hi, *Q_lo;    // [G, H, 64, d_k]  Q^ e^G
-    uint16_t *K_hi, *K_lo;    // [G, H, d_k, 64]  (K^ e^(G_C - G))^T
-    uint16_t *P_hi, *P_lo;    // [G, H, 64, 64]
+    uint16_t *Wn_hi, *Wn_lo;  // [G, H] x (64 x d_k)  -W
+    uint16_t *Q_hi, *Q_lo;    // [G, H] x (64 x d_k)  Q^ e^G
+    uint16_t *K_hi, *K_lo;    // [G, H] x (d_k x 64)  (K^ e^(G_C - G))^T
+    uint16_t *P_hi, *P_lo;    // [G, H] x (64 x 64)
     float *Ut;                // [G, H, 64, d_v]
     float *gC;                // [G, H, d_k]  e^(G_C)
     int G_max;
 };
+
+// Offset of element (row, k) of an R x K matrix stored in MFMA A-operand
+// order: 16 x 32 tiles (row tile major, then k step), each tile as 64 lanes x
+// 8 consecutive elements with lane = row % 16 + 16 ((k % 32) / 8), the
+// layout of v_mfma_f32_16x16x32_bf16's A operand.  A wave's load of one
+// tile is one contiguous kilobyte (eight whole 128-byte lines).
+template <int K>
+__device__ __forceinline__ size_t opnd_off(int row, int k) {
+    return ((size_t)((row / 16) * (K / 32) + k / 32) * kWave + row % 16 + 16 * ((k % 32) / 8)) * 8 + k % 8;
+}
 
 struct WsLayout {
     size_t meta, vv, Wn_hi, Wn_lo, Q_hi, Q_lo, K_hi, K_lo, P_hi, P_lo, Ut, gC, total;
@@ -389,7 +399,7 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
         if (bs > bt) {
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
-                const int idx = (16 * bt + 4 * lk + rr) * kChunk + 16 * bs + lr;
+                const size_t idx = opnd_off<kChunk>(16 * bt + 4 * lk + rr, 16 * bs + lr);
                 Ph[idx] = 0;
                 Pl[idx] = 0;
             }
@@ -449,7 +459,8 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
         for (int rr = 0; rr < 4; ++rr) {
             const int t = 16 * bt + 4 * lk + rr, sv = 16 * bs + lr;
             L.A[t][sv] = sv < t ? L.beta[t] * aA[rr] : 0.f;
-            split_bits(sv <= t ? aP[rr] : 0.f, Ph[t * kChunk + sv], Pl[t * kChunk + sv]);
+            const size_t idx = opnd_off<kChunk>(t, sv);
+            split_bits(sv <= t ? aP[rr] : 0.f, Ph[idx], Pl[idx]);
         }
     }
     // 4. decayed factors for the scan: Q^ e^G (rows), (K^ e^(G_C - G))^T, e^(G_C)
@@ -466,8 +477,9 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
             hv[e] = hb;
             lv[e] = (__bf16)(v - (float)hb);
         }
-        *reinterpret_cast<bf16x8 *>(ws.Q_hi + gh * kChunk * DK + r * DK + i0) = hv;
-        *reinterpret_cast<bf16x8 *>(ws.Q_lo + gh * kChunk * DK + r * DK + i0) = lv;
+        const size_t o = gh * kChunk * DK + opnd_off<DK>(r, i0);
+        *reinterpret_cast<bf16x8 *>(ws.Q_hi + o) = hv;
+        *reinterpret_cast<bf16x8 *>(ws.Q_lo + o) = lv;
     }
     for (int e8 = tid; e8 < kChunk * DK / 8; e8 += kIntraThreads) {
         const int i = e8 % DK, r0 = 8 * (e8 / DK);   // lanes along channels: column reads spread over banks
@@ -482,8 +494,9 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
             hv[e] = hb;
             lv[e] = (__bf16)(v - (float)hb);
         }
-        *reinterpret_cast<bf16x8 *>(ws.K_hi + gh * DK * kChunk + i * kChunk + r0) = hv;
-        *reinterpret_cast<bf16x8 *>(ws.K_lo + gh * DK * kChunk + i * kChunk + r0) = lv;
+        const size_t o = gh * DK * kChunk + opnd_off<kChunk>(i, r0);
+        *reinterpret_cast<bf16x8 *>(ws.K_hi + o) = hv;
+        *reinterpret_cast<bf16x8 *>(ws.K_lo + o) = lv;
     }
     if (tid < DK) ws.gC[gh * DK + tid] = exp2f(L.G[last][tid]);
 
@@ -576,7 +589,7 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
             for (int rr = 0; rr < 4; ++rr) {
                 const int t = 16 * rt + 4 * lk + rr;
                 if (isw) {
-                    const size_t o = gh * kChunk * DK + t * DK + col;
+                    const size_t o = gh * kChunk * DK + opnd_off<DK>(t, col);
                     split_bits(-acc[rr], ws.Wn_hi[o], ws.Wn_lo[o]);
                 } else {
                     ws.Ut[gh * kChunk * DV + t * DV + (col - DK)] = acc[rr];
@@ -621,16 +634,16 @@ __device__ __forceinline__ Split8 load_split8(const uint16_t *hi, const uint16_t
 template <int DK>
 __device__ __forceinline__ void scan_load_a(const PrefillWs &ws, size_t gh, int w4, int lr, int lk, ScanOps<DK> &o) {
     constexpr int KS = DK / 32;
-    const size_t rw = gh * kChunk * DK + (16 * w4 + lr) * DK + 8 * lk;
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
-        o.w[k] = load_split8(ws.Wn_hi, ws.Wn_lo, rw + 32 * k);
-        o.q[k] = load_split8(ws.Q_hi, ws.Q_lo, rw + 32 * k);
+        const size_t rw = gh * kChunk * DK + opnd_off<DK>(16 * w4 + lr, 32 * k + 8 * lk);
+        o.w[k] = load_split8(ws.Wn_hi, ws.Wn_lo, rw);
+        o.q[k] = load_split8(ws.Q_hi, ws.Q_lo, rw);
     }
-    const size_t rp = gh * kChunk * kChunk + (16 * w4 + lr) * kChunk + 8 * lk;
 #pragma unroll
     for (int k = 0; k < 2; ++k)   // rows below 32 have P = 0 in tokens 32..63
-        if (w4 >= 2 || k == 0) o.pm[k] = load_split8(ws.P_hi, ws.P_lo, rp + 32 * k);
+        if (w4 >= 2 || k == 0)
+            o.pm[k] = load_split8(ws.P_hi, ws.P_lo, gh * kChunk * kChunk + opnd_off<kChunk>(16 * w4 + lr, 32 * k + 8 * lk));
 }
 
 // second half: Kd^T, U~ and e^(G_C)
@@ -640,9 +653,10 @@ __device__ __forceinline__ void scan_load_b(const PrefillWs &ws, size_t gh, int 
     constexpr int TS = DK / 64;
 #pragma unroll
     for (int m = 0; m < TS; ++m) {
-        const size_t rk = gh * DK * kChunk + (16 * (TS * w4 + m) + lr) * kChunk + 8 * lk;
 #pragma unroll
-        for (int k = 0; k < 2; ++k) o.kd[m][k] = load_split8(ws.K_hi, ws.K_lo, rk + 32 * k);
+        for (int k = 0; k < 2; ++k)
+            o.kd[m][k] = load_split8(ws.K_hi, ws.K_lo,
+                                     gh * DK * kChunk + opnd_off<kChunk>(16 * (TS * w4 + m) + lr, 32 * k + 8 * lk));
 #pragma unroll
         for (int r = 0; r < 4; ++r) o.gc[m][r] = ws.gC[gh * DK + 16 * (TS * w4 + m) + 4 * lk + r];
     }
