@@ -291,12 +291,31 @@ __device__ __forceinline__ void prep_gates(const PrefillParams &p, int t0, int n
 
 constexpr float kSafeSpan = 60.f;
 
-// bf16 pair of an fp32 value, as raw bits
-__device__ __forceinline__ void split_bits(float x, uint16_t &hi, uint16_t &lo) {
-    const __bf16 h = (__bf16)x;
-    const __bf16 l = (__bf16)(x - (float)h);
-    hi = __builtin_bit_cast(uint16_t, h);
-    lo = __builtin_bit_cast(uint16_t, l);
+// A 16 x 16 fp32 tile in the MFMA result layout (lane l holds rows
+// 4 (l / 16) + r, column l % 16) written to a split bf16 matrix with K
+// columns in operand order, as 16-byte stores: through the wave's LDS
+// scratch, lanes 0..31 each take 8 consecutive columns of one row.
+template <int K>
+__device__ __forceinline__ void store_tile_split(float (*scr)[17], const f32x4 &v, int lane, uint16_t *hi,
+                                                 uint16_t *lo, int row0, int col0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) scr[4 * (lane / 16) + r][lane % 16] = v[r];
+    __builtin_amdgcn_wave_barrier();
+    if (lane < 32) {
+        const int row = lane % 16, kq = lane / 16;
+        bf16x8 hv, lv;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float x = scr[row][8 * kq + e];
+            const __bf16 hb = (__bf16)x;
+            hv[e] = hb;
+            lv[e] = (__bf16)(x - (float)hb);
+        }
+        const size_t o = opnd_off<K>(row0 + row, col0 + 8 * kq);
+        *reinterpret_cast<bf16x8 *>(hi + o) = hv;
+        *reinterpret_cast<bf16x8 *>(lo + o) = lv;
+    }
+    __builtin_amdgcn_wave_barrier();
 }
 
 // 8 consecutive fp32 values of an LDS row (16-byte aligned)
@@ -397,11 +416,11 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
         const int bt = lbt[tile], bs = lbs[tile];
         f32x4 aA = {0.f, 0.f, 0.f, 0.f}, aP = aA;
         if (bs > bt) {
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const size_t idx = opnd_off<kChunk>(16 * bt + 4 * lk + rr, 16 * bs + lr);
-                Ph[idx] = 0;
-                Pl[idx] = 0;
+            if (lane < 32) {
+                const bf16x8 z = {};
+                const size_t o = opnd_off<kChunk>(16 * bt + lane % 16, 16 * bs + 8 * (lane / 16));
+                *reinterpret_cast<bf16x8 *>(Ph + o) = z;
+                *reinterpret_cast<bf16x8 *>(Pl + o) = z;
             }
             continue;
         }
@@ -459,14 +478,17 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
         for (int rr = 0; rr < 4; ++rr) {
             const int t = 16 * bt + 4 * lk + rr, sv = 16 * bs + lr;
             L.A[t][sv] = sv < t ? L.beta[t] * aA[rr] : 0.f;
-            const size_t idx = opnd_off<kChunk>(t, sv);
-            split_bits(sv <= t ? aP[rr] : 0.f, Ph[idx], Pl[idx]);
+            aP[rr] = sv <= t ? aP[rr] : 0.f;
         }
+        store_tile_split<kChunk>(L.D[wave], aP, lane, Ph, Pl, 16 * bt, 16 * bs);
     }
     // 4. decayed factors for the scan: Q^ e^G (rows), (K^ e^(G_C - G))^T, e^(G_C)
+    //    Unit e8 (8 elements) is stored at 8 e8 in operand order, so each wave
+    //    writes whole lines: tile e8 / 64, lane e8 % 64 of that tile.
     const int last = max(n - 1, 0);
     for (int e8 = tid; e8 < kChunk * DK / 8; e8 += kIntraThreads) {
-        const int r = e8 / (DK / 8), i0 = 8 * (e8 % (DK / 8));
+        const int tl = e8 / kWave, ln = e8 % kWave;
+        const int r = 16 * (tl / KS) + ln % 16, i0 = 32 * (tl % KS) + 8 * (ln / 16);
         float x[8];
         lds8(&L.Q[r][i0], x);
         bf16x8 hv, lv;
@@ -477,12 +499,13 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
             hv[e] = hb;
             lv[e] = (__bf16)(v - (float)hb);
         }
-        const size_t o = gh * kChunk * DK + opnd_off<DK>(r, i0);
+        const size_t o = gh * kChunk * DK + (size_t)8 * e8;   // = opnd_off<DK>(r, i0)
         *reinterpret_cast<bf16x8 *>(ws.Q_hi + o) = hv;
         *reinterpret_cast<bf16x8 *>(ws.Q_lo + o) = lv;
     }
     for (int e8 = tid; e8 < kChunk * DK / 8; e8 += kIntraThreads) {
-        const int i = e8 % DK, r0 = 8 * (e8 / DK);   // lanes along channels: column reads spread over banks
+        const int tl = e8 / kWave, ln = e8 % kWave;
+        const int i = 16 * (tl / 2) + ln % 16, r0 = 32 * (tl % 2) + 8 * (ln / 16);
         const float gl = L.G[last][i];
         bf16x8 hv, lv;
 #pragma unroll
@@ -494,7 +517,7 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
             hv[e] = hb;
             lv[e] = (__bf16)(v - (float)hb);
         }
-        const size_t o = gh * DK * kChunk + opnd_off<kChunk>(i, r0);
+        const size_t o = gh * DK * kChunk + (size_t)8 * e8;   // = opnd_off<kChunk>(i, r0)
         *reinterpret_cast<bf16x8 *>(ws.K_hi + o) = hv;
         *reinterpret_cast<bf16x8 *>(ws.K_lo + o) = lv;
     }
@@ -585,15 +608,14 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             acc = mma3(ta[rt][0], rb[0], acc);
             if (rt >= 2) acc = mma3(ta[rt][1], rb[1], acc);   // T is lower triangular
+            if (isw) {
+                const f32x4 wn = -acc;
+                store_tile_split<DK>(L.D[wave], wn, lane, ws.Wn_hi + gh * kChunk * DK, ws.Wn_lo + gh * kChunk * DK,
+                                     16 * rt, 16 * ct);
+            } else {
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int t = 16 * rt + 4 * lk + rr;
-                if (isw) {
-                    const size_t o = gh * kChunk * DK + opnd_off<DK>(t, col);
-                    split_bits(-acc[rr], ws.Wn_hi[o], ws.Wn_lo[o]);
-                } else {
-                    ws.Ut[gh * kChunk * DV + t * DV + (col - DK)] = acc[rr];
-                }
+                for (int rr = 0; rr < 4; ++rr)
+                    ws.Ut[gh * kChunk * DV + (16 * rt + 4 * lk + rr) * DV + (col - DK)] = acc[rr];
             }
         }
     }
