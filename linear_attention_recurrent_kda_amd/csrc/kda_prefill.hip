@@ -690,8 +690,12 @@ template <int DK, int DV, typename Tin>
 __global__ __launch_bounds__(kScanThreads) void kda_prefill_scan_kernel(PrefillParams p, PrefillWs ws) {
     constexpr int CB = kColBlock, CH = 2 * DK + DV, KS = DK / 32, TS = DK / 64;
     static_assert(CH <= kScanThreads, "one thread per conv channel");
+    // S in fp32 (two buffers) and, for the MFMA B operands, S and U split into
+    // bf16 hi / lo and transposed (a lane's 8 consecutive rows are one 16-byte
+    // read); rows padded by 8 to spread the transposed 2-byte writes over banks
     __shared__ __align__(16) float S[2][DK][CB];
-    __shared__ __align__(16) float U[kChunk][CB];
+    __shared__ __align__(16) __bf16 Sh[2][CB][DK + 8], Sl[2][CB][DK + 8];
+    __shared__ __align__(16) __bf16 Uh[CB][kChunk + 8], Ul[CB][kChunk + 8];
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int team = wave / 4, w4 = wave % 4;
     const int lr = lane % 16, lk = lane / 16;
@@ -730,7 +734,14 @@ __global__ __launch_bounds__(kScanThreads) void kda_prefill_scan_kernel(PrefillP
     }
 
     float *Sg = p.state + ((size_t)slot * H + h) * DK * DV;
-    for (int e = tid; e < DK * CB; e += kScanThreads) S[0][e / CB][e % CB] = Sg[(e / CB) * DV + j0 + e % CB];
+    for (int e = tid; e < DK * CB; e += kScanThreads) {
+        const int row = e / CB, col = e % CB;
+        const float x = Sg[row * DV + j0 + col];
+        const __bf16 hb = (__bf16)x;
+        S[0][row][col] = x;
+        Sh[0][col][row] = hb;
+        Sl[0][col][row] = (__bf16)(x - (float)hb);
+    }
 
     // bf16x3 product with the three partial products in separate
     // accumulators (short dependency chains), summed at the end
@@ -767,10 +778,8 @@ __global__ __launch_bounds__(kScanThreads) void kda_prefill_scan_kernel(PrefillP
             Split8 sb[KS];
 #pragma unroll
             for (int k = 0; k < KS; ++k) {
-                float x[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] = S[cur][32 * k + 8 * lk + e][lr];
-                sb[k] = split8(x);
+                sb[k].hi = *reinterpret_cast<const bf16x8 *>(&Sh[cur][lr][32 * k + 8 * lk]);
+                sb[k].lo = *reinterpret_cast<const bf16x8 *>(&Sl[cur][lr][32 * k + 8 * lk]);
             }
             Acc3 au;
             zero3(au);
@@ -781,7 +790,12 @@ __global__ __launch_bounds__(kScanThreads) void kda_prefill_scan_kernel(PrefillP
                 mma3s(ops.q[k], sb[k], ao);
             }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) U[16 * w4 + 4 * lk + r][lr] = ops.ut[r] + sum3(au, r);
+            for (int r = 0; r < 4; ++r) {
+                const float u = ops.ut[r] + sum3(au, r);
+                const __bf16 hb = (__bf16)u;
+                Uh[lr][16 * w4 + 4 * lk + r] = hb;
+                Ul[lr][16 * w4 + 4 * lk + r] = (__bf16)(u - (float)hb);
+            }
         } else if (c + 1 < nch) {
             scan_load_a<DK>(ws, gnext, w4, lr, lk, ops);
         }
@@ -793,10 +807,8 @@ __global__ __launch_bounds__(kScanThreads) void kda_prefill_scan_kernel(PrefillP
             Split8 ub[2];
 #pragma unroll
             for (int k = 0; k < 2; ++k) {
-                float x[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] = U[32 * k + 8 * lk + e][lr];
-                ub[k] = split8(x);
+                ub[k].hi = *reinterpret_cast<const bf16x8 *>(&Uh[lr][32 * k + 8 * lk]);
+                ub[k].lo = *reinterpret_cast<const bf16x8 *>(&Ul[lr][32 * k + 8 * lk]);
             }
             // P rows beyond the chunk and above the diagonal are 0
 #pragma unroll
@@ -811,7 +823,11 @@ __global__ __launch_bounds__(kScanThreads) void kda_prefill_scan_kernel(PrefillP
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int row = 16 * (TS * w4 + m) + 4 * lk + r;
-                    S[cur ^ 1][row][lr] = ops.gc[m][r] * S[cur][row][lr] + sum3(as, r);
+                    const float x = ops.gc[m][r] * S[cur][row][lr] + sum3(as, r);
+                    const __bf16 hb = (__bf16)x;
+                    S[cur ^ 1][row][lr] = x;
+                    Sh[cur ^ 1][lr][row] = hb;
+                    Sl[cur ^ 1][lr][row] = (__bf16)(x - (float)hb);
                 }
             }
 #pragma unroll
