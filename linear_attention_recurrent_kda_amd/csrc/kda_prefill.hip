@@ -139,7 +139,8 @@ __global__ void kda_prefill_meta_kernel(PrefillParams p, PrefillWs ws) {
 //
 // LDS holds q^, k^ (rows, zero past the chunk's end), the decay prefix sums,
 // A and T: about 143 KiB at d_k = 128, one workgroup per CU.  Only v goes
-// through the workspace (L2).
+// through the workspace (L2).  The factors for the scan (P, Q^ e^G, Kd^T,
+// -W as bf16 hi/lo; U~ in fp32) are written in the order its loads read.
 // ---------------------------------------------------------------------------
 constexpr int kIntraThreads = 512;
 constexpr int kIntraWaves = kIntraThreads / kWave;
@@ -154,7 +155,7 @@ struct __align__(16) IntraLds {
     float A[kChunk][kChunk + 1];        // beta_t (K K^T * decay), strictly lower part used
     float T[kChunk][kChunk + 4];        // (I + A)^-1
     float Z[3][16][17];                 // block-inverse scratch
-    float D[kIntraWaves][16][17];       // per-wave scratch of the direct tile path
+    float D[kIntraWaves][16][17];       // per-wave scratch: direct tiles, tile stores
     float beta[kChunk];
     int safe[4];
 };
