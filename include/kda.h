@@ -165,7 +165,9 @@ kda_status kda_spec_commit(const kda_layer *layer, const kda_cache *cache,
  *   inputs: total_T tokens; y [total_T, H, d_v] fp32.
  *   chunk: 64.  workspace: >= kda_chunk_prefill_workspace_bytes(...).
  * The state and window at slot_idx[s] are the start state (zero them for a
- * fresh sequence) and are replaced by the final ones.
+ * fresh sequence) and are replaced by the final ones.  total_T = 0 is
+ * allowed: inputs' pointers and y are then not read and may be NULL (the
+ * dtype must still be valid); cu_seqlens is still checked.
  */
 kda_status kda_chunk_prefill(const kda_layer *layer, const kda_cache *cache,
                              const int32_t *slot_idx, const int32_t *cu_seqlens,

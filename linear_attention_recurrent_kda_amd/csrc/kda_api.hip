@@ -158,11 +158,18 @@ KDA_EXPORT kda_status kda_chunk_prefill(const kda_layer *layer, const kda_cache 
                                         size_t workspace_bytes, void *hip_stream) {
     KDA_TRY(check_layer(layer));
     KDA_TRY(check_cache(cache));
-    KDA_TRY(check_inputs(inputs));
     if (N_seq < 1 || total_T < 0 || chunk <= 0) return KDA_ERR_SHAPE;
     if (chunk != 64) return KDA_ERR_UNSUPPORTED;
-    if (!slot_idx || !cu_seqlens || !y) return KDA_ERR_NULL;
-    if (!aligned(slot_idx, 4) || !aligned(cu_seqlens, 4) || !aligned(y, 16)) return KDA_ERR_ALIGN;
+    // with no tokens the inputs and y are never read (and may be NULL)
+    if (!inputs) return KDA_ERR_NULL;
+    if (inputs->dtype != KDA_F32 && inputs->dtype != KDA_BF16) return KDA_ERR_DTYPE;
+    if (total_T > 0) {
+        KDA_TRY(check_inputs(inputs));
+        if (!y) return KDA_ERR_NULL;
+        if (!aligned(y, 16)) return KDA_ERR_ALIGN;
+    }
+    if (!slot_idx || !cu_seqlens) return KDA_ERR_NULL;
+    if (!aligned(slot_idx, 4) || !aligned(cu_seqlens, 4)) return KDA_ERR_ALIGN;
     const size_t need = prefill_workspace_bytes(layer->H, layer->d_k, layer->d_v, total_T, N_seq, chunk);
     if (need && !workspace) return KDA_ERR_NULL;
     if (workspace_bytes < need) return KDA_ERR_WORKSPACE;

@@ -142,6 +142,15 @@ def test_prefill_validation(lib):
         assert p(wb=need - 1) == 6
         assert p(ws=None) == 1
     assert lib.kda_chunk_prefill_workspace_bytes(ctypes.byref(L), 128, 1, 32) == 0
+    # tokens need their input pointers; with no tokens only the dtype is checked
+    Inull = good_inputs()
+    Inull.x_q = None
+    assert lib.kda_chunk_prefill(ctypes.byref(L), ctypes.byref(C), FAKE, FAKE, 1, 128, 64,
+                                 ctypes.byref(Inull), FAKE, FAKE, 1 << 30, None) == 1
+    Ibad = good_inputs()
+    Ibad.dtype = 7
+    assert lib.kda_chunk_prefill(ctypes.byref(L), ctypes.byref(C), FAKE, FAKE, 1, 0, 64,
+                                 ctypes.byref(Ibad), None, FAKE, 1 << 30, None) == 3
 
 
 def test_copy_probe_validation(lib):

@@ -218,6 +218,21 @@ def test_full_length_32k_sampled():
     assert err < 1e-3
 
 
+def test_all_sequences_empty():
+    """total_T = 0: nothing to compute; states and windows stay bitwise."""
+    g = synth.rng(985)
+    H, dk, dv = 2, 128, 128
+    params = synth.layer_params(g, H, dk, dv)
+    dl, _ = layer_pair(params)
+    inp = synth.token_inputs(g, (0,), H, dk, dv, "bf16")
+    cache = new_cache(3, H, dk, dv, "bf16", fill_seed=5)
+    s_before, w_before = cache.state.clone(), cache.conv_state.clone()
+    y, _ = run_prefill(dl, cache, [2, 0, 1], [0, 0, 0], inp, "bf16")
+    assert y.shape == (0, H, dv)
+    assert torch.equal(cache.state, s_before) and torch.equal(cache.conv_state, w_before)
+    assert cache.err_flag.item() == 0
+
+
 def test_invalid_cu_seqlens_flags_and_leaves_state():
     g = synth.rng(990)
     H, dk, dv = 2, 64, 64
