@@ -54,6 +54,22 @@ def verify_bytes_per_seq_head(T=8, dk=128, dv=128, B=16, in_bytes=2):
             + (dk + ch * 4 + dv) * 4 / B)                     # params
 
 
+def verify_delta_bytes_per_seq_head(T=8, dk=128, dv=128, B=16, in_bytes=2):
+    ch = 2 * dk + dv
+    return (dk * dv * 4 + 3 * ch * in_bytes                  # S0 + window read
+            + T * ((3 * dk + 2 * dv) * in_bytes + in_bytes)   # inputs
+            + T * ch * (4 + in_bytes)                         # replay records
+            + T * dv * 4                                      # outputs
+            + (dk + ch * 4 + dv) * 4 / B)                     # params
+
+
+def commit_delta_bytes_per_seq_head(L, dk=128, dv=128, in_bytes=2):
+    ch = 2 * dk + dv
+    return (2 * dk * dv * 4                  # live state read + write
+            + L * (2 * dk + dv) * 4          # alpha, k^, d of the accepted tokens
+            + 2 * 3 * ch * in_bytes)         # window rows read + written
+
+
 # the files that define the decode kernel and its launch: the counter
 # summary is stale once any of them changes
 DECODE_SOURCES = ("kda_recurrent.hip", "kda_device.h", "kda_internal.h")
@@ -304,6 +320,18 @@ def extras(torch, api, synth, layer, cache, step_inputs, y, slots, B, H, dk, dv,
                                        "algorithmic_gbs": vb / svs / 1e9, "frac_of_8tbs": vb / svs / 8e12}
     ex["spec_commit_b16"] = {"us_per_call": sc * 1e6, "mean_accepted": Lm,
                              "algorithmic_gbs": cb / sc / 1e9}
+    # replayable deltas instead of snapshots (same workload, same accepted lengths)
+    delta = api.new_spec_delta(layer, Bv, T, torch.bfloat16, "cuda:0")
+    svd = timed(torch, stream, lambda: api.kda_spec_verify_delta(layer, cache, live, vinp, yv, delta), 20)
+    scd = timed(torch, stream, lambda: api.kda_spec_commit_delta(layer, cache, live, delta, acc), 20)
+    vdb = verify_delta_bytes_per_seq_head(T, dk, dv, Bv) * Bv * H
+    cdb = sum(commit_delta_bytes_per_seq_head(int(L), dk, dv) for L in acc.cpu().tolist()) * H
+    ex["spec_verify_delta_b16_t8"] = {"us_per_call": svd * 1e6, "token_heads_per_s": Bv * T * H / svd,
+                                      "algorithmic_gbs": vdb / svd / 1e9, "frac_of_8tbs": vdb / svd / 8e12,
+                                      "bytes_per_call": vdb}
+    ex["spec_commit_delta_b16"] = {"us_per_call": scd * 1e6, "mean_accepted": Lm,
+                                   "algorithmic_gbs": cdb / scd / 1e9, "bytes_per_call": cdb}
+    ex["spec_step_b16_t8"] = {"snapshots_us": (sv + sc) * 1e6, "deltas_us": (svd + scd) * 1e6}
     ex["chunk_prefill_t32k"] = prefill_extra(torch, api, synth, stream)
     return ex
 

@@ -155,6 +155,65 @@ kda_status kda_spec_commit(const kda_layer *layer, const kda_cache *cache,
                            kda_dtype window_dtype, void *hip_stream);
 
 /*
+ * Replayable-delta verification: the same verification as kda_spec_verify,
+ * but instead of a full state snapshot per token (d_k*d_v*4 bytes) it keeps a
+ * small replay record per (sequence, token, head), and the commit re-applies
+ * the accepted records to the live state.  The verification of draft tokens
+ * is that of "vLLM Kimi K3 support", section "Speculative decoding with
+ * DSpark"; the pages do not say how a rejected suffix is rolled back, and
+ * this form moves about a sixth of the snapshot form's bytes per verified
+ * token at d_k = d_v = 128.
+ *
+ * Record layout.  The record buffer is [B, T, H] records of
+ * kda_spec_delta_bytes(layer, 1, 1, dtype) / H bytes each = (2 d_k + d_v) *
+ * (4 + sizeof(input)) bytes, record (b, t, h) at index (b*T + t)*H + h:
+ *   float alpha[d_k];    per-channel decay of the token
+ *   float khat[d_k];     the normalised key k^
+ *   float d[d_v];        beta * (v - S'^T k^): the rank-one update's row
+ *   input x[2d_k + d_v]; the token's raw (pre-conv) inputs q | k | v
+ * so that the state after the token is diag(alpha) S + khat d^T, evaluated
+ * in fp32 with the same two roundings per element as kda_decode.
+ */
+
+/* Bytes of the record buffer for B sequences x T draft tokens (0 on invalid
+ * sizes: 1 <= T <= 16, B >= 0, a valid layer and dtype). */
+size_t kda_spec_delta_bytes(const kda_layer *layer, int32_t B, int32_t T, kda_dtype dtype);
+
+/*
+ * kda_spec_verify_delta -- verify T draft tokens per sequence from the state
+ * at slot_idx[b] (NOT modified), writing y [B, T, H, d_v] fp32 exactly as
+ * kda_spec_verify does (bitwise) and one replay record per processed token
+ * into `delta` (delta_bytes >= kda_spec_delta_bytes(layer, B, T, dtype),
+ * 16-byte aligned).  draft_len [B] or NULL as in kda_spec_verify: records of
+ * tokens past draft_len[b] are not written.  Padding (-1) and bad slots as for
+ * decode.  Errors: KDA_ERR_WORKSPACE when delta_bytes is too small.
+ */
+kda_status kda_spec_verify_delta(const kda_layer *layer, const kda_cache *cache,
+                                 const int32_t *slot_idx, int32_t B, int32_t T,
+                                 const int32_t *draft_len, const kda_inputs *inputs,
+                                 float *y, void *delta, size_t delta_bytes,
+                                 void *hip_stream);
+
+/*
+ * kda_spec_commit_delta -- keep the accepted prefix of a delta verification.
+ *   accepted_len [B] int32 (device), each in [0, T]: replays records
+ *   0 .. L-1 of sequence b onto the state at slot_idx[b] and sets its conv
+ *   window to the last three raw inputs of (window, accepted tokens).  The
+ *   result is bitwise equal to L kda_decode calls (and to kda_spec_commit
+ *   after kda_spec_verify).  L = 0 and slot -1 are no-ops; a length outside
+ *   [0, T] or a bad slot sets err_flag and leaves that sequence untouched.
+ *   L must not exceed the draft_len the verification ran with (later records
+ *   were not written).  `dtype` is the input (and window) dtype of the
+ *   verification; T, B and `delta` must be the ones it was called with.
+ *   The live slot must not have changed since the verification.
+ */
+kda_status kda_spec_commit_delta(const kda_layer *layer, const kda_cache *cache,
+                                 const int32_t *slot_idx, const void *delta,
+                                 size_t delta_bytes, const int32_t *accepted_len,
+                                 int32_t B, int32_t T, kda_dtype dtype,
+                                 void *hip_stream);
+
+/*
  * kda_chunk_prefill -- many tokens per sequence in chunks (the prefill path,
  * "vLLM Kimi K3 support", section "Fused kernels and metadata optimisation",
  * KDA prefill bullet).  Same result as running the tokens one by one; inside

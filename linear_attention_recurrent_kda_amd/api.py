@@ -234,6 +234,76 @@ def kda_spec_commit(layer: Layer, cache: Cache, slot_idx: torch.Tensor, snap_slo
         accepted_len.data_ptr(), B, T, wdt, _stream(stream)))
 
 
+def _dtype_code(dt) -> int:
+    if dt == torch.bfloat16:
+        return _lib.KDA_BF16
+    if dt == torch.float32:
+        return _lib.KDA_F32
+    raise TypeError(f"inputs must be float32 or bfloat16, not {dt}")
+
+
+def kda_spec_delta_bytes(layer: Layer, B: int, T: int, dtype=torch.bfloat16) -> int:
+    """Bytes of the replay-record buffer of B sequences x T draft tokens."""
+    L = layer.c_struct()
+    return int(_lib.load().kda_spec_delta_bytes(ctypes.byref(L), B, T, _dtype_code(dtype)))
+
+
+def new_spec_delta(layer: Layer, B: int, T: int, dtype=torch.bfloat16, device="cuda") -> torch.Tensor:
+    """An uninitialised record buffer, uint8 [B, T, H, record_bytes]."""
+    n = kda_spec_delta_bytes(layer, B, T, dtype)
+    if n == 0 and B > 0:
+        raise ValueError("invalid sizes for a record buffer")
+    rec = n // max(B * T * layer.H, 1)
+    return torch.empty((B, T, layer.H, rec), dtype=torch.uint8, device=device)
+
+
+def _delta_buf(delta: torch.Tensor, B: int):
+    _check(delta, "delta", torch.uint8)
+    if delta.dim() != 4 or delta.shape[0] != B:
+        raise ValueError("delta must be a [B, T, H, record_bytes] uint8 buffer (new_spec_delta)")
+    return delta.shape[1], delta.numel()
+
+
+def kda_spec_verify_delta(layer: Layer, cache: Cache, slot_idx: torch.Tensor, inputs: Inputs,
+                          y: torch.Tensor, delta: torch.Tensor, draft_len: Optional[torch.Tensor] = None,
+                          stream=None) -> None:
+    """Verification with replay records instead of snapshots: inputs
+    [B, T, H, .], y [B, T, H, d_v], delta from new_spec_delta(layer, B, T)."""
+    _check(slot_idx, "slot_idx", torch.int32)
+    B = slot_idx.numel()
+    T, nbytes = _delta_buf(delta, B)
+    _check(y, "y", torch.float32)
+    if tuple(y.shape) != (B, T, layer.H, layer.d_v):
+        raise ValueError("y must be [B, T, H, d_v]")
+    dl = None
+    if draft_len is not None:
+        _check(draft_len, "draft_len", torch.int32)
+        if draft_len.numel() != B:
+            raise ValueError("draft_len must be [B]")
+        dl = draft_len.data_ptr()
+    L, C, I = layer.c_struct(), cache.c_struct(layer), inputs.c_struct(layer, (B, T))
+    if cache.conv_state.dtype != inputs.dtype:
+        raise TypeError("conv_state dtype must equal the input dtype")
+    _raise("kda_spec_verify_delta", _lib.load().kda_spec_verify_delta(
+        ctypes.byref(L), ctypes.byref(C), slot_idx.data_ptr(), B, T, dl, ctypes.byref(I),
+        y.data_ptr(), delta.data_ptr(), nbytes, _stream(stream)))
+
+
+def kda_spec_commit_delta(layer: Layer, cache: Cache, slot_idx: torch.Tensor, delta: torch.Tensor,
+                          accepted_len: torch.Tensor, stream=None) -> None:
+    """Replay the first accepted_len[b] records of each sequence onto its live slot."""
+    _check(slot_idx, "slot_idx", torch.int32)
+    _check(accepted_len, "accepted_len", torch.int32)
+    B = slot_idx.numel()
+    if accepted_len.numel() != B:
+        raise ValueError("accepted_len must be [B]")
+    T, nbytes = _delta_buf(delta, B)
+    L, C = layer.c_struct(), cache.c_struct(layer)
+    _raise("kda_spec_commit_delta", _lib.load().kda_spec_commit_delta(
+        ctypes.byref(L), ctypes.byref(C), slot_idx.data_ptr(), delta.data_ptr(), nbytes,
+        accepted_len.data_ptr(), B, T, _dtype_code(cache.conv_state.dtype), _stream(stream)))
+
+
 def kda_chunk_prefill_workspace_bytes(layer: Layer, total_T: int, N_seq: int, chunk: int = 64) -> int:
     L = layer.c_struct()
     return int(_lib.load().kda_chunk_prefill_workspace_bytes(ctypes.byref(L), total_T, N_seq, chunk))

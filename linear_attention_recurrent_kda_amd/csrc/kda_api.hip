@@ -87,7 +87,7 @@ KDA_EXPORT kda_status kda_decode(const kda_layer *layer, const kda_cache *cache,
     p.slot_idx = slot_idx;
     p.B = B;
     p.T = 1;
-    return launch_recurrent(p, layer->d_k, layer->d_v, inputs->dtype, false,
+    return launch_recurrent(p, layer->d_k, layer->d_v, inputs->dtype, RecKind::decode,
                             static_cast<hipStream_t>(hip_stream));
 }
 
@@ -97,7 +97,7 @@ KDA_EXPORT kda_status kda_spec_verify(const kda_layer *layer, const kda_cache *c
                                       const kda_inputs *inputs, float *y, void *hip_stream) {
     KDA_TRY(check_layer(layer));
     KDA_TRY(check_cache(cache));
-    if (B < 0 || T < 1 || T > 16) return KDA_ERR_SHAPE;
+    if (B < 0 || T < 1 || T > kMaxDraft) return KDA_ERR_SHAPE;
     if (B == 0) return KDA_OK;
     KDA_TRY(check_inputs(inputs));
     if ((size_t)B * layer->H > 0x7fffffffu) return KDA_ERR_SHAPE;
@@ -111,7 +111,7 @@ KDA_EXPORT kda_status kda_spec_verify(const kda_layer *layer, const kda_cache *c
     p.draft_len = draft_len;
     p.B = B;
     p.T = T;
-    return launch_recurrent(p, layer->d_k, layer->d_v, inputs->dtype, true,
+    return launch_recurrent(p, layer->d_k, layer->d_v, inputs->dtype, RecKind::verify,
                             static_cast<hipStream_t>(hip_stream));
 }
 
@@ -122,7 +122,7 @@ KDA_EXPORT kda_status kda_spec_commit(const kda_layer *layer, const kda_cache *c
     KDA_TRY(check_layer(layer));
     KDA_TRY(check_cache(cache));
     if (window_dtype != KDA_F32 && window_dtype != KDA_BF16) return KDA_ERR_DTYPE;
-    if (B < 0 || T < 1 || T > 16) return KDA_ERR_SHAPE;
+    if (B < 0 || T < 1 || T > kMaxDraft) return KDA_ERR_SHAPE;
     if (B == 0) return KDA_OK;
     if ((size_t)B * layer->H > 0x7fffffffu) return KDA_ERR_SHAPE;
     if (!slot_idx || !snap_slots || !accepted_len) return KDA_ERR_NULL;
@@ -143,6 +143,67 @@ KDA_EXPORT kda_status kda_spec_commit(const kda_layer *layer, const kda_cache *c
     p.window_words = (int)((size_t)(layer->conv_w - 1) * (2 * layer->d_k + layer->d_v) *
                            elem_size(window_dtype) / 4);
     return launch_commit(p, static_cast<hipStream_t>(hip_stream));
+}
+
+KDA_EXPORT size_t kda_spec_delta_bytes(const kda_layer *layer, int32_t B, int32_t T, kda_dtype dtype) {
+    if (check_layer(layer) != KDA_OK || B < 0 || T < 1 || T > kMaxDraft) return 0;
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return 0;
+    return (size_t)B * T * layer->H * spec_delta_record_bytes(layer->d_k, layer->d_v, dtype);
+}
+
+KDA_EXPORT kda_status kda_spec_verify_delta(const kda_layer *layer, const kda_cache *cache,
+                                            const int32_t *slot_idx, int32_t B, int32_t T,
+                                            const int32_t *draft_len, const kda_inputs *inputs,
+                                            float *y, void *delta, size_t delta_bytes,
+                                            void *hip_stream) {
+    KDA_TRY(check_layer(layer));
+    KDA_TRY(check_cache(cache));
+    if (B < 0 || T < 1 || T > kMaxDraft) return KDA_ERR_SHAPE;
+    if (B == 0) return KDA_OK;
+    KDA_TRY(check_inputs(inputs));
+    if ((size_t)B * layer->H > 0x7fffffffu) return KDA_ERR_SHAPE;
+    if (!slot_idx || !y || !delta) return KDA_ERR_NULL;
+    if (!aligned(slot_idx, 4) || (draft_len && !aligned(draft_len, 4))) return KDA_ERR_ALIGN;
+    if (!aligned(y, 16) || !aligned(delta, 16)) return KDA_ERR_ALIGN;
+    if (delta_bytes < kda_spec_delta_bytes(layer, B, T, inputs->dtype)) return KDA_ERR_WORKSPACE;
+    RecParams p = rec_params(layer, cache, inputs, y);
+    p.slot_idx = slot_idx;
+    p.draft_len = draft_len;
+    p.delta = delta;
+    p.B = B;
+    p.T = T;
+    return launch_recurrent(p, layer->d_k, layer->d_v, inputs->dtype, RecKind::verify_delta,
+                            static_cast<hipStream_t>(hip_stream));
+}
+
+KDA_EXPORT kda_status kda_spec_commit_delta(const kda_layer *layer, const kda_cache *cache,
+                                            const int32_t *slot_idx, const void *delta,
+                                            size_t delta_bytes, const int32_t *accepted_len,
+                                            int32_t B, int32_t T, kda_dtype dtype,
+                                            void *hip_stream) {
+    KDA_TRY(check_layer(layer));
+    KDA_TRY(check_cache(cache));
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_DTYPE;
+    if (B < 0 || T < 1 || T > kMaxDraft) return KDA_ERR_SHAPE;
+    if (B == 0) return KDA_OK;
+    if ((size_t)B * layer->H > 0x7fffffffu) return KDA_ERR_SHAPE;
+    if (!slot_idx || !delta || !accepted_len) return KDA_ERR_NULL;
+    if (!aligned(slot_idx, 4) || !aligned(accepted_len, 4)) return KDA_ERR_ALIGN;
+    if (!aligned(delta, 16)) return KDA_ERR_ALIGN;
+    if (delta_bytes < kda_spec_delta_bytes(layer, B, T, dtype)) return KDA_ERR_WORKSPACE;
+    CommitDeltaParams p{};
+    p.state = cache->state;
+    p.window = cache->conv_state;
+    p.n_slots = cache->n_slots;
+    p.err_flag = cache->err_flag;
+    p.stream_state = (layer->flags & KDA_STREAM_STATE) ? 1 : 0;
+    p.slot_idx = slot_idx;
+    p.accepted_len = accepted_len;
+    p.delta = delta;
+    p.B = B;
+    p.H = layer->H;
+    p.T = T;
+    return launch_commit_delta(p, layer->d_k, layer->d_v, dtype, static_cast<hipStream_t>(hip_stream));
 }
 
 KDA_EXPORT size_t kda_chunk_prefill_workspace_bytes(const kda_layer *layer, int32_t total_T,

@@ -26,6 +26,7 @@ struct RecParams {
     const int32_t *slot_idx;    // [B]
     const int32_t *snap_slots;  // [B, T] (verify)
     const int32_t *draft_len;   // [B] or null (verify)
+    void *delta;                // replay records (verify, delta mode)
     // inputs, rows n = b (decode) or b*T + t (verify)
     const void *x_q, *x_k, *x_v, *g, *b, *z;
     float *y;
@@ -41,6 +42,18 @@ struct CommitParams {
     int B, H, T;
     int state_elems;   // d_k * d_v
     int window_words;  // (conv_w - 1) * C_h * sizeof(input) / 4
+};
+
+// Delta commit: replay accepted records onto the live slots.
+struct CommitDeltaParams {
+    float *state;
+    void *window;
+    int n_slots;
+    int32_t *err_flag;
+    int stream_state;
+    const int32_t *slot_idx, *accepted_len;
+    const void *delta;          // records of kda_spec_verify_delta
+    int B, H, T;
 };
 
 struct PrefillParams {
@@ -61,9 +74,18 @@ struct PrefillParams {
     size_t workspace_bytes;
 };
 
-kda_status launch_recurrent(const RecParams &p, int d_k, int d_v, kda_dtype dt, bool verify,
+// most draft tokens per verification
+constexpr int kMaxDraft = 16;
+
+enum class RecKind { decode, verify, verify_delta };
+
+kda_status launch_recurrent(const RecParams &p, int d_k, int d_v, kda_dtype dt, RecKind kind,
                             hipStream_t stream);
 kda_status launch_commit(const CommitParams &p, hipStream_t stream);
+kda_status launch_commit_delta(const CommitDeltaParams &p, int d_k, int d_v, kda_dtype dt,
+                               hipStream_t stream);
+// bytes of one (sequence, token, head) replay record
+size_t spec_delta_record_bytes(int d_k, int d_v, kda_dtype dt);
 kda_status launch_prefill(const PrefillParams &p, int d_k, int d_v, kda_dtype dt,
                           hipStream_t stream);
 size_t prefill_workspace_bytes(int H, int d_k, int d_v, int total_T, int N_seq, int chunk);

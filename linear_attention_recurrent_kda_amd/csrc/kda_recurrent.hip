@@ -17,7 +17,10 @@
 //     d  = beta (v - u),   S = S' + k^ d^T,  o = p + (k^.q^) d  (= S^T q^)
 //     y  = o / sqrt(mean(o^2) + eps_r) * w * sigmoid(z)
 // Decode and verify instantiate the same code, so verify + commit(L) equals
-// L decode launches bit for bit.
+// L decode launches bit for bit.  Verify keeps either a full state snapshot
+// per token, or (delta mode) the token's replay record (alpha, k^, d and the
+// raw conv inputs); the delta commit re-applies S = diag(alpha) S + k^ d^T
+// with the same fp32 operations, so it reaches the same bits.
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -68,6 +71,31 @@ struct TokenLds {
     float kq;         // k^ . q^
 };
 
+// Replay record of one (sequence, token, head) in delta mode, at byte offset
+// ((b*T + t)*H + h) * rec_bytes of the record buffer:
+//   float alpha[DK]; float khat[DK]; float d[DV]; Tin x[2*DK + DV]
+// (x = the raw, pre-conv inputs q|k|v of the token: the conv window of a
+// later commit is rebuilt from them).
+template <int DK, int DV, typename Tin>
+struct DeltaRec {
+    static constexpr int CH = 2 * DK + DV;
+    static constexpr int kFloats = 2 * DK + DV;
+    static constexpr size_t kBytes = (size_t)CH * (4 + sizeof(Tin));
+    static_assert(kBytes % 16 == 0, "records must stay 16-byte aligned");
+    __device__ static float *f(void *base, size_t rec) {
+        return reinterpret_cast<float *>(static_cast<char *>(base) + rec * kBytes);
+    }
+    __device__ static const float *f(const void *base, size_t rec) {
+        return reinterpret_cast<const float *>(static_cast<const char *>(base) + rec * kBytes);
+    }
+    __device__ static Tin *x(void *base, size_t rec) {
+        return reinterpret_cast<Tin *>(f(base, rec) + kFloats);
+    }
+    __device__ static const Tin *x(const void *base, size_t rec) {
+        return reinterpret_cast<const Tin *>(f(base, rec) + kFloats);
+    }
+};
+
 // Raw operands of the conv for the channels one lane owns (c = tid + NT*k):
 // the tap weights, the three window entries and the T new inputs.
 template <int DK, int DV, int NT, typename Tin, int TMAX>
@@ -109,8 +137,9 @@ __device__ __forceinline__ void conv_fetch(const RecParams &p, int tid, int b, i
 
 // Conv (+ activation) of the owned channels for every token into LDS; the
 // window rows after each token go to the live slot (decode) or to the
-// token's snapshot slot (verify).
-template <int DK, int DV, int NT, typename Tin, int TMAX, bool VERIFY>
+// token's snapshot slot (verify); delta mode keeps the raw inputs in the
+// token's record instead.
+template <int DK, int DV, int NT, typename Tin, int TMAX, bool VERIFY, bool DELTA>
 __device__ __forceinline__ void conv_compute(const RecParams &p, int tid, int b, int h, int slot, int T,
                                              const ConvRegs<DK, DV, NT, Tin, TMAX> &cr,
                                              TokenLds<DK, DV> *tok) {
@@ -131,7 +160,9 @@ __device__ __forceinline__ void conv_compute(const RecParams &p, int tid, int b,
             acc = fmaf(w.z, to_f32(cr.x[k][t + 2]), acc);
             acc = fmaf(w.w, to_f32(cr.x[k][t + 3]), acc);
             tok[t].conv[cs] = p.silu ? acc * sigmoid(acc) : acc;
-            if (VERIFY && own) {
+            if (DELTA && own) {
+                DeltaRec<DK, DV, Tin>::x(p.delta, ((size_t)b * p.T + t) * p.H + h)[c] = cr.x[k][t + 3];
+            } else if (VERIFY && own) {
                 const int ss = p.snap_slots[(size_t)b * p.T + t];
                 if (ss >= 0 && ss < p.n_slots) {
                     Tin *sw = static_cast<Tin *>(p.window) + ((size_t)ss * p.H + h) * 3 * CH;
@@ -220,9 +251,13 @@ __device__ __forceinline__ void prep_token(const RecParams &p, int lane, int j,
     }
 }
 
-template <int DK, int DV, int NT, typename Tin, int TMAX, bool VERIFY, bool STREAM>
+enum RecMode { kDecode = 0, kVerify = 1, kVerifyDelta = 2 };
+
+template <int DK, int DV, int NT, typename Tin, int TMAX, int MODE, bool STREAM>
 __global__ __launch_bounds__(NT) void kda_recurrent_kernel(RecParams p) {
     using G = RecGeo<DK, DV, NT>;
+    constexpr bool VERIFY = MODE != kDecode;
+    constexpr bool DELTA = MODE == kVerifyDelta;
     __shared__ TokenLds<DK, DV> tok[TMAX];
     __shared__ float4 red[G::NW][2][G::CG];
 
@@ -256,7 +291,7 @@ __global__ __launch_bounds__(NT) void kda_recurrent_kernel(RecParams p) {
     for (int i = 0; i < G::RPT; ++i) s[i] = load_state4<STREAM>(S + (size_t)(rg + G::RG * i) * DV + 4 * cg);
 
     // 2. conv (+ window update / window snapshots)
-    conv_compute<DK, DV, NT, Tin, TMAX, VERIFY>(p, tid, b, h, slot, T, cr, tok);
+    conv_compute<DK, DV, NT, Tin, TMAX, VERIFY, DELTA>(p, tid, b, h, slot, T, cr, tok);
     __syncthreads();
     // 3. norms and gates, one wave per token
 #pragma unroll
@@ -265,6 +300,14 @@ __global__ __launch_bounds__(NT) void kda_recurrent_kernel(RecParams p) {
         if (t < T) prep_token<DK, DV, Tin, TPW>(p, lane, j, pr, tok[t]);
     }
     __syncthreads();
+    // delta mode: alpha and k^ of every token into its record
+    if (DELTA) {
+        for (int i = tid; i < T * 2 * DK; i += NT) {
+            const int t = i / (2 * DK), e = i % (2 * DK);
+            DeltaRec<DK, DV, Tin>::f(p.delta, ((size_t)b * p.T + t) * p.H + h)[e] =
+                e < DK ? tok[t].alpha[e] : tok[t].conv[e];
+        }
+    }
 
     // 4. the recurrence, tokens in order, state in registers
     for (int t = 0; t < T; ++t) {
@@ -301,7 +344,11 @@ __global__ __launch_bounds__(NT) void kda_recurrent_kernel(RecParams p) {
 #pragma unroll
         for (int i = 0; i < G::RPT; ++i) s[i] = fma4(tk.conv[DK + rg + G::RG * i], d, s[i]);
 
-        if (VERIFY) {
+        if (DELTA) {
+            if (tid < G::CG)
+                *reinterpret_cast<float4 *>(DeltaRec<DK, DV, Tin>::f(p.delta, ((size_t)b * p.T + t) * p.H + h) +
+                                            2 * DK + 4 * cg) = d;
+        } else if (VERIFY) {
             const int ss = p.snap_slots[(size_t)b * p.T + t];
             if (ss >= 0 && ss < p.n_slots) {
                 float *D = p.state + ((size_t)ss * p.H + h) * DK * DV;
@@ -357,6 +404,69 @@ __global__ __launch_bounds__(256) void kda_commit_kernel(CommitParams p) {
     for (int i = threadIdx.x; i < p.window_words; i += blockDim.x) dw[i] = sw[i];
 }
 
+// Delta commit: replay the first L = accepted_len[b] records of sequence b
+// onto its live state, S <- diag(alpha_t) S + k^_t d_t^T for t < L (the same
+// two fp32 roundings per element as the verify and decode kernels), and
+// rebuild the conv window as rows L, L+1, L+2 of [window rows 0..2, x_1..x_T].
+// One workgroup per (sequence, head), the decode kernel's tile geometry.
+template <int DK, int DV, int NT, typename Tin, bool STREAM>
+__global__ __launch_bounds__(NT) void kda_commit_delta_kernel(CommitDeltaParams p) {
+    using G = RecGeo<DK, DV, NT>;
+    using R = DeltaRec<DK, DV, Tin>;
+    constexpr int CH = 2 * DK + DV;
+    constexpr int NF = R::kFloats;
+    __shared__ float rec[kMaxDraft][NF];
+
+    const int tid = threadIdx.x;
+    const int cg = tid % G::CG, rg = tid / G::CG;
+    const int b = blockIdx.x / p.H, h = blockIdx.x % p.H;
+    const int L = p.accepted_len[b];
+    const int dst = p.slot_idx[b];
+    if (L == 0 || dst == -1) return;
+    if (L < 0 || L > p.T || dst < 0 || dst >= p.n_slots) {
+        if (tid == 0) flag_error(p.err_flag);
+        return;
+    }
+    float *S = p.state + ((size_t)dst * p.H + h) * DK * DV;
+    float4 s[G::RPT];
+#pragma unroll
+    for (int i = 0; i < G::RPT; ++i) s[i] = load_state4<STREAM>(S + (size_t)(rg + G::RG * i) * DV + 4 * cg);
+
+    // the float part of the L records into LDS (16-byte loads)
+    for (int i = tid; i < L * (NF / 4); i += NT) {
+        const int t = i / (NF / 4), e = 4 * (i % (NF / 4));
+        const float4 v = *reinterpret_cast<const float4 *>(R::f(p.delta, ((size_t)b * p.T + t) * p.H + h) + e);
+        rec[t][e] = v.x; rec[t][e + 1] = v.y; rec[t][e + 2] = v.z; rec[t][e + 3] = v.w;
+    }
+    // conv window: per channel, read the three source rows, then write
+    Tin *win = static_cast<Tin *>(p.window) + ((size_t)dst * p.H + h) * 3 * CH;
+    for (int c = tid; c < CH; c += NT) {
+        Tin x[3];
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            const int r = L + j;   // row of [w0, w1, w2, x_1 .. x_T]
+            x[j] = r < 3 ? win[r * CH + c] : R::x(p.delta, ((size_t)b * p.T + (r - 3)) * p.H + h)[c];
+        }
+#pragma unroll
+        for (int j = 0; j < 3; ++j) win[j * CH + c] = x[j];
+    }
+    __syncthreads();
+
+    for (int t = 0; t < L; ++t) {
+        const float *a = rec[t];
+        const float4 d = make_float4(a[2 * DK + 4 * cg], a[2 * DK + 4 * cg + 1],
+                                     a[2 * DK + 4 * cg + 2], a[2 * DK + 4 * cg + 3]);
+#pragma unroll
+        for (int i = 0; i < G::RPT; ++i) {
+            const int r = rg + G::RG * i;
+            s[i] = s[i] * a[r];
+            s[i] = fma4(a[DK + r], d, s[i]);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < G::RPT; ++i) store_state4<STREAM>(S + (size_t)(rg + G::RG * i) * DV + 4 * cg, s[i]);
+}
+
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
@@ -365,38 +475,47 @@ __global__ __launch_bounds__(256) void kda_commit_kernel(CommitParams p) {
 #endif
 constexpr int kRecThreads = KDA_REC_THREADS;   // lanes per (sequence, head) workgroup
 
-template <int DK, int DV, typename Tin, bool STREAM>
-static kda_status launch_rec_typed(const RecParams &p, bool verify, hipStream_t stream) {
+template <int DK, int DV, typename Tin, bool STREAM, int MODE>
+static void launch_rec_mode(const RecParams &p, hipStream_t stream) {
     const dim3 grid((unsigned)(p.B * p.H)), block(kRecThreads);
-    if (!verify) {
-        hipLaunchKernelGGL((kda_recurrent_kernel<DK, DV, kRecThreads, Tin, 1, false, STREAM>), grid, block,
+    if (MODE == kDecode) {
+        hipLaunchKernelGGL((kda_recurrent_kernel<DK, DV, kRecThreads, Tin, 1, kDecode, STREAM>), grid, block,
                            0, stream, p);
     } else if (p.T <= 8) {
-        hipLaunchKernelGGL((kda_recurrent_kernel<DK, DV, kRecThreads, Tin, 8, true, STREAM>), grid, block,
+        hipLaunchKernelGGL((kda_recurrent_kernel<DK, DV, kRecThreads, Tin, 8, MODE, STREAM>), grid, block,
                            0, stream, p);
     } else {
-        hipLaunchKernelGGL((kda_recurrent_kernel<DK, DV, kRecThreads, Tin, 16, true, STREAM>), grid, block,
-                           0, stream, p);
+        hipLaunchKernelGGL((kda_recurrent_kernel<DK, DV, kRecThreads, Tin, kMaxDraft, MODE, STREAM>), grid,
+                           block, 0, stream, p);
+    }
+}
+
+template <int DK, int DV, typename Tin, bool STREAM>
+static kda_status launch_rec_typed(const RecParams &p, RecKind kind, hipStream_t stream) {
+    switch (kind) {
+        case RecKind::decode: launch_rec_mode<DK, DV, Tin, STREAM, kDecode>(p, stream); break;
+        case RecKind::verify: launch_rec_mode<DK, DV, Tin, STREAM, kVerify>(p, stream); break;
+        case RecKind::verify_delta: launch_rec_mode<DK, DV, Tin, STREAM, kVerifyDelta>(p, stream); break;
     }
     return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
 template <int DK, int DV>
-static kda_status launch_rec_dt(const RecParams &p, kda_dtype dt, bool verify, hipStream_t s) {
+static kda_status launch_rec_dt(const RecParams &p, kda_dtype dt, RecKind kind, hipStream_t s) {
     if (p.stream_state)
-        return dt == KDA_BF16 ? launch_rec_typed<DK, DV, uint16_t, true>(p, verify, s)
-                              : launch_rec_typed<DK, DV, float, true>(p, verify, s);
-    return dt == KDA_BF16 ? launch_rec_typed<DK, DV, uint16_t, false>(p, verify, s)
-                          : launch_rec_typed<DK, DV, float, false>(p, verify, s);
+        return dt == KDA_BF16 ? launch_rec_typed<DK, DV, uint16_t, true>(p, kind, s)
+                              : launch_rec_typed<DK, DV, float, true>(p, kind, s);
+    return dt == KDA_BF16 ? launch_rec_typed<DK, DV, uint16_t, false>(p, kind, s)
+                          : launch_rec_typed<DK, DV, float, false>(p, kind, s);
 }
 
-kda_status launch_recurrent(const RecParams &p, int d_k, int d_v, kda_dtype dt, bool verify,
+kda_status launch_recurrent(const RecParams &p, int d_k, int d_v, kda_dtype dt, RecKind kind,
                             hipStream_t stream) {
     if (p.B == 0) return KDA_OK;
-    if (d_k == 128 && d_v == 128) return launch_rec_dt<128, 128>(p, dt, verify, stream);
-    if (d_k == 64 && d_v == 64) return launch_rec_dt<64, 64>(p, dt, verify, stream);
-    if (d_k == 128 && d_v == 64) return launch_rec_dt<128, 64>(p, dt, verify, stream);
-    if (d_k == 64 && d_v == 128) return launch_rec_dt<64, 128>(p, dt, verify, stream);
+    if (d_k == 128 && d_v == 128) return launch_rec_dt<128, 128>(p, dt, kind, stream);
+    if (d_k == 64 && d_v == 64) return launch_rec_dt<64, 64>(p, dt, kind, stream);
+    if (d_k == 128 && d_v == 64) return launch_rec_dt<128, 64>(p, dt, kind, stream);
+    if (d_k == 64 && d_v == 128) return launch_rec_dt<64, 128>(p, dt, kind, stream);
     return KDA_ERR_UNSUPPORTED;
 }
 
@@ -404,6 +523,37 @@ kda_status launch_commit(const CommitParams &p, hipStream_t stream) {
     if (p.B == 0) return KDA_OK;
     hipLaunchKernelGGL(kda_commit_kernel, dim3((unsigned)(p.B * p.H)), dim3(256), 0, stream, p);
     return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+template <int DK, int DV>
+static void launch_commit_delta_shape(const CommitDeltaParams &p, kda_dtype dt, hipStream_t s) {
+    const dim3 grid((unsigned)(p.B * p.H)), block(kRecThreads);
+    if (p.stream_state) {
+        if (dt == KDA_BF16)
+            hipLaunchKernelGGL((kda_commit_delta_kernel<DK, DV, kRecThreads, uint16_t, true>), grid, block, 0, s, p);
+        else
+            hipLaunchKernelGGL((kda_commit_delta_kernel<DK, DV, kRecThreads, float, true>), grid, block, 0, s, p);
+    } else {
+        if (dt == KDA_BF16)
+            hipLaunchKernelGGL((kda_commit_delta_kernel<DK, DV, kRecThreads, uint16_t, false>), grid, block, 0, s, p);
+        else
+            hipLaunchKernelGGL((kda_commit_delta_kernel<DK, DV, kRecThreads, float, false>), grid, block, 0, s, p);
+    }
+}
+
+kda_status launch_commit_delta(const CommitDeltaParams &p, int d_k, int d_v, kda_dtype dt,
+                               hipStream_t stream) {
+    if (p.B == 0) return KDA_OK;
+    if (d_k == 128 && d_v == 128) launch_commit_delta_shape<128, 128>(p, dt, stream);
+    else if (d_k == 64 && d_v == 64) launch_commit_delta_shape<64, 64>(p, dt, stream);
+    else if (d_k == 128 && d_v == 64) launch_commit_delta_shape<128, 64>(p, dt, stream);
+    else if (d_k == 64 && d_v == 128) launch_commit_delta_shape<64, 128>(p, dt, stream);
+    else return KDA_ERR_UNSUPPORTED;
+    return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+size_t spec_delta_record_bytes(int d_k, int d_v, kda_dtype dt) {
+    return (size_t)(2 * d_k + d_v) * (4 + (dt == KDA_BF16 ? 2 : 4));
 }
 
 }  // namespace kda

@@ -129,6 +129,34 @@ def test_spec_validation(lib):
     assert c(0, 8) == 0
 
 
+def test_spec_delta_validation(lib):
+    L, C, I = good_layer(), good_cache(), good_inputs()
+    rec = (2 * L.d_k + L.d_v) * (4 + 2)      # bf16 inputs: fp32 alpha, k^, d + raw q|k|v
+    assert lib.kda_spec_delta_bytes(ctypes.byref(L), 3, 8, _lib.KDA_BF16) == 3 * 8 * L.H * rec
+    assert lib.kda_spec_delta_bytes(ctypes.byref(L), 3, 8, _lib.KDA_F32) == 3 * 8 * L.H * (2 * L.d_k + L.d_v) * 8
+    assert lib.kda_spec_delta_bytes(ctypes.byref(L), 3, 17, _lib.KDA_BF16) == 0
+    assert lib.kda_spec_delta_bytes(ctypes.byref(L), 3, 8, 9) == 0
+    need = lib.kda_spec_delta_bytes(ctypes.byref(L), 2, 8, _lib.KDA_BF16)
+    v = lambda B, T, d=FAKE, nb=need, dl=None: lib.kda_spec_verify_delta(
+        ctypes.byref(L), ctypes.byref(C), FAKE, B, T, dl, ctypes.byref(I), FAKE, d, nb, None)
+    assert v(2, 0) == 2
+    assert v(2, 17) == 2
+    assert v(2, 8, d=None) == 1
+    assert v(2, 8, d=FAKE + 4) == 4
+    assert v(2, 8, nb=need - 1) == 6
+    assert v(2, 8, dl=FAKE + 2) == 4
+    assert v(0, 8, d=None) == 0
+    c = lambda B, T, d=FAKE, nb=need, acc=FAKE, wd=_lib.KDA_BF16: lib.kda_spec_commit_delta(
+        ctypes.byref(L), ctypes.byref(C), FAKE, d, nb, acc, B, T, wd, None)
+    assert c(2, 8, wd=5) == 3
+    assert c(2, 20) == 2
+    assert c(2, 8, acc=None) == 1
+    assert c(2, 8, d=None) == 1
+    assert c(2, 8, nb=need - 1) == 6
+    assert c(2, 8, acc=FAKE + 2) == 4
+    assert c(0, 8) == 0
+
+
 def test_prefill_validation(lib):
     L, C, I = good_layer(), good_cache(), good_inputs()
     p = lambda chunk=64, n=1, T=128, ws=FAKE, wb=1 << 30, cu=FAKE: lib.kda_chunk_prefill(
