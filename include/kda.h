@@ -235,6 +235,35 @@ kda_status kda_chunk_prefill(const kda_layer *layer, const kda_cache *cache,
                              void *workspace, size_t workspace_bytes,
                              void *hip_stream);
 
+/*
+ * kda_chunk_prefill_ckpt -- kda_chunk_prefill that also keeps interval
+ * checkpoints of each sequence's state.  The interval-based retention of
+ * "vLLM Kimi K3 support" (section "Agentic cache retention policies")
+ * checkpoints the KDA state at a fixed token interval (32K tokens is its
+ * example) and at prompt boundaries; the prompt-boundary state is the final
+ * state this call leaves in the live slot, and this call adds the interval
+ * ones (read here as: a later request that shares the first (j+1)*interval
+ * tokens can start from checkpoint j).
+ *   ckpt_interval: tokens between checkpoints, a positive multiple of chunk.
+ *   ckpt_slots [N_seq, ckpt_per_seq] int32 (device): after the first
+ *     (j+1)*ckpt_interval tokens of sequence s, its state and conv window are
+ *     written to slot ckpt_slots[s*ckpt_per_seq + j] (-1: not kept), for
+ *     j < min(ckpt_per_seq, len_s / ckpt_interval).  Other indices outside
+ *     [0, n_slots) set err_flag and are skipped.  Checkpoint slots must not
+ *     alias each other or any live slot of the call.
+ * Everything else (outputs, final state, errors) is exactly kda_chunk_prefill;
+ * a checkpoint equals the state a prefill of that many tokens would leave.
+ * Errors: KDA_ERR_NULL for a NULL ckpt_slots, KDA_ERR_SHAPE for ckpt_per_seq
+ * < 1 or an interval that is not a positive multiple of chunk.
+ */
+kda_status kda_chunk_prefill_ckpt(const kda_layer *layer, const kda_cache *cache,
+                                  const int32_t *slot_idx, const int32_t *cu_seqlens,
+                                  int32_t N_seq, int32_t total_T, int32_t chunk,
+                                  const kda_inputs *inputs, float *y,
+                                  const int32_t *ckpt_slots, int32_t ckpt_interval,
+                                  int32_t ckpt_per_seq, void *workspace,
+                                  size_t workspace_bytes, void *hip_stream);
+
 /* Bytes of device workspace kda_chunk_prefill needs (0 on invalid sizes). */
 size_t kda_chunk_prefill_workspace_bytes(const kda_layer *layer, int32_t total_T,
                                          int32_t N_seq, int32_t chunk);

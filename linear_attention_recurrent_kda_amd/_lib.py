@@ -21,7 +21,7 @@ STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE"
 
 # every function include/kda.h declares
 EXPORTS = ("kda_decode", "kda_spec_verify", "kda_spec_commit", "kda_spec_delta_bytes",
-           "kda_spec_verify_delta", "kda_spec_commit_delta", "kda_chunk_prefill",
+           "kda_spec_verify_delta", "kda_spec_commit_delta", "kda_chunk_prefill", "kda_chunk_prefill_ckpt",
            "kda_chunk_prefill_workspace_bytes", "kda_copy_probe", "kda_status_string",
            "kda_abi_version")
 
@@ -83,6 +83,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_chunk_prefill.argtypes = [ctypes.POINTER(KdaLayer), ctypes.POINTER(KdaCache), P, P,
                                       i32, i32, i32, ctypes.POINTER(KdaInputs), P, P,
                                       ctypes.c_size_t, P]
+    lib.kda_chunk_prefill_ckpt.restype = ctypes.c_int
+    lib.kda_chunk_prefill_ckpt.argtypes = [ctypes.POINTER(KdaLayer), ctypes.POINTER(KdaCache), P, P,
+                                           i32, i32, i32, ctypes.POINTER(KdaInputs), P, P, i32, i32, P,
+                                           ctypes.c_size_t, P]
     lib.kda_chunk_prefill_workspace_bytes.restype = ctypes.c_size_t
     lib.kda_chunk_prefill_workspace_bytes.argtypes = [ctypes.POINTER(KdaLayer), i32, i32, i32]
     lib.kda_copy_probe.restype = ctypes.c_int

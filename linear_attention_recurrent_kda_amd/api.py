@@ -309,13 +309,7 @@ def kda_chunk_prefill_workspace_bytes(layer: Layer, total_T: int, N_seq: int, ch
     return int(_lib.load().kda_chunk_prefill_workspace_bytes(ctypes.byref(L), total_T, N_seq, chunk))
 
 
-def kda_chunk_prefill(layer: Layer, cache: Cache, slot_idx: torch.Tensor, cu_seqlens: torch.Tensor,
-                      inputs: Inputs, y: torch.Tensor, workspace: Optional[torch.Tensor] = None,
-                      chunk: int = 64, stream=None) -> None:
-    """Chunked prefill of N_seq sequences packed along the token axis:
-    slot_idx [N_seq], cu_seqlens [N_seq + 1] int32, inputs [total_T, H, .],
-    y [total_T, H, d_v].  A workspace of the size query's bytes is allocated
-    here (torch) when none is given."""
+def _prefill_args(layer, cache, slot_idx, cu_seqlens, inputs, y, workspace, chunk):
     _check(slot_idx, "slot_idx", torch.int32)
     _check(cu_seqlens, "cu_seqlens", torch.int32)
     N = slot_idx.numel()
@@ -332,9 +326,38 @@ def kda_chunk_prefill(layer: Layer, cache: Cache, slot_idx: torch.Tensor, cu_seq
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=y.device)
     wp, wb = (None, 0) if workspace is None else (workspace.data_ptr(), workspace.numel() * workspace.element_size())
+    return L, C, I, N, total_T, wp, wb, workspace
+
+
+def kda_chunk_prefill(layer: Layer, cache: Cache, slot_idx: torch.Tensor, cu_seqlens: torch.Tensor,
+                      inputs: Inputs, y: torch.Tensor, workspace: Optional[torch.Tensor] = None,
+                      chunk: int = 64, stream=None) -> None:
+    """Chunked prefill of N_seq sequences packed along the token axis:
+    slot_idx [N_seq], cu_seqlens [N_seq + 1] int32, inputs [total_T, H, .],
+    y [total_T, H, d_v].  A workspace of the size query's bytes is allocated
+    here (torch) when none is given."""
+    L, C, I, N, total_T, wp, wb, keep = _prefill_args(layer, cache, slot_idx, cu_seqlens, inputs, y,
+                                                      workspace, chunk)
     _raise("kda_chunk_prefill", _lib.load().kda_chunk_prefill(
         ctypes.byref(L), ctypes.byref(C), slot_idx.data_ptr(), cu_seqlens.data_ptr(), N, total_T,
         chunk, ctypes.byref(I), y.data_ptr(), wp, wb, _stream(stream)))
+
+
+def kda_chunk_prefill_ckpt(layer: Layer, cache: Cache, slot_idx: torch.Tensor, cu_seqlens: torch.Tensor,
+                           inputs: Inputs, y: torch.Tensor, ckpt_slots: torch.Tensor, ckpt_interval: int,
+                           workspace: Optional[torch.Tensor] = None, chunk: int = 64, stream=None) -> None:
+    """kda_chunk_prefill plus interval checkpoints: ckpt_slots [N_seq, per_seq]
+    int32; the state and window after (j+1)*ckpt_interval tokens of sequence
+    s go to ckpt_slots[s, j] (-1: not kept)."""
+    _check(ckpt_slots, "ckpt_slots", torch.int32)
+    if ckpt_slots.dim() != 2 or ckpt_slots.shape[0] != slot_idx.numel():
+        raise ValueError("ckpt_slots must be [N_seq, per_seq]")
+    L, C, I, N, total_T, wp, wb, keep = _prefill_args(layer, cache, slot_idx, cu_seqlens, inputs, y,
+                                                      workspace, chunk)
+    _raise("kda_chunk_prefill_ckpt", _lib.load().kda_chunk_prefill_ckpt(
+        ctypes.byref(L), ctypes.byref(C), slot_idx.data_ptr(), cu_seqlens.data_ptr(), N, total_T,
+        chunk, ctypes.byref(I), y.data_ptr(), ckpt_slots.data_ptr(), int(ckpt_interval),
+        int(ckpt_slots.shape[1]), wp, wb, _stream(stream)))
 
 
 def kda_copy_probe(dst: torch.Tensor, src: torch.Tensor, stream=None) -> None:

@@ -212,11 +212,13 @@ KDA_EXPORT size_t kda_chunk_prefill_workspace_bytes(const kda_layer *layer, int3
     return prefill_workspace_bytes(layer->H, layer->d_k, layer->d_v, total_T, N_seq, chunk);
 }
 
-KDA_EXPORT kda_status kda_chunk_prefill(const kda_layer *layer, const kda_cache *cache,
-                                        const int32_t *slot_idx, const int32_t *cu_seqlens,
-                                        int32_t N_seq, int32_t total_T, int32_t chunk,
-                                        const kda_inputs *inputs, float *y, void *workspace,
-                                        size_t workspace_bytes, void *hip_stream) {
+namespace {
+
+kda_status prefill_common(const kda_layer *layer, const kda_cache *cache, const int32_t *slot_idx,
+                          const int32_t *cu_seqlens, int32_t N_seq, int32_t total_T, int32_t chunk,
+                          const kda_inputs *inputs, float *y, const int32_t *ckpt_slots,
+                          int32_t ckpt_interval, int32_t ckpt_per_seq, void *workspace,
+                          size_t workspace_bytes, void *hip_stream) {
     KDA_TRY(check_layer(layer));
     KDA_TRY(check_cache(cache));
     if (N_seq < 1 || total_T < 0 || chunk <= 0) return KDA_ERR_SHAPE;
@@ -248,8 +250,38 @@ KDA_EXPORT kda_status kda_chunk_prefill(const kda_layer *layer, const kda_cache 
     p.y = y;
     p.workspace = workspace;
     p.workspace_bytes = workspace_bytes;
+    p.ckpt_slots = ckpt_slots;
+    p.ckpt_interval = ckpt_interval;
+    p.ckpt_per_seq = ckpt_per_seq;
     return launch_prefill(p, layer->d_k, layer->d_v, inputs->dtype,
                           static_cast<hipStream_t>(hip_stream));
+}
+
+}  // namespace
+
+KDA_EXPORT kda_status kda_chunk_prefill(const kda_layer *layer, const kda_cache *cache,
+                                        const int32_t *slot_idx, const int32_t *cu_seqlens,
+                                        int32_t N_seq, int32_t total_T, int32_t chunk,
+                                        const kda_inputs *inputs, float *y, void *workspace,
+                                        size_t workspace_bytes, void *hip_stream) {
+    return prefill_common(layer, cache, slot_idx, cu_seqlens, N_seq, total_T, chunk, inputs, y,
+                          nullptr, 0, 0, workspace, workspace_bytes, hip_stream);
+}
+
+KDA_EXPORT kda_status kda_chunk_prefill_ckpt(const kda_layer *layer, const kda_cache *cache,
+                                             const int32_t *slot_idx, const int32_t *cu_seqlens,
+                                             int32_t N_seq, int32_t total_T, int32_t chunk,
+                                             const kda_inputs *inputs, float *y,
+                                             const int32_t *ckpt_slots, int32_t ckpt_interval,
+                                             int32_t ckpt_per_seq, void *workspace,
+                                             size_t workspace_bytes, void *hip_stream) {
+    if (!ckpt_slots) return KDA_ERR_NULL;
+    if (!aligned(ckpt_slots, 4)) return KDA_ERR_ALIGN;
+    if (ckpt_per_seq < 1 || ckpt_interval < chunk || chunk <= 0 || ckpt_interval % chunk != 0)
+        return KDA_ERR_SHAPE;
+    return prefill_common(layer, cache, slot_idx, cu_seqlens, N_seq, total_T, chunk, inputs, y,
+                          ckpt_slots, ckpt_interval, ckpt_per_seq, workspace, workspace_bytes,
+                          hip_stream);
 }
 
 KDA_EXPORT kda_status kda_copy_probe(float *dst, const float *src, size_t n, void *hip_stream) {

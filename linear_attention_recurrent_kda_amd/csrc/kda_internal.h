@@ -72,6 +72,10 @@ struct PrefillParams {
     float *y;
     void *workspace;
     size_t workspace_bytes;
+    // interval checkpoints: state and window after every ckpt_interval tokens
+    // of sequence s go to ckpt_slots[s * ckpt_per_seq + j] (null: none)
+    const int32_t *ckpt_slots;
+    int ckpt_interval, ckpt_per_seq;
 };
 
 // most draft tokens per verification

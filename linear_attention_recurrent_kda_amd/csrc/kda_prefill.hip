@@ -731,6 +731,23 @@ __global__ __launch_bounds__(kScanThreads) void kda_prefill_scan_kernel(PrefillP
         if (ch < CH) {
 #pragma unroll
             for (int j = 0; j < 3; ++j) win[j * CH + ch] = nv[j];
+            // checkpoint windows: the three raw inputs before each checkpoint
+            // position (every position is >= 64, so all rows are inputs)
+            const int nck = p.ckpt_slots ? min(p.ckpt_per_seq, len / p.ckpt_interval) : 0;
+            for (int j = 0; j < nck; ++j) {
+                const int ck = p.ckpt_slots[(size_t)s * p.ckpt_per_seq + j];
+                if (!slot_ok(ck, p.n_slots)) continue;
+                const Tin *src;
+                int stride, off;
+                if (ch < DK) { src = static_cast<const Tin *>(p.x_q); stride = DK; off = ch; }
+                else if (ch < 2 * DK) { src = static_cast<const Tin *>(p.x_k); stride = DK; off = ch - DK; }
+                else { src = static_cast<const Tin *>(p.x_v); stride = DV; off = ch - 2 * DK; }
+                Tin *cw = static_cast<Tin *>(p.window) + ((size_t)ck * H + h) * 3 * CH;
+                const int pos = (j + 1) * p.ckpt_interval;
+#pragma unroll
+                for (int r = 0; r < 3; ++r)
+                    cw[r * CH + ch] = src[((size_t)(p.cu_seqlens[s] + pos - 3 + r) * H + h) * stride + off];
+            }
         }
     }
 
@@ -840,6 +857,23 @@ __global__ __launch_bounds__(kScanThreads) void kda_prefill_scan_kernel(PrefillP
             scan_load_b<DK, DV>(ws, gnext, w4, lr, lk, j0, ops);
         }
         __syncthreads();
+        // interval checkpoint: the state after this chunk is in S[(c + 1) & 1],
+        // which is not written again before two more barriers
+        if (p.ckpt_slots) {
+            const int pos = min((c + 1) * kChunk, len);
+            const int j = pos / p.ckpt_interval - 1;
+            if (pos % p.ckpt_interval == 0 && j < p.ckpt_per_seq) {
+                const int ck = p.ckpt_slots[(size_t)s * p.ckpt_per_seq + j];
+                if (slot_ok(ck, p.n_slots)) {
+                    float *D = p.state + ((size_t)ck * H + h) * DK * DV;
+                    const int nxt = (c + 1) & 1;
+                    for (int e = tid; e < DK * CB; e += kScanThreads)
+                        D[(e / CB) * DV + j0 + e % CB] = S[nxt][e / CB][e % CB];
+                } else if (ck != -1 && tid == 0 && blockIdx.z == 0) {
+                    flag_error(p.err_flag);
+                }
+            }
+        }
     }
     const int fin = nch & 1;
     for (int e = tid; e < DK * CB; e += kScanThreads) Sg[(e / CB) * DV + j0 + e % CB] = S[fin][e / CB][e % CB];

@@ -181,6 +181,21 @@ def test_prefill_validation(lib):
                                  ctypes.byref(Ibad), None, FAKE, 1 << 30, None) == 3
 
 
+def test_prefill_ckpt_validation(lib):
+    L, C, I = good_layer(), good_cache(), good_inputs()
+    p = lambda ck=FAKE, iv=128, per=2, chunk=64, n=1, T=128: lib.kda_chunk_prefill_ckpt(
+        ctypes.byref(L), ctypes.byref(C), FAKE, FAKE, n, T, chunk, ctypes.byref(I), FAKE, ck, iv, per,
+        FAKE, 1 << 30, None)
+    assert p(ck=None) == 1
+    assert p(ck=FAKE + 2) == 4
+    assert p(iv=0) == 2
+    assert p(iv=32) == 2
+    assert p(iv=96) == 2
+    assert p(per=0) == 2
+    assert p(chunk=32, iv=64) == 5
+    assert p(n=0) == 2
+
+
 def test_copy_probe_validation(lib):
     assert lib.kda_copy_probe(FAKE, FAKE, 0, None) == 0
     assert lib.kda_copy_probe(None, FAKE, 4, None) == 1

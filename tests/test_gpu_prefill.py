@@ -263,3 +263,100 @@ def test_prefill_deterministic():
         y, _ = run_prefill(dl, cache, [0], [T], inp, "bf16")
         outs.append((y, host(cache.state)))
     assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+
+
+# ---------------------------------------------------------------------------
+# interval checkpoints (kda_chunk_prefill_ckpt)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("interval", [64, 128])
+def test_prefill_checkpoints_match_oracle(interval):
+    """Each checkpoint equals the oracle's state and window after that many
+    tokens; outputs and final states are bitwise those of kda_chunk_prefill;
+    slots the call must not touch stay as they were."""
+    g = synth.rng(1200 + interval)
+    H, dk, dv = 4, 128, 128
+    params = synth.layer_params(g, H, dk, dv)
+    dl, ol = layer_pair(params)
+    lens = [300, 128, 70, 0, 63]
+    per = 4
+    total = sum(lens)
+    inp = synth.token_inputs(g, (total,), H, dk, dv, "bf16")
+    N = len(lens)
+    n_slots = N + N * per + 2
+    perm = g.permutation(n_slots).astype(np.int32)
+    live = perm[:N].copy()
+    ck = perm[N:N + N * per].reshape(N, per).copy()
+    ck[2, 0] = -1                       # sequence 2's only checkpoint is not kept
+    s0 = synth.random_state(g, (N, H, dk, dv), 0.2)
+    w0 = synth.window_inputs(g, (N,), H, dk, dv, "bf16")
+    cache = new_cache(n_slots, H, dk, dv, "bf16", fill_seed=5)
+    lt = torch.from_numpy(live).to(DEV).long()
+    cache.state[lt] = torch.from_numpy(s0).to(DEV)
+    cache.conv_state[lt] = to_dev(w0, torch.bfloat16)
+    plain = api.Cache(cache.state.clone(), cache.conv_state.clone(), torch.zeros_like(cache.err_flag))
+    before = api.Cache(cache.state.clone(), cache.conv_state.clone(), None)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    cut = torch.from_numpy(cu).to(DEV)
+    y = torch.full((total, H, dv), 7.0, device=DEV)
+    api.kda_chunk_prefill_ckpt(dl, cache, lt.int(), cut, dev_inputs(inp, "bf16"), y,
+                               torch.from_numpy(ck).to(DEV), interval)
+    y2 = torch.full_like(y, 7.0)
+    api.kda_chunk_prefill(dl, plain, lt.int(), cut, dev_inputs(inp, "bf16"), y2)
+    torch.cuda.synchronize()
+    assert cache.err_flag.item() == 0
+    assert torch.equal(y, y2)
+    assert torch.equal(cache.state[lt], plain.state[lt])
+    assert torch.equal(cache.conv_state[lt], plain.conv_state[lt])
+    written = set()
+    for s in range(N):
+        n_ck = min(per, lens[s] // interval)
+        if n_ck == 0:
+            continue
+        sub = {k: v[None, cu[s]:cu[s + 1]] for k, v in inp.items()}
+        o = kda_oracle.run(ol, s0[s][None], w0[s][None], sub["x_q"], sub["x_k"], sub["x_v"], sub["g"],
+                           sub["b"], sub["z"], y_tokens=0, snapshots=True)
+        for j in range(n_ck):
+            if ck[s, j] == -1:
+                continue
+            pos = (j + 1) * interval
+            slot = int(ck[s, j])
+            written.add(slot)
+            err = state_rel_err(host(cache.state[slot:slot + 1]), o["snap_state"][:, pos - 1])
+            assert err < 1e-4, (s, j, err)
+            assert np.array_equal(host(cache.conv_state[slot]), o["snap_window"][0, pos - 1]), (s, j)
+    # a checkpoint at the last token equals the final state bit for bit
+    if lens[0] % interval == 0 or lens[1] % interval == 0:
+        s = 0 if lens[0] % interval == 0 else 1
+        j = lens[s] // interval - 1
+        if j < per:
+            assert torch.equal(cache.state[int(ck[s, j])], cache.state[int(live[s])])
+    untouched = [i for i in range(n_slots) if i not in written and i not in set(live.tolist())]
+    ut = torch.tensor(untouched, device=DEV).long()
+    assert torch.equal(cache.state[ut], before.state[ut])
+    assert torch.equal(cache.conv_state[ut], before.conv_state[ut])
+    assert len(written) == sum(int(ck[s, j] != -1) for s in range(N) for j in range(min(per, lens[s] // interval)))
+
+
+def test_prefill_checkpoint_bad_slot_flags_error():
+    g = synth.rng(1300)
+    H, dk, dv = 2, 64, 64
+    params = synth.layer_params(g, H, dk, dv)
+    dl, ol = layer_pair(params)
+    T = 192
+    inp = synth.token_inputs(g, (T,), H, dk, dv, "bf16")
+    cache = new_cache(4, H, dk, dv, "bf16")
+    ck = np.array([[2, cache.n_slots + 9, 3]], dtype=np.int32)
+    y = torch.empty((T, H, dv), device=DEV)
+    api.kda_chunk_prefill_ckpt(dl, cache, torch.tensor([0], dtype=torch.int32, device=DEV),
+                               torch.tensor([0, T], dtype=torch.int32, device=DEV), dev_inputs(inp, "bf16"),
+                               y, torch.from_numpy(ck).to(DEV), 64)
+    torch.cuda.synchronize()
+    assert cache.err_flag.item() == 1
+    o = oracle_seq(ol, np.zeros((H, dk, dv)), np.zeros((H, 3, 2 * dk + dv)), inp, 0, T, y_tokens=T)
+    check_tokens(host(y), o["y"][0])
+    assert state_rel_err(host(cache.state[0:1]), o["state"]) < 1e-4
+    # the good checkpoints (64 and 192 tokens) were still written
+    o2 = kda_oracle.run(ol, np.zeros((1, H, dk, dv)), np.zeros((1, H, 3, 2 * dk + dv)),
+                        *(inp[k][None] for k in KEYS), y_tokens=0, snapshots=True)
+    assert state_rel_err(host(cache.state[2:3]), o2["snap_state"][:, 63]) < 1e-4
+    assert state_rel_err(host(cache.state[3:4]), o2["snap_state"][:, 191]) < 1e-4

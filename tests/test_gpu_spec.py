@@ -153,7 +153,7 @@ def test_verify_delta_matches_oracle_and_records():
     ys = torch.empty((B, T, dl.H, dl.d_v), device=DEV)
     api.kda_spec_verify(dl, cache, lt, torch.from_numpy(snaps).to(DEV), I, ys,
                         draft_len=torch.from_numpy(dlen).to(DEV))
-    delta = api.new_spec_delta(dl, B, T, torch.bfloat16, DEV)
+    delta = api.new_spec_delta(dl, B, T, torch.bfloat16, DEV).zero_()
     yd = torch.full((B, T, dl.H, dl.d_v), 7.0, device=DEV)
     api.kda_spec_verify_delta(dl, cache, lt, I, yd, delta, draft_len=torch.from_numpy(dlen).to(DEV))
     torch.cuda.synchronize()
