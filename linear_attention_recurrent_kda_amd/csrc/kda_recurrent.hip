@@ -251,6 +251,23 @@ __device__ __forceinline__ void prep_token(const RecParams &p, int lane, int j,
     }
 }
 
+// y = o / sqrt(mean(o^2) + eps_r) * gate for the 4 columns 4c..4c+3 of one
+// token, by lanes 0 .. d_v/4 - 1 of one wave (a butterfly over those lanes).
+template <int DV>
+__device__ __forceinline__ void output_row(const RecParams &p, float4 o, const float *gate, int c,
+                                           float *yrow) {
+    float ss2 = o.x * o.x;
+    ss2 = fmaf(o.y, o.y, ss2);
+    ss2 = fmaf(o.z, o.z, ss2);
+    ss2 = fmaf(o.w, o.w, ss2);
+#pragma unroll
+    for (int m = 1; m < DV / 4; m <<= 1) ss2 += __shfl_xor(ss2, m, kWave);
+    const float r = 1.0f / sqrtf(ss2 * (1.0f / DV) + p.rms_eps);
+    const float4 gt = make_float4(gate[4 * c], gate[4 * c + 1], gate[4 * c + 2], gate[4 * c + 3]);
+    *reinterpret_cast<float4 *>(yrow + 4 * c) =
+        make_float4(o.x * r * gt.x, o.y * r * gt.y, o.z * r * gt.z, o.w * r * gt.w);
+}
+
 enum RecMode { kDecode = 0, kVerify = 1, kVerifyDelta = 2 };
 
 template <int DK, int DV, int NT, typename Tin, int TMAX, int MODE, bool STREAM>
@@ -258,8 +275,17 @@ __global__ __launch_bounds__(NT) void kda_recurrent_kernel(RecParams p) {
     using G = RecGeo<DK, DV, NT>;
     constexpr bool VERIFY = MODE != kDecode;
     constexpr bool DELTA = MODE == kVerifyDelta;
+    // red[]: per-wave partial sums of u and p.  Double-buffered (token t uses
+    // half t & 1) where LDS allows, so no barrier is needed after a token;
+    // at TMAX = 16 the second half would cost a workgroup per CU.
+    // obuf[]: unnormalised outputs of a multi-token call, normalised after
+    // the recurrence (one wave per token) so the RMSNorm reduction is not on
+    // the token chain.
+    constexpr int NRB = TMAX <= 8 ? 2 : 1;
+    constexpr bool DEFER = TMAX > 1;
     __shared__ TokenLds<DK, DV> tok[TMAX];
-    __shared__ float4 red[G::NW][2][G::CG];
+    __shared__ float4 red[NRB][G::NW][2][G::CG];
+    __shared__ float4 obuf[DEFER ? TMAX : 1][G::CG];
 
     const int tid = threadIdx.x;
     const int lane = tid % kWave, wave = tid / kWave;
@@ -302,10 +328,19 @@ __global__ __launch_bounds__(NT) void kda_recurrent_kernel(RecParams p) {
     __syncthreads();
     // delta mode: alpha and k^ of every token into its record
     if (DELTA) {
-        for (int i = tid; i < T * 2 * DK; i += NT) {
+        constexpr int NI = (TMAX * 2 * DK + NT - 1) / NT;
+        float v[NI];
+#pragma unroll
+        for (int k = 0; k < NI; ++k) {   // all LDS reads first, then the stores
+            const int i = min(tid + NT * k, T * 2 * DK - 1);
             const int t = i / (2 * DK), e = i % (2 * DK);
-            DeltaRec<DK, DV, Tin>::f(p.delta, ((size_t)b * p.T + t) * p.H + h)[e] =
-                e < DK ? tok[t].alpha[e] : tok[t].conv[e];
+            v[k] = e < DK ? tok[t].alpha[e] : tok[t].conv[e];
+        }
+#pragma unroll
+        for (int k = 0; k < NI; ++k) {
+            const int i = tid + NT * k;
+            if (i < T * 2 * DK)
+                DeltaRec<DK, DV, Tin>::f(p.delta, ((size_t)b * p.T + i / (2 * DK)) * p.H + h)[i % (2 * DK)] = v[k];
         }
     }
 
@@ -328,12 +363,13 @@ __global__ __launch_bounds__(NT) void kda_recurrent_kernel(RecParams p) {
             pq.x += __shfl_xor(pq.x, m, kWave); pq.y += __shfl_xor(pq.y, m, kWave);
             pq.z += __shfl_xor(pq.z, m, kWave); pq.w += __shfl_xor(pq.w, m, kWave);
         }
-        if (lane < G::CG) { red[wave][0][cg] = u; red[wave][1][cg] = pq; }
+        const int rb = NRB == 2 ? (t & 1) : 0;
+        if (lane < G::CG) { red[rb][wave][0][cg] = u; red[rb][wave][1][cg] = pq; }
         __syncthreads();
-        float4 U = red[0][0][cg], P = red[0][1][cg];
+        float4 U = red[rb][0][0][cg], P = red[rb][0][1][cg];
 #pragma unroll
         for (int w = 1; w < G::NW; ++w) {
-            const float4 a = red[w][0][cg], c = red[w][1][cg];
+            const float4 a = red[rb][w][0][cg], c = red[rb][w][1][cg];
             U.x += a.x; U.y += a.y; U.z += a.z; U.w += a.w;
             P.x += c.x; P.y += c.y; P.z += c.z; P.w += c.w;
         }
@@ -358,23 +394,22 @@ __global__ __launch_bounds__(NT) void kda_recurrent_kernel(RecParams p) {
                 flag_error(p.err_flag);
             }
         }
-        // output: o = p + (k^.q^) d, RMSNorm over d_v, gate
+        // output: o = p + (k^.q^) d (= S^T q^ of the new state)
         if (tid < G::CG) {
             const float kq = tk.kq;
             const float4 o = make_float4(fmaf(kq, d.x, P.x), fmaf(kq, d.y, P.y),
                                          fmaf(kq, d.z, P.z), fmaf(kq, d.w, P.w));
-            float ss2 = o.x * o.x;
-            ss2 = fmaf(o.y, o.y, ss2);
-            ss2 = fmaf(o.z, o.z, ss2);
-            ss2 = fmaf(o.w, o.w, ss2);
-#pragma unroll
-            for (int m = 1; m < G::CG; m <<= 1) ss2 += __shfl_xor(ss2, m, kWave);
-            const float r = 1.0f / sqrtf(ss2 * (1.0f / DV) + p.rms_eps);
-            const float4 gt = *reinterpret_cast<const float4 *>(&tk.gate[4 * cg]);
-            *reinterpret_cast<float4 *>(yb + (size_t)t * p.H * DV + 4 * cg) =
-                make_float4(o.x * r * gt.x, o.y * r * gt.y, o.z * r * gt.z, o.w * r * gt.w);
+            if (DEFER) obuf[t][cg] = o;
+            else output_row<DV>(p, o, tk.gate, cg, yb);
         }
-        __syncthreads();   // red[] is rewritten by the next token
+        if (NRB == 1) __syncthreads();   // red[] is rewritten by the next token
+    }
+    // RMSNorm + gate of the deferred outputs: token t by lanes 0 .. CG-1 of
+    // wave t % NW, the lanes and reduction order of the inline form
+    if (DEFER) {
+        __syncthreads();
+        for (int t = wave; t < T; t += G::NW)
+            if (lane < G::CG) output_row<DV>(p, obuf[t][lane], tok[t].gate, lane, yb + (size_t)t * p.H * DV);
     }
 
     // 5. the single write of the state tile (decode only: verify leaves S0)
