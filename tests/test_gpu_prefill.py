@@ -194,7 +194,10 @@ def test_prefill_then_decode_continues_the_sequence():
 def test_full_length_32k_sampled():
     """The long-prompt workload at full size: B=1, T=32768, H=32, d=128.
     All heads checked on the first 2048 tokens; 4 sampled heads checked over
-    all 32768 tokens (outputs of the last chunk, final state)."""
+    all 32768 tokens (outputs of the last chunk, final state).  The same call
+    with a checkpoint every 8192 tokens gives bitwise the same outputs, and
+    each checkpoint matches the oracle's state at that token on the sampled
+    heads."""
     cfg = synth.WORKLOADS["prefill_t32k"]
     g = synth.rng(cfg["seed"])
     H, dk, dv, T = cfg["H"], cfg["d_k"], cfg["d_v"], cfg["T"]
@@ -204,18 +207,38 @@ def test_full_length_32k_sampled():
     cache = new_cache(1, H, dk, dv, "bf16")
     print("  running prefill on the GPU", flush=True)
     y, _ = run_prefill(dl, cache, [0], [T], inp, "bf16")
+    # the same call keeping a checkpoint every 8192 tokens (slots 1..4)
+    print("  running prefill with checkpoints on the GPU", flush=True)
+    ckc = new_cache(5, H, dk, dv, "bf16")
+    yc = torch.empty((T, H, dv), device=DEV)
+    api.kda_chunk_prefill_ckpt(dl, ckc, torch.zeros(1, dtype=torch.int32, device=DEV),
+                               torch.tensor([0, T], dtype=torch.int32, device=DEV), dev_inputs(inp, "bf16"),
+                               yc, torch.arange(1, 5, dtype=torch.int32, device=DEV).reshape(1, 4), 8192)
+    torch.cuda.synchronize()
+    assert ckc.err_flag.item() == 0
+    assert np.array_equal(host(yc), y)
+    assert torch.equal(ckc.state[0], cache.state[0])
     print("  oracle: all heads, first 2048 tokens", flush=True)
     z0, w0 = np.zeros((H, dk, dv)), np.zeros((H, 3, 2 * dk + dv))
     o = oracle_seq(ol, z0, w0, inp, 0, 2048)
     check_tokens(y[:2048], o["y"][0])
     heads = [0, 9, 22, 31]
-    print("  oracle: 4 heads, all tokens", flush=True)
     sub = {k: v[:, heads] for k, v in inp.items()}
-    o2 = oracle_seq(ol.heads(heads), z0[heads], w0[heads], sub, 0, T)
+    oh = ol.heads(heads)
+    st, win = z0[heads], w0[heads]
+    for j in range(4):
+        print(f"  oracle: 4 heads, tokens {8192 * j} .. {8192 * (j + 1)}", flush=True)
+        o2 = oracle_seq(oh, st, win, sub, 8192 * j, 8192 * (j + 1), y_tokens=8192 if j == 3 else 0)
+        st, win = o2["state"][0], o2["window"][0]
+        err = state_rel_err(host(ckc.state[j + 1:j + 2, heads]), o2["state"])
+        print(f"  checkpoint {j} state rel err (4 heads) {err:.3e}", flush=True)
+        assert err < 1e-3
+        assert np.array_equal(host(ckc.conv_state[j + 1, heads]), o2["window"][0])
     check_tokens(y[-64:, heads], o2["y"][0, -64:])
     err = state_rel_err(host(cache.state[0:1, heads]), o2["state"])
     print(f"  final state rel err (4 heads) {err:.3e}", flush=True)
     assert err < 1e-3
+    assert torch.equal(ckc.state[4], ckc.state[0])
 
 
 def test_all_sequences_empty():
