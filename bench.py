@@ -93,6 +93,8 @@ def parse():
     ap.add_argument("--prefill-only", action="store_true",
                     help="run only the chunked-prefill measurement (32768 tokens, H=32) and print it; "
                          "for profiling that path")
+    ap.add_argument("--decode-b1-only", action="store_true",
+                    help="run only the batch-1 decode latency measurement and print it; for profiling that path")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the timed region, run one plain copy of this many MiB "
                          "(a known-size kernel for calibrating memory counters)")
@@ -115,6 +117,9 @@ def main():
     if args.prefill_only:
         print(json.dumps({"chunk_prefill_t32k": prefill_extra(torch, api, synth, torch.cuda.current_stream())}),
               flush=True)
+        return
+    if args.decode_b1_only:
+        print(json.dumps({"decode_b1": decode_b1_extra(torch, api, synth)}), flush=True)
         return
     cfg = synth.WORKLOADS["decode_b64"]
     B, H, dk, dv, n_slots = cfg["B"], cfg["H"], cfg["d_k"], cfg["d_v"], cfg["n_slots"]
@@ -333,7 +338,69 @@ def extras(torch, api, synth, layer, cache, step_inputs, y, slots, B, H, dk, dv,
                                    "algorithmic_gbs": cdb / scd / 1e9, "bytes_per_call": cdb}
     ex["spec_step_b16_t8"] = {"snapshots_us": (sv + sc) * 1e6, "deltas_us": (svd + scd) * 1e6}
     ex["chunk_prefill_t32k"] = prefill_extra(torch, api, synth, stream)
+    ex["decode_b1"] = decode_b1_extra(torch, api, synth)
     return ex
+
+
+def decode_b1_extra(torch, api, synth, steps=1000, graph_steps=100):
+    """The batch-1 decode (latency-bound): B=1, H=32, d=128, one slot of a
+    256-slot pool.  Times `steps` back-to-back launches with events (launch
+    gaps included), and the same launches captured `graph_steps` at a time in
+    a HIP graph and replayed (host launch cost removed)."""
+    dev = "cuda:0"
+    cfg = synth.WORKLOADS["decode_b1"]
+    H, dk, dv, n_slots = cfg["H"], cfg["d_k"], cfg["d_v"], cfg["n_slots"]
+    g = synth.rng(cfg["seed"])
+    p = synth.layer_params(g, H, dk, dv)
+    td = lambda a, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(dt)
+    layer = api.Layer(td(p["A"]), td(p["conv_wt"]), td(p["norm_w"]))
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(cfg["seed"])
+    cache = api.Cache(torch.randn((n_slots, H, dk, dv), generator=gen, device=dev) * 0.05,
+                      torch.zeros((n_slots, H, 3, 2 * dk + dv), dtype=torch.bfloat16, device=dev))
+    slot = td(g.permutation(n_slots)[:1].astype(np.int32), torch.int32)
+    inp = synth.token_inputs(g, (steps, 1), H, dk, dv, "bf16")
+    dinp = {k: td(v, torch.bfloat16) for k, v in inp.items()}
+    ins = [api.Inputs(*(dinp[k][t] for k in ("x_q", "x_k", "x_v", "g", "b", "z"))) for t in range(steps)]
+    y = torch.empty((1, H, dv), device=dev)
+    stream = torch.cuda.current_stream()
+    calls = [api.kda_decode_prepared(layer, cache, slot, ins[t], y) for t in range(steps)]
+    for c in calls[:10]:
+        c()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    a.record(stream)
+    for c in calls:
+        c()
+    b.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    ev = a.elapsed_time(b) / 1e3 / steps
+    # the same launches in a graph (captured on torch's capture stream)
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            for t in range(graph_steps):
+                api.kda_decode(layer, cache, slot, ins[t], y)
+    stream.wait_stream(side)
+    graph.replay()
+    torch.cuda.synchronize()
+    reps = steps // graph_steps
+    a.record(stream)
+    for _ in range(reps):
+        graph.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    gs = a.elapsed_time(b) / 1e3 / (reps * graph_steps)
+    bl = (2 * dk * dv * 4 + (3 * dk + 2 * dv) * 2 + 2 + 2 * 3 * (2 * dk + dv) * 2 + dv * 4
+          + (dk + (2 * dk + dv) * 4 + dv) * 4) * H
+    return {"us_per_step_events": ev * 1e6, "us_per_step_wall": wall * 1e6,
+            "us_per_step_graph": gs * 1e6, "bytes_per_step": bl,
+            "algorithmic_gbs_graph": bl / gs / 1e9, "steps": steps}
 
 
 def prefill_mfma_per_chunk_head(dk, dv, col_block=16):

@@ -333,3 +333,44 @@ def test_stream_state_flag_is_bitwise_identical():
         outs.append((y, yv, cache.state.clone(), cache.conv_state.clone()))
     for a, b in zip(*outs):
         assert torch.equal(a, b)
+
+
+def test_decode_in_a_hip_graph_matches_eager():
+    """One decode step captured in a HIP graph (torch.cuda.CUDAGraph on the
+    capture stream) and replayed step after step, with the next step's inputs
+    copied into the captured buffers eagerly between replays: every replay's
+    output and the final state and window equal the eager launches bitwise."""
+    B, H, dk, dv, steps = 4, 4, 128, 128, 6
+    g = synth.rng(1500)
+    params = synth.layer_params(g, H, dk, dv)
+    dl, _ = layer_pair(params)
+    inp = synth.token_inputs(g, (steps, B), H, dk, dv, "bf16")
+    slots = torch.from_numpy(g.permutation(8)[:B].astype(np.int32)).to(DEV)
+    eager = new_cache(8, H, dk, dv, "bf16", fill_seed=3)
+    graphed = api.Cache(eager.state.clone(), eager.conv_state.clone(), torch.zeros_like(eager.err_flag))
+    ye = []
+    for t in range(steps):
+        y = torch.empty((B, H, dv), device=DEV)
+        api.kda_decode(dl, eager, slots, inputs_dev(inp, "bf16", sl=t), y)
+        ye.append(y)
+    static = inputs_dev(inp, "bf16", sl=0)
+    ys = torch.empty((B, H, dv), device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        api.kda_decode(dl, graphed, slots, static, ys)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    # capture does not run the kernel: the graphed pools still hold the start state
+    assert not torch.equal(graphed.state, eager.state)
+    for t in range(steps):
+        src = inputs_dev(inp, "bf16", sl=t)
+        for name in ("x_q", "x_k", "x_v", "g", "b", "z"):
+            getattr(static, name).copy_(getattr(src, name))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(ys, ye[t]), t
+    assert torch.equal(graphed.state, eager.state)
+    assert torch.equal(graphed.conv_state, eager.conv_state)
+    assert graphed.err_flag.item() == 0
