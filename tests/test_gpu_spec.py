@@ -289,6 +289,17 @@ def test_commit_delta_errors_and_padding():
     assert cache.err_flag.item() == 1
     assert torch.equal(cache.state, before_s)
     assert torch.equal(cache.conv_state, before_w)
+    # a sequence with no draft tokens: zero outputs, and its commit (L = 0) is a no-op
+    dlen = np.array([0, T, 2, T], dtype=np.int32)
+    y.fill_(5.0)
+    api.kda_spec_verify_delta(dl, cache, lt, inputs_dev(inp, "bf16"), y, delta,
+                              draft_len=torch.from_numpy(dlen).to(DEV))
+    api.kda_spec_commit_delta(dl, cache, lt, delta, torch.from_numpy(np.array([0, 1, 2, 0], np.int32)).to(DEV))
+    torch.cuda.synchronize()
+    assert torch.all(y[0] == 0) and torch.all(y[2, 2:] == 0) and not torch.any(y[1] == 5.0)
+    assert torch.equal(cache.state[int(live[0])], before_s[int(live[0])])
+    assert torch.equal(cache.conv_state[int(live[3])], before_w[int(live[3])])
+    assert cache.err_flag.item() == 1            # still set from the bad lengths above
     # a bad live slot in the verification flags and zeroes that row
     cache.err_flag.zero_()
     bad = live.copy()
