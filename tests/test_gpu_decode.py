@@ -374,3 +374,53 @@ def test_decode_in_a_hip_graph_matches_eager():
     assert torch.equal(graphed.state, eager.state)
     assert torch.equal(graphed.conv_state, eager.conv_state)
     assert graphed.err_flag.item() == 0
+
+
+def test_alpha_zero_forgets_the_state():
+    """g = +inf (bf16 infinity): alpha = exp(-e^A * inf) = 0 exactly, so the
+    old state is wiped and, from any state, S_1 = beta k^ v^T and
+    o = beta (k^.q^) v as from a zero state; GPU state and outputs match the
+    oracle run from the same (non-zero) start."""
+    dl, ol, inp, slots = _slot_case(seed=720)
+    inp = dict(inp, g=np.full_like(inp["g"], np.inf))
+    cache = new_cache(32, dl.H, dl.d_k, dl.d_v, "bf16", fill_seed=11)
+    st = torch.from_numpy(slots).to(DEV).long()
+    s0, w0 = host(cache.state[st]), host(cache.conv_state[st])
+    y = torch.empty((8, dl.H, dl.d_v), device=DEV)
+    api.kda_decode(dl, cache, torch.from_numpy(slots).to(DEV), inputs_dev(inp, "bf16"), y)
+    torch.cuda.synchronize()
+    o = kda_oracle.run(ol, s0, w0, *(inp[k][:, None] for k in ("x_q", "x_k", "x_v", "g", "b", "z")))
+    z = kda_oracle.run(ol, np.zeros_like(s0), w0, *(inp[k][:, None] for k in ("x_q", "x_k", "x_v", "g", "b", "z")))
+    assert np.array_equal(o["state"], z["state"])            # the oracle forgets S0 as well
+    assert parity_error(host(y), o["y"][:, 0]) <= TOL
+    assert state_rel_err(host(cache.state[st]), o["state"]) < 1e-5
+    assert cache.err_flag.item() == 0
+
+
+def test_large_batch_sampled_sequences():
+    """B = 512 sequences (16384 workgroups, many rounds) over a 2048-slot
+    pool: 6 sampled sequences against the oracle over 3 steps, every slot
+    outside the table bitwise untouched."""
+    B, H, dk, dv, n_slots, steps = 512, 32, 128, 128, 2048, 3
+    g = synth.rng(730)
+    params = synth.layer_params(g, H, dk, dv)
+    dl, ol = layer_pair(params)
+    inp = synth.token_inputs(g, (steps, B), H, dk, dv, "bf16")
+    slots = synth.slot_table(g, B, n_slots)
+    cache = new_cache(n_slots, H, dk, dv, "bf16", fill_seed=12)
+    before_s, before_w = cache.state.clone(), cache.conv_state.clone()
+    pick = np.array([0, 1, 137, 255, 256, 511])
+    s0 = host(cache.state[torch.from_numpy(slots[pick]).long().to(DEV)])
+    w0 = host(cache.conv_state[torch.from_numpy(slots[pick]).long().to(DEV)])
+    y = run_decode_steps(dl, cache, torch.from_numpy(slots).to(DEV), inp, "bf16", steps, B)
+    sub = {k: v[:, pick] for k, v in inp.items()}
+    yo, so, wo = oracle_steps(ol, s0, w0, sub, steps)
+    assert_per_step(y[:, pick], yo)
+    got = host(cache.state[torch.from_numpy(slots[pick]).long().to(DEV)])
+    assert state_rel_err(got, so) < 1e-5
+    assert np.array_equal(host(cache.conv_state[torch.from_numpy(slots[pick]).long().to(DEV)]), wo)
+    untouched = torch.ones(n_slots, dtype=torch.bool, device=DEV)
+    untouched[torch.from_numpy(slots).long().to(DEV)] = False
+    assert torch.equal(cache.state[untouched], before_s[untouched])
+    assert torch.equal(cache.conv_state[untouched], before_w[untouched])
+    assert cache.err_flag.item() == 0
