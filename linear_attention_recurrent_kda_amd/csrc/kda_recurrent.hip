@@ -106,6 +106,20 @@ struct ConvRegs {
     Tin x[CPT][3 + TMAX];
 };
 
+// A global-memory pointer that is the same on every lane, held in scalar
+// registers and typed as global (address space 1), so loads through it stay
+// global loads (a generic pointer would make them flat loads, which the
+// compiler can only wait for with a full drain of the load counter).
+template <typename T>
+using gptr = const __attribute__((address_space(1))) T *;
+template <typename T>
+__device__ __forceinline__ gptr<T> uniform_ptr(const T *ptr) {
+    const uint64_t v = reinterpret_cast<uint64_t>(ptr);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<gptr<T>>(((uint64_t)hi << 32) | lo);
+}
+
 // All loads are unconditional (out-of-range channel slots and tokens re-read a
 // valid element) so the compiler issues them back to back, ahead of the state
 // tile, without branches that would force waits.  Requires T >= 1.
@@ -114,6 +128,13 @@ __device__ __forceinline__ void conv_fetch(const RecParams &p, int tid, int b, i
                                            ConvRegs<DK, DV, NT, Tin, TMAX> &cr) {
     constexpr int CH = 2 * DK + DV;
     const Tin *win = static_cast<const Tin *>(p.window) + ((size_t)slot * p.H + h) * 3 * CH;
+    // the three input bases as wave-uniform (scalar) values: a per-lane
+    // choice among the kernel-argument fields themselves would be compiled
+    // as a vector load of the pointer, a memory round trip before any input
+    // (and the state tile after them) could be requested
+    const gptr<Tin> xq = uniform_ptr(static_cast<const Tin *>(p.x_q));
+    const gptr<Tin> xk = uniform_ptr(static_cast<const Tin *>(p.x_k));
+    const gptr<Tin> xv = uniform_ptr(static_cast<const Tin *>(p.x_v));
 #pragma unroll
     for (int k = 0; k < cr.CPT; ++k) {
         const int c = min(tid + NT * k, CH - 1);
@@ -122,8 +143,7 @@ __device__ __forceinline__ void conv_fetch(const RecParams &p, int tid, int b, i
         cr.x[k][1] = win[CH + c];
         cr.x[k][2] = win[2 * CH + c];
         const bool isq = c < DK, isk = !isq && c < 2 * DK;
-        const Tin *src = isq ? static_cast<const Tin *>(p.x_q)
-                             : (isk ? static_cast<const Tin *>(p.x_k) : static_cast<const Tin *>(p.x_v));
+        const gptr<Tin> src = isq ? xq : (isk ? xk : xv);
         const int stride = isq || isk ? DK : DV;
         const int off = isq ? c : (isk ? c - DK : c - 2 * DK);
 #pragma unroll
@@ -270,60 +290,118 @@ __device__ __forceinline__ void output_row(const RecParams &p, float4 o, const f
 
 enum RecMode { kDecode = 0, kVerify = 1, kVerifyDelta = 2 };
 
+// LDS of one (sequence, head) item.
+// red[]: per-wave partial sums of u and p.  Double-buffered (token t uses
+// half t & 1) where LDS allows, so no barrier is needed after a token; at
+// TMAX = 16 the second half would cost a workgroup per CU.
+// obuf[]: unnormalised outputs of a multi-token call, normalised after the
+// recurrence (one wave per token) so the RMSNorm reduction is not on the
+// token chain.
+template <int DK, int DV, int NT, int TMAX>
+struct RecShared {
+    using G = RecGeo<DK, DV, NT>;
+    static constexpr int NRB = TMAX <= 8 ? 2 : 1;
+    static constexpr bool DEFER = TMAX > 1;
+    TokenLds<DK, DV> tok[TMAX];
+    float4 red[NRB][G::NW][2][G::CG];
+    float4 obuf[DEFER ? TMAX : 1][G::CG];
+};
+
+// Registers of one item between its loads and its computation.
+template <int DK, int DV, int NT, typename Tin, int TMAX>
+struct RecItem {
+    using G = RecGeo<DK, DV, NT>;
+    static constexpr int TPW = (TMAX + G::NW - 1) / G::NW;
+    int b, h, T, slot;
+    bool run;
+    float *yb, *S;
+    ConvRegs<DK, DV, NT, Tin, TMAX> cr;
+    PrepRegs<DK, DV, Tin, TPW> pr;
+    float4 s[G::RPT];
+};
+
+// Slot resolution of item `item` = b * H + h (scalar reads only, so that a
+// workgroup can resolve all of its items before it stores anything).
+template <int DK, int DV, int NT, typename Tin, int TMAX, int MODE>
+__device__ __forceinline__ void rec_resolve(const RecParams &p, int item, RecItem<DK, DV, NT, Tin, TMAX> &it) {
+    constexpr bool VERIFY = MODE != kDecode;
+    const int b = item / p.H, h = item % p.H;
+    it.b = b;
+    it.h = h;
+    int T = 1;
+    if (VERIFY) T = p.draft_len ? min(max(p.draft_len[b], 0), p.T) : p.T;
+    it.T = T;
+    it.slot = p.slot_idx[b];
+    const int y_rows = VERIFY ? p.T : 1;
+    it.yb = p.y + ((size_t)b * y_rows * p.H + h) * DV;   // token t at + t*H*DV
+    it.run = !(it.slot < 0 || it.slot >= p.n_slots || T == 0);
+}
+
+// Rows that will not be computed (padding, a bad slot, no draft tokens):
+// their outputs are zeroed and a bad slot is flagged.  Computed rows get
+// zeros for the draft tokens past their length.
+template <int DK, int DV, int NT, typename Tin, int TMAX, int MODE>
+__device__ __forceinline__ void rec_side(const RecParams &p, const RecItem<DK, DV, NT, Tin, TMAX> &it) {
+    constexpr bool VERIFY = MODE != kDecode;
+    const int tid = threadIdx.x;
+    const bool bad = it.slot < 0 || it.slot >= p.n_slots;
+    if (bad && it.slot != -1 && tid == 0) flag_error(p.err_flag);
+    const int y_rows = VERIFY ? p.T : 1;
+    for (int t = bad ? 0 : it.T; t < y_rows; ++t)
+        for (int j = tid; j < DV; j += NT) it.yb[(size_t)t * p.H * DV + j] = 0.f;
+}
+
+// Every load of a resolved item that will be computed: the small operands
+// first, then the single read of the state tile, so the conv/gate math waits
+// only for the former.
 template <int DK, int DV, int NT, typename Tin, int TMAX, int MODE, bool STREAM>
-__global__ __launch_bounds__(NT) void kda_recurrent_kernel(RecParams p) {
+__device__ __forceinline__ void rec_loads(const RecParams &p, RecItem<DK, DV, NT, Tin, TMAX> &it) {
     using G = RecGeo<DK, DV, NT>;
     constexpr bool VERIFY = MODE != kDecode;
-    constexpr bool DELTA = MODE == kVerifyDelta;
-    // red[]: per-wave partial sums of u and p.  Double-buffered (token t uses
-    // half t & 1) where LDS allows, so no barrier is needed after a token;
-    // at TMAX = 16 the second half would cost a workgroup per CU.
-    // obuf[]: unnormalised outputs of a multi-token call, normalised after
-    // the recurrence (one wave per token) so the RMSNorm reduction is not on
-    // the token chain.
-    constexpr int NRB = TMAX <= 8 ? 2 : 1;
-    constexpr bool DEFER = TMAX > 1;
-    __shared__ TokenLds<DK, DV> tok[TMAX];
-    __shared__ float4 red[NRB][G::NW][2][G::CG];
-    __shared__ float4 obuf[DEFER ? TMAX : 1][G::CG];
-
+    if (!it.run) return;
     const int tid = threadIdx.x;
     const int lane = tid % kWave, wave = tid / kWave;
     const int cg = tid % G::CG, rg = tid / G::CG;
-    const int b = blockIdx.x / p.H, h = blockIdx.x % p.H;
-
-    int T = 1;
-    if (VERIFY) T = p.draft_len ? min(max(p.draft_len[b], 0), p.T) : p.T;
-    const int slot = p.slot_idx[b];
-    const int y_rows = VERIFY ? p.T : 1;
-    float *yb = p.y + ((size_t)b * y_rows * p.H + h) * DV;   // token t at + t*H*DV
-    const bool bad = slot < 0 || slot >= p.n_slots;
-    if (bad && slot != -1 && tid == 0) flag_error(p.err_flag);
-    // zero the outputs of tokens this workgroup will not produce
-    for (int t = bad ? 0 : T; t < y_rows; ++t)
-        for (int j = tid; j < DV; j += NT) yb[(size_t)t * p.H * DV + j] = 0.f;
-    if (bad || T == 0) return;
-
-    // 1. fetch the small operands first, then issue the single read of the
-    //    state tile, so the conv/gate math below waits only for the former
-    constexpr int TPW = (TMAX + G::NW - 1) / G::NW;
-    ConvRegs<DK, DV, NT, Tin, TMAX> cr;
-    conv_fetch<DK, DV, NT, Tin, TMAX, VERIFY>(p, tid, b, h, slot, T, cr);
-    PrepRegs<DK, DV, Tin, TPW> pr;
-    prep_fetch<DK, DV, G::NW, Tin, TPW, VERIFY>(p, wave, lane, b, h, T, pr);
-    float *S = p.state + ((size_t)slot * p.H + h) * DK * DV;
-    float4 s[G::RPT];
+    const int slot = it.slot, T = it.T;
+    conv_fetch<DK, DV, NT, Tin, TMAX, VERIFY>(p, tid, it.b, it.h, slot, T, it.cr);
+    prep_fetch<DK, DV, G::NW, Tin, RecItem<DK, DV, NT, Tin, TMAX>::TPW, VERIFY>(p, wave, lane, it.b, it.h, T, it.pr);
+    it.S = p.state + ((size_t)slot * p.H + it.h) * DK * DV;
+    // the small operands are requested before the state tile (loads return
+    // in issue order, so the conv/gate math then waits only for them)
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < G::RPT; ++i) s[i] = load_state4<STREAM>(S + (size_t)(rg + G::RG * i) * DV + 4 * cg);
+    for (int i = 0; i < G::RPT; ++i) it.s[i] = load_state4<STREAM>(it.S + (size_t)(rg + G::RG * i) * DV + 4 * cg);
+    // and nothing that waits for them is scheduled above them
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// The computation of a fetched item (it.run must be true; uniform over the
+// workgroup): conv, norms and gates, the recurrence with the state in
+// registers, the outputs and the state write.
+template <int DK, int DV, int NT, typename Tin, int TMAX, int MODE, bool STREAM>
+__device__ __forceinline__ void rec_run(const RecParams &p, RecItem<DK, DV, NT, Tin, TMAX> &it,
+                                        RecShared<DK, DV, NT, TMAX> &sh) {
+    using G = RecGeo<DK, DV, NT>;
+    using SH = RecShared<DK, DV, NT, TMAX>;
+    constexpr bool VERIFY = MODE != kDecode;
+    constexpr bool DELTA = MODE == kVerifyDelta;
+    constexpr int TPW = RecItem<DK, DV, NT, Tin, TMAX>::TPW;
+    TokenLds<DK, DV> *tok = sh.tok;
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave, wave = tid / kWave;
+    const int cg = tid % G::CG, rg = tid / G::CG;
+    const int b = it.b, h = it.h, T = it.T, slot = it.slot;
+    float *yb = it.yb;
+    float4 *s = it.s;
 
     // 2. conv (+ window update / window snapshots)
-    conv_compute<DK, DV, NT, Tin, TMAX, VERIFY, DELTA>(p, tid, b, h, slot, T, cr, tok);
+    conv_compute<DK, DV, NT, Tin, TMAX, VERIFY, DELTA>(p, tid, b, h, slot, T, it.cr, tok);
     __syncthreads();
     // 3. norms and gates, one wave per token
 #pragma unroll
     for (int j = 0; j < TPW; ++j) {
         const int t = wave + G::NW * j;
-        if (t < T) prep_token<DK, DV, Tin, TPW>(p, lane, j, pr, tok[t]);
+        if (t < T) prep_token<DK, DV, Tin, TPW>(p, lane, j, it.pr, tok[t]);
     }
     __syncthreads();
     // delta mode: alpha and k^ of every token into its record
@@ -363,13 +441,13 @@ __global__ __launch_bounds__(NT) void kda_recurrent_kernel(RecParams p) {
             pq.x += __shfl_xor(pq.x, m, kWave); pq.y += __shfl_xor(pq.y, m, kWave);
             pq.z += __shfl_xor(pq.z, m, kWave); pq.w += __shfl_xor(pq.w, m, kWave);
         }
-        const int rb = NRB == 2 ? (t & 1) : 0;
-        if (lane < G::CG) { red[rb][wave][0][cg] = u; red[rb][wave][1][cg] = pq; }
+        const int rb = SH::NRB == 2 ? (t & 1) : 0;
+        if (lane < G::CG) { sh.red[rb][wave][0][cg] = u; sh.red[rb][wave][1][cg] = pq; }
         __syncthreads();
-        float4 U = red[rb][0][0][cg], P = red[rb][0][1][cg];
+        float4 U = sh.red[rb][0][0][cg], P = sh.red[rb][0][1][cg];
 #pragma unroll
         for (int w = 1; w < G::NW; ++w) {
-            const float4 a = red[rb][w][0][cg], c = red[rb][w][1][cg];
+            const float4 a = sh.red[rb][w][0][cg], c = sh.red[rb][w][1][cg];
             U.x += a.x; U.y += a.y; U.z += a.z; U.w += a.w;
             P.x += c.x; P.y += c.y; P.z += c.z; P.w += c.w;
         }
@@ -399,24 +477,39 @@ __global__ __launch_bounds__(NT) void kda_recurrent_kernel(RecParams p) {
             const float kq = tk.kq;
             const float4 o = make_float4(fmaf(kq, d.x, P.x), fmaf(kq, d.y, P.y),
                                          fmaf(kq, d.z, P.z), fmaf(kq, d.w, P.w));
-            if (DEFER) obuf[t][cg] = o;
+            if (SH::DEFER) sh.obuf[t][cg] = o;
             else output_row<DV>(p, o, tk.gate, cg, yb);
         }
-        if (NRB == 1) __syncthreads();   // red[] is rewritten by the next token
+        if (SH::NRB == 1) __syncthreads();   // red[] is rewritten by the next token
     }
     // RMSNorm + gate of the deferred outputs: token t by lanes 0 .. CG-1 of
     // wave t % NW, the lanes and reduction order of the inline form
-    if (DEFER) {
+    if (SH::DEFER) {
         __syncthreads();
         for (int t = wave; t < T; t += G::NW)
-            if (lane < G::CG) output_row<DV>(p, obuf[t][lane], tok[t].gate, lane, yb + (size_t)t * p.H * DV);
+            if (lane < G::CG) output_row<DV>(p, sh.obuf[t][lane], tok[t].gate, lane, yb + (size_t)t * p.H * DV);
     }
 
     // 5. the single write of the state tile (decode only: verify leaves S0)
     if (!VERIFY) {
 #pragma unroll
-        for (int i = 0; i < G::RPT; ++i) store_state4<STREAM>(S + (size_t)(rg + G::RG * i) * DV + 4 * cg, s[i]);
+        for (int i = 0; i < G::RPT; ++i) store_state4<STREAM>(it.S + (size_t)(rg + G::RG * i) * DV + 4 * cg, s[i]);
     }
+}
+
+// One workgroup per (sequence, head) item.  Decode is held to three
+// workgroups per CU (its registers would allow four): with four, the
+// batch-64 step measured about 2% slower (more tiles contending for the same
+// bandwidth), while single-round launches gain nothing from the fourth.
+template <int DK, int DV, int NT, typename Tin, int TMAX, int MODE, bool STREAM>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, MODE == kDecode ? 3 : 8)))
+void kda_recurrent_kernel(RecParams p) {
+    __shared__ RecShared<DK, DV, NT, TMAX> sh;
+    RecItem<DK, DV, NT, Tin, TMAX> it;
+    rec_resolve<DK, DV, NT, Tin, TMAX, MODE>(p, blockIdx.x, it);
+    rec_side<DK, DV, NT, Tin, TMAX, MODE>(p, it);
+    rec_loads<DK, DV, NT, Tin, TMAX, MODE, STREAM>(p, it);
+    if (it.run) rec_run<DK, DV, NT, Tin, TMAX, MODE, STREAM>(p, it, sh);
 }
 
 // Commit: copy the snapshot of the last accepted token into the live slot.
