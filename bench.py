@@ -339,7 +339,41 @@ def extras(torch, api, synth, layer, cache, step_inputs, y, slots, B, H, dk, dv,
     ex["spec_step_b16_t8"] = {"snapshots_us": (sv + sc) * 1e6, "deltas_us": (svd + scd) * 1e6}
     ex["chunk_prefill_t32k"] = prefill_extra(torch, api, synth, stream)
     ex["decode_b1"] = decode_b1_extra(torch, api, synth)
+    ex["mixed_batch"] = mixed_extra(torch, api, synth)
     return ex
+
+
+def mixed_extra(torch, api, synth, prompt=4096, n_one=64):
+    """A mixed prefill + decode batch in one kda_chunk_prefill call: one
+    `prompt`-token sequence and `n_one` one-token (decode) rows, H=32, d=128;
+    beside the prompt alone and the one-token rows alone (same call), and the
+    one-token rows through kda_decode."""
+    dev = "cuda:0"
+    H, dk, dv = 32, 128, 128
+    g = synth.rng(106)
+    p = synth.layer_params(g, H, dk, dv)
+    td = lambda a, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(dt)
+    layer = api.Layer(td(p["A"]), td(p["conv_wt"]), td(p["norm_w"]))
+    stream = torch.cuda.current_stream()
+    out = {}
+    for name, lens in (("prompt_plus_decode_rows", [prompt] + [1] * n_one), ("prompt_only", [prompt]),
+                       ("decode_rows_only", [1] * n_one)):
+        N, total = len(lens), sum(lens)
+        cache = api.Cache(torch.zeros((N, H, dk, dv), device=dev),
+                          torch.zeros((N, H, 3, 2 * dk + dv), dtype=torch.bfloat16, device=dev))
+        inp = synth.token_inputs(g, (total,), H, dk, dv, "bf16")
+        I = api.Inputs(*(td(inp[k], torch.bfloat16) for k in ("x_q", "x_k", "x_v", "g", "b", "z")))
+        y = torch.empty((total, H, dv), device=dev)
+        sl = torch.arange(N, dtype=torch.int32, device=dev)
+        cu = td(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32), torch.int32)
+        ws = torch.empty(max(api.kda_chunk_prefill_workspace_bytes(layer, total, N), 16), dtype=torch.uint8, device=dev)
+        out[name + "_us"] = timed(torch, stream, lambda: api.kda_chunk_prefill(layer, cache, sl, cu, I, y, ws), 10) * 1e6
+        if name == "decode_rows_only":
+            yd = torch.empty((N, H, dv), device=dev)
+            out["decode_rows_via_kda_decode_us"] = timed(
+                torch, stream, lambda: api.kda_decode(layer, cache, sl, I, yd), 10) * 1e6
+    out["config"] = f"{prompt}-token prompt + {n_one} one-token rows, H={H}, d={dk}, bf16"
+    return out
 
 
 def decode_b1_extra(torch, api, synth, steps=1000, graph_steps=100):

@@ -224,7 +224,10 @@ kda_status kda_spec_commit_delta(const kda_layer *layer, const kda_cache *cache,
  *   inputs: total_T tokens; y [total_T, H, d_v] fp32.
  *   chunk: 64.  workspace: >= kda_chunk_prefill_workspace_bytes(...).
  * The state and window at slot_idx[s] are the start state (zero them for a
- * fresh sequence) and are replaced by the final ones.  total_T = 0 is
+ * fresh sequence) and are replaced by the final ones.  A batch may mix
+ * prompts with one-token (decode) rows: sequences of exactly one token take
+ * the decode kernel of kda_decode inside this call (bitwise the results of
+ * kda_decode on those rows), so a mixed prefill + decode batch is one call.  total_T = 0 is
  * allowed: inputs' pointers and y are then not read and may be NULL (the
  * dtype must still be valid); cu_seqlens is still checked.
  */

@@ -223,6 +223,10 @@ kda_status prefill_common(const kda_layer *layer, const kda_cache *cache, const 
     KDA_TRY(check_cache(cache));
     if (N_seq < 1 || total_T < 0 || chunk <= 0) return KDA_ERR_SHAPE;
     if (chunk != 64) return KDA_ERR_UNSUPPORTED;
+    // one-dimensional grids: heads x chunk slots, heads x column blocks x sequences
+    const size_t slots = (size_t)total_T / 64 + (size_t)N_seq;
+    if ((size_t)layer->H * slots > 0x7fffffffu || (size_t)layer->H * (layer->d_v / 16) * N_seq > 0x7fffffffu)
+        return KDA_ERR_SHAPE;
     // with no tokens the inputs and y are never read (and may be NULL)
     if (!inputs) return KDA_ERR_NULL;
     if (inputs->dtype != KDA_F32 && inputs->dtype != KDA_BF16) return KDA_ERR_DTYPE;

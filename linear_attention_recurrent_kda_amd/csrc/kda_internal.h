@@ -31,6 +31,12 @@ struct RecParams {
     const void *x_q, *x_k, *x_v, *g, *b, *z;
     float *y;
     int B, H, T;
+    // decode of the one-token sequences of a packed prefill call: sequence b
+    // is token row seq_start[b] (inputs and y); only sequences with
+    // seq_start[b + 1] - seq_start[b] == 1 are processed, and only when
+    // *seq_ok == 1 (null: plain decode)
+    const int32_t *seq_start;
+    const int32_t *seq_ok;
 };
 
 struct CommitParams {

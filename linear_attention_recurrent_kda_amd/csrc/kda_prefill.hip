@@ -35,7 +35,9 @@ constexpr float kLog2e = 1.4426950408889634f;
 // scan multiplies on MFMA are stored pre-split as bf16 pairs (hi = bf16(x),
 // lo = bf16(x - hi)), each matrix in MFMA operand order (opnd_off below).
 struct PrefillWs {
-    int32_t *meta;            // [0]: 1 if cu_seqlens is valid; [1 + s]: first chunk of s, s <= N
+    int32_t *meta;            // [0]: 1 if cu_seqlens is valid; [1 + s]: first chunk of s, s <= N;
+                              // [N + 2]: number of chunk-path sequences; [N + 3 + k]: the k-th;
+                              // [2N + 3]: number of one-token sequences (decode kernel)
     float *vv;                // [G, 64, H, d_v]  conv'd v, rows past a chunk's end unused
     uint16_t *Wn_hi, *Wn_lo;  // [G, H] x (64 x d_k)  -W
     uint16_t *Q_hi, *Q_lo;    // [G, H] x (64 x d_k)  Q^ e^G
@@ -68,7 +70,7 @@ static WsLayout ws_layout(int H, int dk, int dv, int total_T, int N_seq) {
     WsLayout l{};
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes); return o; };
-    l.meta = take(sizeof(int32_t) * (N_seq + 2));
+    l.meta = take(sizeof(int32_t) * (2 * (size_t)N_seq + 4));
     l.vv = take(4 * GH * kChunk * dv);
     l.Wn_hi = take(2 * GH * kChunk * dk);
     l.Wn_lo = take(2 * GH * kChunk * dk);
@@ -102,24 +104,59 @@ __device__ __forceinline__ int upper_index(const int32_t *a, int n, int v) {
 __device__ __forceinline__ bool slot_ok(int slot, int n_slots) { return slot >= 0 && slot < n_slots; }
 
 // ---------------------------------------------------------------------------
-// meta: validate cu_seqlens and count chunks (one lane; N_seq is small)
+// meta: one wave.  Validates cu_seqlens, gives each sequence that takes the
+// chunk path (two or more tokens and a valid slot) its run of chunk slots,
+// and lists those sequences in order, so the intra and scan grids can put
+// all real work ahead of the workgroups that only exit.  One-token
+// sequences take the decode kernel; empty sequences and padding rows take
+// nothing.  64 sequences per step, prefix sums across the wave.
 // ---------------------------------------------------------------------------
-__global__ void kda_prefill_meta_kernel(PrefillParams p, PrefillWs ws) {
-    if (threadIdx.x != 0) return;
-    const int N = p.N_seq;
-    bool ok = p.cu_seqlens[0] == 0 && p.cu_seqlens[N] == p.total_T;
-    for (int s = 0; s < N && ok; ++s) ok = p.cu_seqlens[s + 1] >= p.cu_seqlens[s];
-    int32_t *cs = ws.meta + 1;
-    cs[0] = 0;
-    for (int s = 0; s < N; ++s) {
-        const int len = ok ? p.cu_seqlens[s + 1] - p.cu_seqlens[s] : 0;
-        cs[s + 1] = cs[s] + (len + kChunk - 1) / kChunk;
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1) {
+        const int u = __shfl_up(v, m, kWave);
+        if (lane >= m) v += u;
     }
-    ws.meta[0] = ok ? 1 : 0;
-    if (!ok) flag_error(p.err_flag);
-    for (int s = 0; s < N && ok; ++s) {
-        const int sl = p.slot_idx[s];
-        if (sl != -1 && !slot_ok(sl, p.n_slots)) flag_error(p.err_flag);
+    return v;
+}
+
+__global__ __launch_bounds__(64) void kda_prefill_meta_kernel(PrefillParams p, PrefillWs ws) {
+    const int lane = threadIdx.x, N = p.N_seq;
+    int32_t *cs = ws.meta + 1;
+    int32_t *list = ws.meta + N + 3;
+    bool ok = true, bad_slot = false;
+    int chunks = 0, longs = 0, ones = 0;
+    if (lane == 0) cs[0] = 0;
+    for (int base = 0; base < N; base += kWave) {
+        const int s = base + lane;
+        int nch = 0, isl = 0;
+        if (s < N) {
+            const int a0 = p.cu_seqlens[s], a1 = p.cu_seqlens[s + 1];
+            ok = ok && a1 >= a0;
+            const int sl = p.slot_idx[s];
+            bad_slot = bad_slot || (sl != -1 && !slot_ok(sl, p.n_slots));
+            if (a1 - a0 >= 2 && slot_ok(sl, p.n_slots)) {
+                nch = (a1 - a0 + kChunk - 1) / kChunk;
+                isl = 1;
+            }
+            ones += a1 - a0 == 1 && slot_ok(sl, p.n_slots);
+        }
+        const int ic = wave_incl_scan(nch, lane), il = wave_incl_scan(isl, lane);
+        if (s < N) {
+            cs[s + 1] = chunks + ic;
+            if (isl) list[longs + il - 1] = s;
+        }
+        chunks += __shfl(ic, kWave - 1, kWave);
+        longs += __shfl(il, kWave - 1, kWave);
+    }
+    ok = __all(ok) && p.cu_seqlens[0] == 0 && p.cu_seqlens[N] == p.total_T;
+    bad_slot = __any(bad_slot);
+    ones = wave_incl_scan(ones, lane);
+    if (lane == kWave - 1) ws.meta[2 * N + 3] = ok ? ones : 0;
+    if (lane == 0) {
+        ws.meta[0] = ok ? 1 : 0;
+        ws.meta[N + 2] = ok ? longs : 0;
+        if (!ok || bad_slot) flag_error(p.err_flag);
     }
 }
 
@@ -333,13 +370,16 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
     __shared__ IntraLds<DK, DV> L;
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int lr = lane % 16, lk = lane / 16;
-    const int gidx = blockIdx.x, h = blockIdx.y, H = p.H;
+    // one-dimensional grid, heads fastest: every real chunk dispatches ahead
+    // of the chunk slots that only exit
+    const int H = p.H, h = (int)(blockIdx.x % (unsigned)H), gidx = (int)(blockIdx.x / (unsigned)H);
     if (ws.meta[0] != 1) return;
     const int32_t *cs = ws.meta + 1;
     if (gidx >= cs[p.N_seq]) return;
     const int s = upper_index(cs, p.N_seq + 1, gidx);
     const int slot = p.slot_idx[s];
     if (!slot_ok(slot, p.n_slots)) return;
+    if (p.cu_seqlens[s + 1] - p.cu_seqlens[s] == 1) return;   // a one-token sequence: decode kernel
     const int c = gidx - cs[s];
     const int t0 = p.cu_seqlens[s] + c * kChunk;
     const int n = min(kChunk, p.cu_seqlens[s + 1] - t0);
@@ -700,17 +740,26 @@ __global__ __launch_bounds__(kScanThreads) void kda_prefill_scan_kernel(PrefillP
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int team = wave / 4, w4 = wave % 4;
     const int lr = lane % 16, lk = lane / 16;
-    const int s = blockIdx.x, h = blockIdx.y, j0 = blockIdx.z * CB, H = p.H;
+    // one-dimensional grid: workgroup x = h + H * column block + NX * k for
+    // the k-th chunk-path sequence, so all real work dispatches ahead of the
+    // workgroups that only exit, and the column blocks of a head share an
+    // XCD (workgroups go to XCDs round-robin; H a multiple of 8)
+    const int H = p.H, NX = H * (DV / CB);
+    const int xb = (int)(blockIdx.x % (unsigned)NX), k = (int)(blockIdx.x / (unsigned)NX);
+    const int h = xb % H, zb = xb / H, j0 = zb * CB;
     if (ws.meta[0] != 1) return;
+    if (k >= ws.meta[p.N_seq + 2]) return;
+    const int s = ws.meta[p.N_seq + 3 + k];
     const int slot = p.slot_idx[s];
     if (!slot_ok(slot, p.n_slots)) return;
     const int32_t *cs = ws.meta + 1;
     const int g0 = cs[s], nch = cs[s + 1] - cs[s];
     const int len = p.cu_seqlens[s + 1] - p.cu_seqlens[s];
+    if (len == 1) return;   // a one-token sequence: decode kernel (state, window, output)
 
     // the window after the sequence: the last 3 raw inputs (older rows from
     // the previous window when len < 3); read everything, then write
-    if (blockIdx.z == 0) {
+    if (zb == 0) {
         Tin *win = static_cast<Tin *>(p.window) + ((size_t)slot * H + h) * 3 * CH;
         const int ch = tid;
         Tin nv[3];
@@ -869,7 +918,7 @@ __global__ __launch_bounds__(kScanThreads) void kda_prefill_scan_kernel(PrefillP
                     const int nxt = (c + 1) & 1;
                     for (int e = tid; e < DK * CB; e += kScanThreads)
                         D[(e / CB) * DV + j0 + e % CB] = S[nxt][e / CB][e % CB];
-                } else if (ck != -1 && tid == 0 && blockIdx.z == 0) {
+                } else if (ck != -1 && tid == 0 && zb == 0) {
                     flag_error(p.err_flag);
                 }
             }
@@ -907,14 +956,20 @@ __global__ __launch_bounds__(256) void kda_prefill_norm_kernel(PrefillParams p, 
     const int H = p.H, c0 = 4 * (lane % LPR);
     const size_t nrows = (size_t)p.total_T * H;
     const bool valid = ws.meta[0] == 1;
+    const bool ones = ws.meta[2 * p.N_seq + 3] > 0;   // any rows already final
 #pragma unroll 2
     for (int pass = 0; pass < kNormRows / RPB; ++pass) {
         const size_t r = (size_t)blockIdx.x * kNormRows + pass * RPB + wave * RPW + lane / LPR;
         const bool in = r < nrows;
         const size_t rr = in ? r : 0;
         const int t = (int)(rr / H), h = (int)(rr % H);
-        bool live = in && valid;
-        if (live) live = slot_ok(p.slot_idx[upper_index(p.cu_seqlens, p.N_seq + 1, t)], p.n_slots);
+        bool live = in && valid, done = false;
+        if (live) {
+            const int sq = upper_index(p.cu_seqlens, p.N_seq + 1, t);
+            live = slot_ok(p.slot_idx[sq], p.n_slots);
+            // rows of one-token sequences are already final (decode kernel)
+            if (ones) done = live && p.cu_seqlens[sq + 1] - p.cu_seqlens[sq] == 1;
+        }
         float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
         if (in) o = *reinterpret_cast<const float4 *>(p.y + rr * DV + c0);
         float ss = o.x * o.x;
@@ -942,7 +997,7 @@ __global__ __launch_bounds__(256) void kda_prefill_norm_kernel(PrefillParams p, 
         out.z = o.z * rn * (w.z * sigmoid(zf[2]));
         out.w = o.w * rn * (w.w * sigmoid(zf[3]));
         if (!live) out = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (in) *reinterpret_cast<float4 *>(p.y + rr * DV + c0) = out;
+        if (in && !done) *reinterpret_cast<float4 *>(p.y + rr * DV + c0) = out;
     }
 }
 
@@ -970,12 +1025,29 @@ static kda_status launch_prefill_typed(const PrefillParams &p, hipStream_t strea
 
     hipLaunchKernelGGL(kda_prefill_meta_kernel, dim3(1), dim3(64), 0, stream, p, ws);
     if (p.total_T > 0) {
-        hipLaunchKernelGGL((kda_prefill_intra_kernel<DK, DV, Tin>), dim3((unsigned)ws.G_max, (unsigned)p.H),
+        // one-token sequences (decode rows of a mixed batch) take the decode
+        // kernel: one state read and write instead of a chunk's workspace
+        // round trip; the chunk kernels below skip them
+        RecParams r{};
+        r.A = p.A; r.conv_wt = p.conv_wt; r.norm_w = p.norm_w;
+        r.q_scale = p.q_scale; r.l2_eps = p.l2_eps; r.rms_eps = p.rms_eps;
+        r.silu = p.silu;
+        r.state = p.state; r.window = p.window; r.n_slots = p.n_slots;
+        r.slot_idx = p.slot_idx;
+        r.x_q = p.x_q; r.x_k = p.x_k; r.x_v = p.x_v; r.g = p.g; r.b = p.b; r.z = p.z;
+        r.y = p.y;
+        r.B = p.N_seq; r.H = p.H; r.T = 1;
+        r.seq_start = p.cu_seqlens;
+        r.seq_ok = ws.meta;
+        const kda_status st = launch_recurrent(r, DK, DV, sizeof(Tin) == 2 ? KDA_BF16 : KDA_F32, RecKind::decode,
+                                               stream);
+        if (st != KDA_OK) return st;
+        hipLaunchKernelGGL((kda_prefill_intra_kernel<DK, DV, Tin>), dim3((unsigned)((size_t)p.H * ws.G_max)),
                            dim3(kIntraThreads), 0, stream, p, ws);
     }
     hipLaunchKernelGGL((kda_prefill_scan_kernel<DK, DV, Tin>),
-                       dim3((unsigned)p.N_seq, (unsigned)p.H, (unsigned)(DV / kColBlock)), dim3(kScanThreads), 0,
-                       stream, p, ws);
+                       dim3((unsigned)((size_t)p.H * (DV / kColBlock) * p.N_seq)), dim3(kScanThreads), 0, stream, p,
+                       ws);
     if (p.total_T > 0) {
         const size_t rows = (size_t)p.total_T * p.H;
         hipLaunchKernelGGL((kda_prefill_norm_kernel<DV, Tin>), dim3((unsigned)((rows + kNormRows - 1) / kNormRows)),

@@ -124,7 +124,7 @@ __device__ __forceinline__ gptr<T> uniform_ptr(const T *ptr) {
 // valid element) so the compiler issues them back to back, ahead of the state
 // tile, without branches that would force waits.  Requires T >= 1.
 template <int DK, int DV, int NT, typename Tin, int TMAX, bool VERIFY>
-__device__ __forceinline__ void conv_fetch(const RecParams &p, int tid, int b, int h, int slot, int T,
+__device__ __forceinline__ void conv_fetch(const RecParams &p, int tid, int b, int row, int h, int slot, int T,
                                            ConvRegs<DK, DV, NT, Tin, TMAX> &cr) {
     constexpr int CH = 2 * DK + DV;
     const Tin *win = static_cast<const Tin *>(p.window) + ((size_t)slot * p.H + h) * 3 * CH;
@@ -149,7 +149,7 @@ __device__ __forceinline__ void conv_fetch(const RecParams &p, int tid, int b, i
 #pragma unroll
         for (int t = 0; t < TMAX; ++t) {
             const int tt = min(t, T - 1);
-            const size_t n = VERIFY ? (size_t)b * p.T + tt : (size_t)b;
+            const size_t n = VERIFY ? (size_t)b * p.T + tt : (size_t)row;
             cr.x[k][3 + t] = src[(n * p.H + h) * stride + off];
         }
     }
@@ -210,7 +210,7 @@ struct PrepRegs {
 };
 
 template <int DK, int DV, int NW, typename Tin, int TPW, bool VERIFY>
-__device__ __forceinline__ void prep_fetch(const RecParams &p, int wave, int lane, int b, int h, int T,
+__device__ __forceinline__ void prep_fetch(const RecParams &p, int wave, int lane, int b, int row, int h, int T,
                                            PrepRegs<DK, DV, Tin, TPW> &pr) {
 #pragma unroll
     for (int e = 0; e < pr.EK; ++e) pr.A[e] = p.A[h * DK + lane + kWave * e];
@@ -219,7 +219,7 @@ __device__ __forceinline__ void prep_fetch(const RecParams &p, int wave, int lan
 #pragma unroll
     for (int j = 0; j < TPW; ++j) {
         const int t = min(wave + NW * j, T - 1);
-        const size_t n = VERIFY ? (size_t)b * p.T + t : (size_t)b;
+        const size_t n = VERIFY ? (size_t)b * p.T + t : (size_t)row;
         const Tin *g = static_cast<const Tin *>(p.g) + (n * p.H + h) * DK;
         const Tin *z = static_cast<const Tin *>(p.z) + (n * p.H + h) * DV;
 #pragma unroll
@@ -313,7 +313,9 @@ struct RecItem {
     using G = RecGeo<DK, DV, NT>;
     static constexpr int TPW = (TMAX + G::NW - 1) / G::NW;
     int b, h, T, slot;
+    int row;       // input / output row of a decode item
     bool run;
+    bool routed;   // a one-token row of a packed prefill call
     float *yb, *S;
     ConvRegs<DK, DV, NT, Tin, TMAX> cr;
     PrepRegs<DK, DV, Tin, TPW> pr;
@@ -332,9 +334,18 @@ __device__ __forceinline__ void rec_resolve(const RecParams &p, int item, RecIte
     if (VERIFY) T = p.draft_len ? min(max(p.draft_len[b], 0), p.T) : p.T;
     it.T = T;
     it.slot = p.slot_idx[b];
+    int row = b;
+    bool take = true;
+    it.routed = !VERIFY && p.seq_start != nullptr;
+    if (it.routed) {
+        const int a0 = p.seq_start[b];
+        row = a0;
+        take = *p.seq_ok == 1 && p.seq_start[b + 1] - a0 == 1;
+    }
+    it.row = row;
     const int y_rows = VERIFY ? p.T : 1;
-    it.yb = p.y + ((size_t)b * y_rows * p.H + h) * DV;   // token t at + t*H*DV
-    it.run = !(it.slot < 0 || it.slot >= p.n_slots || T == 0);
+    it.yb = p.y + ((size_t)row * y_rows * p.H + h) * DV;   // token t at + t*H*DV
+    it.run = take && !(it.slot < 0 || it.slot >= p.n_slots || T == 0);
 }
 
 // Rows that will not be computed (padding, a bad slot, no draft tokens):
@@ -343,6 +354,8 @@ __device__ __forceinline__ void rec_resolve(const RecParams &p, int item, RecIte
 template <int DK, int DV, int NT, typename Tin, int TMAX, int MODE>
 __device__ __forceinline__ void rec_side(const RecParams &p, const RecItem<DK, DV, NT, Tin, TMAX> &it) {
     constexpr bool VERIFY = MODE != kDecode;
+    // the prefill call flags bad slots and writes every row it does not compute
+    if (it.routed) return;
     const int tid = threadIdx.x;
     const bool bad = it.slot < 0 || it.slot >= p.n_slots;
     if (bad && it.slot != -1 && tid == 0) flag_error(p.err_flag);
@@ -363,8 +376,9 @@ __device__ __forceinline__ void rec_loads(const RecParams &p, RecItem<DK, DV, NT
     const int lane = tid % kWave, wave = tid / kWave;
     const int cg = tid % G::CG, rg = tid / G::CG;
     const int slot = it.slot, T = it.T;
-    conv_fetch<DK, DV, NT, Tin, TMAX, VERIFY>(p, tid, it.b, it.h, slot, T, it.cr);
-    prep_fetch<DK, DV, G::NW, Tin, RecItem<DK, DV, NT, Tin, TMAX>::TPW, VERIFY>(p, wave, lane, it.b, it.h, T, it.pr);
+    conv_fetch<DK, DV, NT, Tin, TMAX, VERIFY>(p, tid, it.b, it.row, it.h, slot, T, it.cr);
+    prep_fetch<DK, DV, G::NW, Tin, RecItem<DK, DV, NT, Tin, TMAX>::TPW, VERIFY>(p, wave, lane, it.b, it.row, it.h, T,
+                                                                              it.pr);
     it.S = p.state + ((size_t)slot * p.H + it.h) * DK * DV;
     // the small operands are requested before the state tile (loads return
     // in issue order, so the conv/gate math then waits only for them)

@@ -383,3 +383,40 @@ def test_prefill_checkpoint_bad_slot_flags_error():
                         *(inp[k][None] for k in KEYS), y_tokens=0, snapshots=True)
     assert state_rel_err(host(cache.state[2:3]), o2["snap_state"][:, 63]) < 1e-4
     assert state_rel_err(host(cache.state[3:4]), o2["snap_state"][:, 191]) < 1e-4
+
+
+def test_mixed_batch_one_token_rows_equal_decode_bitwise():
+    """A packed batch mixing prompts and one-token (decode) rows: the
+    one-token sequences take the decode kernel inside kda_chunk_prefill, so
+    their outputs, states and windows equal a kda_decode call on the same
+    rows bit for bit; the longer sequences match the oracle."""
+    g = synth.rng(1400)
+    H, dk, dv = 4, 128, 128
+    params = synth.layer_params(g, H, dk, dv)
+    dl, ol = layer_pair(params)
+    lens = [300, 1, 1, 5, 0, 1, 70]
+    N, total = len(lens), sum(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    inp = synth.token_inputs(g, (total,), H, dk, dv, "bf16")
+    slots = g.permutation(2 * N)[:N].astype(np.int32)
+    cache = new_cache(2 * N, H, dk, dv, "bf16", fill_seed=14)
+    ref = api.Cache(cache.state.clone(), cache.conv_state.clone(), torch.zeros_like(cache.err_flag))
+    s0, w0 = host(cache.state[torch.from_numpy(slots).long().to(DEV)]), host(cache.conv_state[torch.from_numpy(slots).long().to(DEV)])
+    y, _ = run_prefill(dl, cache, slots, lens, inp, "bf16")
+    assert cache.err_flag.item() == 0
+    one = [s for s in range(N) if lens[s] == 1]
+    rows = cu[one]
+    yd = torch.empty((len(one), H, dv), device=DEV)
+    api.kda_decode(dl, ref, torch.from_numpy(slots[one]).to(DEV), dev_inputs({k: v[rows] for k, v in inp.items()}, "bf16"), yd)
+    torch.cuda.synchronize()
+    assert np.array_equal(y[rows], host(yd))
+    st = torch.from_numpy(slots[one]).long().to(DEV)
+    assert torch.equal(cache.state[st], ref.state[st])
+    assert torch.equal(cache.conv_state[st], ref.conv_state[st])
+    for s in (0, 3, 6):
+        o = oracle_seq(ol, s0[s], w0[s], inp, cu[s], cu[s + 1])
+        check_tokens(y[cu[s]:cu[s + 1]], o["y"][0])
+        assert state_rel_err(host(cache.state[int(slots[s]):int(slots[s]) + 1]), o["state"]) < 1e-4
+    # the empty sequence's slot is untouched
+    e = int(slots[4])
+    assert torch.equal(cache.state[e], ref.state[e])
