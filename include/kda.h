@@ -78,7 +78,10 @@ typedef enum kda_dtype {
                                 (many layers, large batches); slower when they
                                 do (a 128 MiB working set re-used call after
                                 call fits the 256 MB Infinity Cache).  Results
-                                are bitwise identical either way.              */
+                                are bitwise identical either way.  Without the
+                                flag, kda_decode streams by itself when a call
+                                touches more than 256 MiB of state
+                                (B * H * d_k * d_v * 4 bytes).                 */
 
 /* Parameters of one KDA layer (device pointers, fp32). */
 typedef struct kda_layer {

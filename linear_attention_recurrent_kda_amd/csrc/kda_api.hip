@@ -18,6 +18,9 @@ bool finite_nonneg(float x) { return isfinite(x) && x >= 0.f; }
 
 size_t elem_size(kda_dtype dt) { return dt == KDA_BF16 ? 2 : 4; }
 
+// kda_decode streams its state traffic above this many state bytes per call
+constexpr size_t kStreamAutoBytes = (size_t)256 << 20;
+
 kda_status check_layer(const kda_layer *L) {
     if (!L) return KDA_ERR_NULL;
     if (!L->A || !L->conv_wt || !L->norm_w) return KDA_ERR_NULL;
@@ -87,6 +90,10 @@ KDA_EXPORT kda_status kda_decode(const kda_layer *layer, const kda_cache *cache,
     p.slot_idx = slot_idx;
     p.B = B;
     p.T = 1;
+    // a call whose states exceed the 256 MB Infinity Cache cannot find them
+    // cached on its next call: stream them (measured faster from 384 MiB up,
+    // slower at 256 MiB and below)
+    if ((size_t)B * layer->H * layer->d_k * layer->d_v * sizeof(float) > kStreamAutoBytes) p.stream_state = 1;
     return launch_recurrent(p, layer->d_k, layer->d_v, inputs->dtype, RecKind::decode,
                             static_cast<hipStream_t>(hip_stream));
 }
