@@ -522,9 +522,25 @@ def cpu_baseline(synth, p, inp, B, H, dk, dv):
         o = kda_oracle.run(ol, st, win, tb["x_q"], tb["x_k"], tb["x_v"], tb["g"], tb["b"], tb["z"])
         el += time.perf_counter() - t0
         st, win, runs = o["state"], o["window"], runs + 1
+    # the same oracle on one core, over a quarter of the sequences
+    q = max(B // 4, 1)
+    sub = {k: np.ascontiguousarray(v[:q]) for k, v in tb.items()}
+    t0 = time.perf_counter()
+    kda_oracle.run(ol, st[:q], win[:q], sub["x_q"], sub["x_k"], sub["x_v"], sub["g"], sub["b"], sub["z"],
+                   n_threads=1)
+    el1 = time.perf_counter() - t0
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": B * H * n * runs / el, "unit": "token·heads/s", "cores": cores, "kind": "oracle",
             "sample": f"decode_b64: {runs} x {n} steps x {B} sequences x {H} heads (fp64, OpenMP "
-                      f"over sequence x head), {el:.1f} s"}
+                      f"over sequence x head), {el:.1f} s",
+            "one_core_value": q * H * n / el1,
+            "one_core_sample": f"{n} steps x {q} sequences x {H} heads on one thread, {el1:.1f} s",
+            "cpu_model": model}
 
 
 if __name__ == "__main__":
