@@ -309,7 +309,7 @@ def kda_chunk_prefill_workspace_bytes(layer: Layer, total_T: int, N_seq: int, ch
     return int(_lib.load().kda_chunk_prefill_workspace_bytes(ctypes.byref(L), total_T, N_seq, chunk))
 
 
-def _prefill_args(layer, cache, slot_idx, cu_seqlens, inputs, y, workspace, chunk):
+def _prefill_args(layer, cache, slot_idx, cu_seqlens, inputs, y, workspace, chunk, stream):
     _check(slot_idx, "slot_idx", torch.int32)
     _check(cu_seqlens, "cu_seqlens", torch.int32)
     N = slot_idx.numel()
@@ -325,6 +325,10 @@ def _prefill_args(layer, cache, slot_idx, cu_seqlens, inputs, y, workspace, chun
     need = int(_lib.load().kda_chunk_prefill_workspace_bytes(ctypes.byref(L), total_T, N, chunk))
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=y.device)
+        # allocated on the current stream, used on the launch stream: keep the
+        # caching allocator from handing it out again before the call is done
+        if stream is not None:
+            workspace.record_stream(stream)
     wp, wb = (None, 0) if workspace is None else (workspace.data_ptr(), workspace.numel() * workspace.element_size())
     return L, C, I, N, total_T, wp, wb, workspace
 
@@ -337,7 +341,7 @@ def kda_chunk_prefill(layer: Layer, cache: Cache, slot_idx: torch.Tensor, cu_seq
     y [total_T, H, d_v].  A workspace of the size query's bytes is allocated
     here (torch) when none is given."""
     L, C, I, N, total_T, wp, wb, keep = _prefill_args(layer, cache, slot_idx, cu_seqlens, inputs, y,
-                                                      workspace, chunk)
+                                                      workspace, chunk, stream)
     _raise("kda_chunk_prefill", _lib.load().kda_chunk_prefill(
         ctypes.byref(L), ctypes.byref(C), slot_idx.data_ptr(), cu_seqlens.data_ptr(), N, total_T,
         chunk, ctypes.byref(I), y.data_ptr(), wp, wb, _stream(stream)))
@@ -353,7 +357,7 @@ def kda_chunk_prefill_ckpt(layer: Layer, cache: Cache, slot_idx: torch.Tensor, c
     if ckpt_slots.dim() != 2 or ckpt_slots.shape[0] != slot_idx.numel():
         raise ValueError("ckpt_slots must be [N_seq, per_seq]")
     L, C, I, N, total_T, wp, wb, keep = _prefill_args(layer, cache, slot_idx, cu_seqlens, inputs, y,
-                                                      workspace, chunk)
+                                                      workspace, chunk, stream)
     _raise("kda_chunk_prefill_ckpt", _lib.load().kda_chunk_prefill_ckpt(
         ctypes.byref(L), ctypes.byref(C), slot_idx.data_ptr(), cu_seqlens.data_ptr(), N, total_T,
         chunk, ctypes.byref(I), y.data_ptr(), ckpt_slots.data_ptr(), int(ckpt_interval),
