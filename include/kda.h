@@ -41,6 +41,13 @@
  *     cache->err_flag is set, 1 is stored there.  Two rows of one call naming
  *     the same slot, or snapshot slots that alias live slots, are undefined.
  *   - Shapes: d_k, d_v in {64, 128}; conv_w = 4; H >= 1.
+ *   - Debug validation: with the environment variable KDA_CHECK=1 every call
+ *     first copies its slot tables (slot_idx, snap_slots, ckpt_slots) to the
+ *     host on hip_stream, synchronising it, and returns KDA_ERR_SHAPE for an
+ *     entry outside [-1, n_slots) or KDA_ERR_ALIAS when two non-negative
+ *     entries coincide (two rows on one slot; a snapshot or checkpoint slot
+ *     on a live slot or on another one); nothing is launched then.  Not for
+ *     serving or graph capture (it synchronises).
  */
 #ifndef KDA_H
 #define KDA_H
@@ -62,7 +69,8 @@ typedef enum kda_status {
     KDA_ERR_ALIGN = 4,       /* a pointer breaks the alignment rule            */
     KDA_ERR_UNSUPPORTED = 5, /* valid but not built (d_k, d_v, conv_w, flags)   */
     KDA_ERR_WORKSPACE = 6,   /* workspace smaller than the size query returns  */
-    KDA_ERR_LAUNCH = 7       /* the HIP launch reported an error               */
+    KDA_ERR_LAUNCH = 7,      /* the HIP launch reported an error               */
+    KDA_ERR_ALIAS = 8        /* KDA_CHECK only: slot tables alias (see below)  */
 } kda_status;
 
 typedef enum kda_dtype {

@@ -17,7 +17,7 @@ KDA_STREAM_STATE = 2
 
 STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE",
           4: "KDA_ERR_ALIGN", 5: "KDA_ERR_UNSUPPORTED", 6: "KDA_ERR_WORKSPACE",
-          7: "KDA_ERR_LAUNCH"}
+          7: "KDA_ERR_LAUNCH", 8: "KDA_ERR_ALIAS"}
 
 # every function include/kda.h declares
 EXPORTS = ("kda_decode", "kda_spec_verify", "kda_spec_commit", "kda_spec_delta_bytes",

@@ -3,6 +3,11 @@
 // launchers.  Validation runs before any HIP call, so every error status is
 // returned without touching the device.
 #include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <vector>
 
 #include "kda_internal.h"
 
@@ -53,6 +58,51 @@ kda_status check_inputs(const kda_inputs *in) {
     return KDA_OK;
 }
 
+// ---------------------------------------------------------------------------
+// KDA_CHECK=1: debug validation of the slot tables on the host.  The tables
+// are copied from the device on the call's stream (which is synchronised, so
+// this mode is for debugging, not for serving or graph capture) and checked
+// for what the kernels cannot detect: two rows naming the same slot, and
+// snapshot / checkpoint slots that alias a live slot or each other.
+// ---------------------------------------------------------------------------
+bool check_mode() {
+    const char *e = getenv("KDA_CHECK");
+    return e && strcmp(e, "0") != 0 && e[0] != '\0';
+}
+
+// Copy n int32 from the device; false on a HIP error.
+bool fetch_table(const int32_t *dev, size_t n, std::vector<int32_t> &host, hipStream_t stream) {
+    host.resize(n);
+    if (n == 0) return true;
+    if (hipMemcpyAsync(host.data(), dev, n * sizeof(int32_t), hipMemcpyDeviceToHost, stream) != hipSuccess)
+        return false;
+    return hipStreamSynchronize(stream) == hipSuccess;
+}
+
+// Every entry of `live` and `extra` in [-1, n_slots) (KDA_ERR_SHAPE), and the
+// non-negative entries distinct across both tables (KDA_ERR_ALIAS).
+kda_status check_distinct(const std::vector<int32_t> &live, const std::vector<int32_t> &extra, int n_slots) {
+    std::vector<int32_t> all;
+    all.reserve(live.size() + extra.size());
+    for (const auto *t : {&live, &extra})
+        for (int32_t v : *t) {
+            if (v < -1 || v >= n_slots) return KDA_ERR_SHAPE;
+            if (v >= 0) all.push_back(v);
+        }
+    std::sort(all.begin(), all.end());
+    return std::adjacent_find(all.begin(), all.end()) == all.end() ? KDA_OK : KDA_ERR_ALIAS;
+}
+
+kda_status debug_check(const int32_t *live_dev, size_t n_live, const int32_t *extra_dev, size_t n_extra,
+                       int n_slots, void *hip_stream) {
+    if (!check_mode()) return KDA_OK;
+    hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    std::vector<int32_t> live, extra;
+    if (!fetch_table(live_dev, n_live, live, st)) return KDA_ERR_LAUNCH;
+    if (extra_dev && !fetch_table(extra_dev, n_extra, extra, st)) return KDA_ERR_LAUNCH;
+    return check_distinct(live, extra, n_slots);
+}
+
 #define KDA_TRY(expr)                      \
     do {                                   \
         const kda_status st_ = (expr);     \
@@ -86,6 +136,7 @@ KDA_EXPORT kda_status kda_decode(const kda_layer *layer, const kda_cache *cache,
     if (!slot_idx || !y) return KDA_ERR_NULL;
     if (!aligned(slot_idx, 4)) return KDA_ERR_ALIGN;
     if (!aligned(y, 16)) return KDA_ERR_ALIGN;
+    KDA_TRY(debug_check(slot_idx, B, nullptr, 0, cache->n_slots, hip_stream));
     RecParams p = rec_params(layer, cache, inputs, y);
     p.slot_idx = slot_idx;
     p.B = B;
@@ -112,6 +163,7 @@ KDA_EXPORT kda_status kda_spec_verify(const kda_layer *layer, const kda_cache *c
     if (!aligned(slot_idx, 4) || !aligned(snap_slots, 4) || (draft_len && !aligned(draft_len, 4)))
         return KDA_ERR_ALIGN;
     if (!aligned(y, 16)) return KDA_ERR_ALIGN;
+    KDA_TRY(debug_check(slot_idx, B, snap_slots, (size_t)B * T, cache->n_slots, hip_stream));
     RecParams p = rec_params(layer, cache, inputs, y);
     p.slot_idx = slot_idx;
     p.snap_slots = snap_slots;
@@ -135,6 +187,7 @@ KDA_EXPORT kda_status kda_spec_commit(const kda_layer *layer, const kda_cache *c
     if (!slot_idx || !snap_slots || !accepted_len) return KDA_ERR_NULL;
     if (!aligned(slot_idx, 4) || !aligned(snap_slots, 4) || !aligned(accepted_len, 4))
         return KDA_ERR_ALIGN;
+    KDA_TRY(debug_check(slot_idx, B, snap_slots, (size_t)B * T, cache->n_slots, hip_stream));
     CommitParams p{};
     p.state = cache->state;
     p.window = cache->conv_state;
@@ -173,6 +226,7 @@ KDA_EXPORT kda_status kda_spec_verify_delta(const kda_layer *layer, const kda_ca
     if (!aligned(slot_idx, 4) || (draft_len && !aligned(draft_len, 4))) return KDA_ERR_ALIGN;
     if (!aligned(y, 16) || !aligned(delta, 16)) return KDA_ERR_ALIGN;
     if (delta_bytes < kda_spec_delta_bytes(layer, B, T, inputs->dtype)) return KDA_ERR_WORKSPACE;
+    KDA_TRY(debug_check(slot_idx, B, nullptr, 0, cache->n_slots, hip_stream));
     RecParams p = rec_params(layer, cache, inputs, y);
     p.slot_idx = slot_idx;
     p.draft_len = draft_len;
@@ -198,6 +252,7 @@ KDA_EXPORT kda_status kda_spec_commit_delta(const kda_layer *layer, const kda_ca
     if (!aligned(slot_idx, 4) || !aligned(accepted_len, 4)) return KDA_ERR_ALIGN;
     if (!aligned(delta, 16)) return KDA_ERR_ALIGN;
     if (delta_bytes < kda_spec_delta_bytes(layer, B, T, dtype)) return KDA_ERR_WORKSPACE;
+    KDA_TRY(debug_check(slot_idx, B, nullptr, 0, cache->n_slots, hip_stream));
     CommitDeltaParams p{};
     p.state = cache->state;
     p.window = cache->conv_state;
@@ -248,6 +303,8 @@ kda_status prefill_common(const kda_layer *layer, const kda_cache *cache, const 
     if (need && !workspace) return KDA_ERR_NULL;
     if (workspace_bytes < need) return KDA_ERR_WORKSPACE;
     if (workspace && !aligned(workspace, 16)) return KDA_ERR_ALIGN;
+    KDA_TRY(debug_check(slot_idx, N_seq, ckpt_slots, ckpt_slots ? (size_t)N_seq * ckpt_per_seq : 0,
+                        cache->n_slots, hip_stream));
     PrefillParams p{};
     p.A = layer->A; p.conv_wt = layer->conv_wt; p.norm_w = layer->norm_w;
     p.q_scale = layer->q_scale; p.l2_eps = layer->l2_eps; p.rms_eps = layer->rms_eps;
@@ -312,6 +369,8 @@ KDA_EXPORT const char *kda_status_string(kda_status s) {
         case KDA_ERR_UNSUPPORTED: return "unsupported configuration (d_k, d_v, conv_w, chunk or flags)";
         case KDA_ERR_WORKSPACE: return "workspace too small";
         case KDA_ERR_LAUNCH: return "kernel launch failed";
+        case KDA_ERR_ALIAS: return "slot tables alias (KDA_CHECK): two rows name the same slot, or "
+                                   "snapshot/checkpoint slots alias live slots or each other";
     }
     return "unknown status";
 }

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_function(lib):
 
 def test_abi_version_and_status_strings(lib):
     assert lib.kda_abi_version() == 1
-    for code in range(8):
+    for code in range(9):
         s = lib.kda_status_string(code)
         assert s and s != b"unknown status"
     assert lib.kda_status_string(99) == b"unknown status"
