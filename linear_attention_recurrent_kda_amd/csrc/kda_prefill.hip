@@ -221,6 +221,13 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
 __device__ __forceinline__ float silu_hw(float x) {
     return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x * kLog2e));
 }
+// 2^x by the hardware instruction, for the decay factors of the chunk
+// algebra: every argument is a difference of log2-decay prefix sums (<= 0,
+// or <= 60 on a diagonal tile that passed the span check), so the library
+// form's range handling is not needed (a result below 2^-126 flushes to 0,
+// far under the products it scales).
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // log2(alpha) = -e^A softplus(g) / ln 2, softplus(g) = max(g, 0) + ln(1 + e^-|g|)
 __device__ __forceinline__ float log2_alpha_hw(float ea, float g) {
     const float sp2 = fmaxf(g, 0.f) * kLog2e + __builtin_amdgcn_logf(1.0f + __builtin_amdgcn_exp2f(-fabsf(g) * kLog2e));
@@ -478,10 +485,10 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const float gr = L.G[r][c0 + e];
-                    const float et = exp2f(L.G[t][c0 + e] - gr);
+                    const float et = exp2_hw(L.G[t][c0 + e] - gr);
                     ka[e] *= et;
                     qa[e] *= et;
-                    kb[e] *= exp2f(gr - L.G[sr][c0 + e]);
+                    kb[e] *= exp2_hw(gr - L.G[sr][c0 + e]);
                 }
                 const Split8 b = split8(kb);
                 aA = mma3(split8(ka), b, aA);
@@ -496,7 +503,7 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int sv = r + 4 * lk + j;
-                    const float e = exp2f(fminf(gt - L.G[sv][ch], 0.f)) * L.K[sv][ch];
+                    const float e = exp2_hw(fminf(gt - L.G[sv][ch], 0.f)) * L.K[sv][ch];
                     da[j] = fmaf(kv, e, da[j]);
                     dp[j] = fmaf(qv, e, dp[j]);
                 }
@@ -535,7 +542,7 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
         bf16x8 hv, lv;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float v = x[e] * exp2f(L.G[r][i0 + e]);
+            const float v = x[e] * exp2_hw(L.G[r][i0 + e]);
             const __bf16 hb = (__bf16)v;
             hv[e] = hb;
             lv[e] = (__bf16)(v - (float)hb);
@@ -553,7 +560,7 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
         for (int e = 0; e < 8; ++e) {
             const int r = r0 + e;
             // k^ rows past n are zero
-            const float v = L.K[r][i] * exp2f(fminf(gl - L.G[r][i], 0.f));
+            const float v = L.K[r][i] * exp2_hw(fminf(gl - L.G[r][i], 0.f));
             const __bf16 hb = (__bf16)v;
             hv[e] = hb;
             lv[e] = (__bf16)(v - (float)hb);
@@ -562,7 +569,7 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
         *reinterpret_cast<bf16x8 *>(ws.K_hi + o) = hv;
         *reinterpret_cast<bf16x8 *>(ws.K_lo + o) = lv;
     }
-    if (tid < DK) ws.gC[gh * DK + tid] = exp2f(L.G[last][tid]);
+    if (tid < DK) ws.gC[gh * DK + tid] = exp2_hw(L.G[last][tid]);
 
     // 5. T = (I + A)^-1 by 16 x 16 blocks: the diagonal blocks by forward
     //    substitution, then block row b = 1, 2, 3 from
@@ -640,7 +647,7 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int sv = 32 * k2 + 8 * lk + e;
-                x[e] = isw ? L.beta[sv] * L.K[sv][col] * exp2f(L.G[sv][col]) : L.beta[sv] * vpre[ci][k2][e];
+                x[e] = isw ? L.beta[sv] * L.K[sv][col] * exp2_hw(L.G[sv][col]) : L.beta[sv] * vpre[ci][k2][e];
             }
             rb[k2] = split8(x);
         }
