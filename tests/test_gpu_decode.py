@@ -309,11 +309,13 @@ def test_repeated_runs_bitwise_identical():
         assert torch.equal(a, b)
 
 
-def test_stream_state_flag_is_bitwise_identical():
-    """KDA_STREAM_STATE only changes cache hints: decode and verify results
-    are bitwise the same with and without it."""
-    g = synth.rng(740)
-    H, dk, dv, B, T = 4, 128, 128, 6, 5
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (64, 128), (128, 64)])
+def test_stream_state_flag_is_bitwise_identical(dk, dv):
+    """KDA_STREAM_STATE only changes cache policy (buffer operations sized to
+    the d_k x d_v tile): decode and verify results are bitwise the same with
+    and without it, for every supported head size."""
+    g = synth.rng(740 + dk + 2 * dv)
+    H, B, T = 4, 6, 5
     params = synth.layer_params(g, H, dk, dv)
     dl, _ = layer_pair(params)
     ds, _ = layer_pair(params)
