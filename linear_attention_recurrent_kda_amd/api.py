@@ -147,6 +147,52 @@ def _raise(fn: str, code: int):
         raise KdaError(fn, code)
 
 
+# While prepared() runs an entry point, the marshalled C call is recorded
+# here instead of being issued.
+_recording: Optional[list] = None
+
+
+def _call(name: str, *args, keep=None) -> None:
+    """Issue C entry point `name` with marshalled arguments (or record it;
+    `keep` holds objects the recorded call needs alive, e.g. a workspace
+    allocated here)."""
+    if _recording is not None:
+        _recording.append((name, args, keep))
+        return
+    _raise(name, getattr(_lib.load(), name)(*args))
+
+
+def prepared(entry, *args, **kwargs):
+    """Check and marshal one call of a launching entry point of this module
+    (kda_decode, kda_spec_verify, kda_spec_commit, kda_spec_verify_delta,
+    kda_spec_commit_delta, kda_chunk_prefill, kda_chunk_prefill_ckpt) once,
+    without launching it; return a zero-argument callable that issues exactly
+    that C call again each time (for launch loops where per-call Python
+    overhead would leave the GPU idle).  The callable keeps the arguments
+    alive and raises KdaError on a non-OK status.  The stream is fixed at
+    preparation (the current stream unless `stream=` is given)."""
+    global _recording
+    if _recording is not None:
+        raise RuntimeError("prepared() does not nest")
+    _recording = []
+    try:
+        entry(*args, **kwargs)
+        rec = _recording
+    finally:
+        _recording = None
+    if len(rec) != 1:
+        raise ValueError(f"{getattr(entry, '__name__', entry)} does not issue exactly one C call")
+    name, cargs, held = rec[0]
+    fn = getattr(_lib.load(), name)
+
+    def call():
+        rc = fn(*cargs)
+        if rc:
+            raise KdaError(name, rc)
+    call.keep = (args, kwargs, cargs, held)
+    return call
+
+
 def kda_decode(layer: Layer, cache: Cache, slot_idx: torch.Tensor, inputs: Inputs,
                y: torch.Tensor, stream=None) -> None:
     """One token per sequence; slot_idx [B] int32, inputs [B, H, .], y [B, H, d_v]."""
@@ -158,35 +204,14 @@ def kda_decode(layer: Layer, cache: Cache, slot_idx: torch.Tensor, inputs: Input
     L, C, I = layer.c_struct(), cache.c_struct(layer), inputs.c_struct(layer, (B,))
     if cache.conv_state.dtype != inputs.dtype:
         raise TypeError("conv_state dtype must equal the input dtype")
-    _raise("kda_decode", _lib.load().kda_decode(ctypes.byref(L), ctypes.byref(C), slot_idx.data_ptr(),
-                                                B, ctypes.byref(I), y.data_ptr(), _stream(stream)))
+    _call("kda_decode", ctypes.byref(L), ctypes.byref(C), slot_idx.data_ptr(),
+          B, ctypes.byref(I), y.data_ptr(), _stream(stream))
 
 
 def kda_decode_prepared(layer: Layer, cache: Cache, slot_idx: torch.Tensor, inputs: Inputs,
                         y: torch.Tensor, stream=None):
-    """Check and marshal the arguments of one kda_decode call once; return a
-    zero-argument callable that issues exactly that call (for launch loops
-    where per-call Python overhead would leave the GPU idle).  The callable
-    keeps the tensors alive; it raises KdaError on a non-OK status."""
-    _check(slot_idx, "slot_idx", torch.int32)
-    B = slot_idx.numel()
-    _check(y, "y", torch.float32)
-    if tuple(y.shape) != (B, layer.H, layer.d_v):
-        raise ValueError("y must be [B, H, d_v]")
-    L, C, I = layer.c_struct(), cache.c_struct(layer), inputs.c_struct(layer, (B,))
-    if cache.conv_state.dtype != inputs.dtype:
-        raise TypeError("conv_state dtype must equal the input dtype")
-    fn = _lib.load().kda_decode
-    args = (ctypes.byref(L), ctypes.byref(C), slot_idx.data_ptr(), B, ctypes.byref(I),
-            y.data_ptr(), _stream(stream))
-    keep = (L, C, I, layer, cache, slot_idx, inputs, y)
-
-    def call():
-        rc = fn(*args)
-        if rc:
-            raise KdaError("kda_decode", rc)
-    call.keep = keep
-    return call
+    """prepared(kda_decode, ...): a zero-argument callable issuing this call."""
+    return prepared(kda_decode, layer, cache, slot_idx, inputs, y, stream=stream)
 
 
 def kda_spec_verify(layer: Layer, cache: Cache, slot_idx: torch.Tensor, snap_slots: torch.Tensor,
@@ -212,9 +237,9 @@ def kda_spec_verify(layer: Layer, cache: Cache, slot_idx: torch.Tensor, snap_slo
     L, C, I = layer.c_struct(), cache.c_struct(layer), inputs.c_struct(layer, (B, T))
     if cache.conv_state.dtype != inputs.dtype:
         raise TypeError("conv_state dtype must equal the input dtype")
-    _raise("kda_spec_verify", _lib.load().kda_spec_verify(
-        ctypes.byref(L), ctypes.byref(C), slot_idx.data_ptr(), snap_slots.data_ptr(), B, T, dl,
-        ctypes.byref(I), y.data_ptr(), _stream(stream)))
+    _call("kda_spec_verify",
+          ctypes.byref(L), ctypes.byref(C), slot_idx.data_ptr(), snap_slots.data_ptr(), B, T, dl,
+          ctypes.byref(I), y.data_ptr(), _stream(stream))
 
 
 def kda_spec_commit(layer: Layer, cache: Cache, slot_idx: torch.Tensor, snap_slots: torch.Tensor,
@@ -229,9 +254,9 @@ def kda_spec_commit(layer: Layer, cache: Cache, slot_idx: torch.Tensor, snap_slo
     T = snap_slots.shape[1]
     L, C = layer.c_struct(), cache.c_struct(layer)
     wdt = _lib.KDA_BF16 if cache.conv_state.dtype == torch.bfloat16 else _lib.KDA_F32
-    _raise("kda_spec_commit", _lib.load().kda_spec_commit(
-        ctypes.byref(L), ctypes.byref(C), slot_idx.data_ptr(), snap_slots.data_ptr(),
-        accepted_len.data_ptr(), B, T, wdt, _stream(stream)))
+    _call("kda_spec_commit",
+          ctypes.byref(L), ctypes.byref(C), slot_idx.data_ptr(), snap_slots.data_ptr(),
+          accepted_len.data_ptr(), B, T, wdt, _stream(stream))
 
 
 def _dtype_code(dt) -> int:
@@ -284,9 +309,9 @@ def kda_spec_verify_delta(layer: Layer, cache: Cache, slot_idx: torch.Tensor, in
     L, C, I = layer.c_struct(), cache.c_struct(layer), inputs.c_struct(layer, (B, T))
     if cache.conv_state.dtype != inputs.dtype:
         raise TypeError("conv_state dtype must equal the input dtype")
-    _raise("kda_spec_verify_delta", _lib.load().kda_spec_verify_delta(
-        ctypes.byref(L), ctypes.byref(C), slot_idx.data_ptr(), B, T, dl, ctypes.byref(I),
-        y.data_ptr(), delta.data_ptr(), nbytes, _stream(stream)))
+    _call("kda_spec_verify_delta",
+          ctypes.byref(L), ctypes.byref(C), slot_idx.data_ptr(), B, T, dl, ctypes.byref(I),
+          y.data_ptr(), delta.data_ptr(), nbytes, _stream(stream))
 
 
 def kda_spec_commit_delta(layer: Layer, cache: Cache, slot_idx: torch.Tensor, delta: torch.Tensor,
@@ -299,9 +324,9 @@ def kda_spec_commit_delta(layer: Layer, cache: Cache, slot_idx: torch.Tensor, de
         raise ValueError("accepted_len must be [B]")
     T, nbytes = _delta_buf(delta, B)
     L, C = layer.c_struct(), cache.c_struct(layer)
-    _raise("kda_spec_commit_delta", _lib.load().kda_spec_commit_delta(
-        ctypes.byref(L), ctypes.byref(C), slot_idx.data_ptr(), delta.data_ptr(), nbytes,
-        accepted_len.data_ptr(), B, T, _dtype_code(cache.conv_state.dtype), _stream(stream)))
+    _call("kda_spec_commit_delta",
+          ctypes.byref(L), ctypes.byref(C), slot_idx.data_ptr(), delta.data_ptr(), nbytes,
+          accepted_len.data_ptr(), B, T, _dtype_code(cache.conv_state.dtype), _stream(stream))
 
 
 def kda_chunk_prefill_workspace_bytes(layer: Layer, total_T: int, N_seq: int, chunk: int = 64) -> int:
@@ -342,9 +367,9 @@ def kda_chunk_prefill(layer: Layer, cache: Cache, slot_idx: torch.Tensor, cu_seq
     here (torch) when none is given."""
     L, C, I, N, total_T, wp, wb, keep = _prefill_args(layer, cache, slot_idx, cu_seqlens, inputs, y,
                                                       workspace, chunk, stream)
-    _raise("kda_chunk_prefill", _lib.load().kda_chunk_prefill(
-        ctypes.byref(L), ctypes.byref(C), slot_idx.data_ptr(), cu_seqlens.data_ptr(), N, total_T,
-        chunk, ctypes.byref(I), y.data_ptr(), wp, wb, _stream(stream)))
+    _call("kda_chunk_prefill",
+          ctypes.byref(L), ctypes.byref(C), slot_idx.data_ptr(), cu_seqlens.data_ptr(), N, total_T,
+          chunk, ctypes.byref(I), y.data_ptr(), wp, wb, _stream(stream), keep=keep)
 
 
 def kda_chunk_prefill_ckpt(layer: Layer, cache: Cache, slot_idx: torch.Tensor, cu_seqlens: torch.Tensor,
@@ -358,10 +383,10 @@ def kda_chunk_prefill_ckpt(layer: Layer, cache: Cache, slot_idx: torch.Tensor, c
         raise ValueError("ckpt_slots must be [N_seq, per_seq]")
     L, C, I, N, total_T, wp, wb, keep = _prefill_args(layer, cache, slot_idx, cu_seqlens, inputs, y,
                                                       workspace, chunk, stream)
-    _raise("kda_chunk_prefill_ckpt", _lib.load().kda_chunk_prefill_ckpt(
-        ctypes.byref(L), ctypes.byref(C), slot_idx.data_ptr(), cu_seqlens.data_ptr(), N, total_T,
-        chunk, ctypes.byref(I), y.data_ptr(), ckpt_slots.data_ptr(), int(ckpt_interval),
-        int(ckpt_slots.shape[1]), wp, wb, _stream(stream)))
+    _call("kda_chunk_prefill_ckpt",
+          ctypes.byref(L), ctypes.byref(C), slot_idx.data_ptr(), cu_seqlens.data_ptr(), N, total_T,
+          chunk, ctypes.byref(I), y.data_ptr(), ckpt_slots.data_ptr(), int(ckpt_interval),
+          int(ckpt_slots.shape[1]), wp, wb, _stream(stream), keep=keep)
 
 
 def kda_copy_probe(dst: torch.Tensor, src: torch.Tensor, stream=None) -> None:
@@ -369,8 +394,7 @@ def kda_copy_probe(dst: torch.Tensor, src: torch.Tensor, stream=None) -> None:
     _check(src, "src", torch.float32)
     if dst.numel() != src.numel():
         raise ValueError("dst and src sizes differ")
-    _raise("kda_copy_probe", _lib.load().kda_copy_probe(dst.data_ptr(), src.data_ptr(), src.numel(),
-                                                        _stream(stream)))
+    _call("kda_copy_probe", dst.data_ptr(), src.data_ptr(), src.numel(), _stream(stream))
 
 
 def kda_status_string(code: int) -> str:

@@ -200,3 +200,15 @@ def test_copy_probe_validation(lib):
     assert lib.kda_copy_probe(FAKE, FAKE, 0, None) == 0
     assert lib.kda_copy_probe(None, FAKE, 4, None) == 1
     assert lib.kda_copy_probe(FAKE + 4, FAKE, 4, None) == 4
+
+
+def test_prepared_needs_exactly_one_launch():
+    """api.prepared() records the C call of a launching entry point instead
+    of issuing it; a function that issues none is refused, and it does not
+    nest."""
+    from linear_attention_recurrent_kda_amd import api
+    with pytest.raises(ValueError):
+        api.prepared(lambda: None)
+    with pytest.raises(RuntimeError):
+        api.prepared(lambda: api.prepared(lambda: None))
+    assert api._recording is None
