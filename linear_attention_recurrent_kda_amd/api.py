@@ -129,7 +129,7 @@ class Inputs:
 def _check(t: torch.Tensor, name: str, dtype=None):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.device.type != "cuda":
+    if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor (got {t.device})")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
