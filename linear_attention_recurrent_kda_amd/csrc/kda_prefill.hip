@@ -314,22 +314,47 @@ __device__ __forceinline__ void prep_rows(const PrefillParams &p, const Tin *x, 
 
 // log2(alpha) of the chunk's tokens for channels ch0 .. ch0 + 63 and its
 // prefix sums over the chunk into G (rows past n add nothing); one wave.
+// The gate inputs are fetched 8 channels per lane (8 row loads per lane
+// instead of 64 narrow ones), log2(alpha) goes to G, and then each lane
+// turns its channel's column of G into prefix sums, adding in token order.
 template <int DK, typename Tin>
 __device__ __forceinline__ void prep_gates(const PrefillParams &p, int t0, int n, int h, int lane, int ch0,
                                            float (*G)[DK + 1]) {
-    const int H = p.H, ch = ch0 + lane;
+    typedef Tin V8 __attribute__((ext_vector_type(8)));
+    constexpr int LPR = 64 / 8;          // lanes per row of 64 channels
+    constexpr int RPI = kWave / LPR;     // rows per wave-wide load
+    constexpr int NI = kChunk / RPI;     // loads per lane
+    const int H = p.H, sub = lane % LPR, r0 = lane / LPR, cl = ch0 + 8 * sub;
     const Tin *g = static_cast<const Tin *>(p.g);
-    Tin raw[kChunk];
+    V8 raw[NI];
 #pragma unroll
-    for (int j = 0; j < kChunk; ++j) raw[j] = g[((size_t)(t0 + min(j, n - 1)) * H + h) * DK + ch];
-    const float ea = expf(p.A[h * DK + ch]);
+    for (int i = 0; i < NI; ++i) {
+        const int row = r0 + RPI * i;
+        raw[i] = *reinterpret_cast<const V8 *>(g + ((size_t)(t0 + min(row, n - 1)) * H + h) * DK + cl);
+    }
+    float ea[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ea[e] = expf(p.A[h * DK + cl + e]);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int row = r0 + RPI * i;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            // alpha below 2^-200 is 0 in fp32 either way; the floor keeps the
+            // prefix sums finite (g = +inf would give -inf - -inf = NaN later)
+            const float la = fmaxf(log2_alpha_hw(ea[e], to_f32(raw[i][e])), -200.f);
+            G[row][cl + e] = row < n ? la : 0.f;
+        }
+    }
+    // the column a lane sums was written by other lanes of this wave
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int ch = ch0 + lane;
     float acc = 0.f;
 #pragma unroll
     for (int j = 0; j < kChunk; ++j) {
-        // alpha below 2^-200 is 0 in fp32 either way; the floor keeps the
-        // prefix sums finite (g = +inf would give -inf - -inf = NaN later)
-        const float la = fmaxf(log2_alpha_hw(ea, to_f32(raw[j])), -200.f);
-        acc += j < n ? la : 0.f;
+        acc += G[j][ch];
         G[j][ch] = acc;
     }
 }
