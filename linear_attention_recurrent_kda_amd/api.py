@@ -9,6 +9,7 @@ status raises ``KdaError``.  All computation happens in the HIP kernels.
 from __future__ import annotations
 
 import ctypes
+import threading
 from dataclasses import dataclass
 from typing import Optional
 
@@ -147,17 +148,18 @@ def _raise(fn: str, code: int):
         raise KdaError(fn, code)
 
 
-# While prepared() runs an entry point, the marshalled C call is recorded
-# here instead of being issued.
-_recording: Optional[list] = None
+# While prepared() runs an entry point on a thread, the marshalled C call is
+# recorded here (per thread) instead of being issued.
+_tls = threading.local()
 
 
 def _call(name: str, *args, keep=None) -> None:
     """Issue C entry point `name` with marshalled arguments (or record it;
     `keep` holds objects the recorded call needs alive, e.g. a workspace
     allocated here)."""
-    if _recording is not None:
-        _recording.append((name, args, keep))
+    rec = getattr(_tls, "recording", None)
+    if rec is not None:
+        rec.append((name, args, keep))
         return
     _raise(name, getattr(_lib.load(), name)(*args))
 
@@ -171,15 +173,13 @@ def prepared(entry, *args, **kwargs):
     overhead would leave the GPU idle).  The callable keeps the arguments
     alive and raises KdaError on a non-OK status.  The stream is fixed at
     preparation (the current stream unless `stream=` is given)."""
-    global _recording
-    if _recording is not None:
+    if getattr(_tls, "recording", None) is not None:
         raise RuntimeError("prepared() does not nest")
-    _recording = []
+    rec = _tls.recording = []
     try:
         entry(*args, **kwargs)
-        rec = _recording
     finally:
-        _recording = None
+        _tls.recording = None
     if len(rec) != 1:
         raise ValueError(f"{getattr(entry, '__name__', entry)} does not issue exactly one C call")
     name, cargs, held = rec[0]

@@ -211,4 +211,26 @@ def test_prepared_needs_exactly_one_launch():
         api.prepared(lambda: None)
     with pytest.raises(RuntimeError):
         api.prepared(lambda: api.prepared(lambda: None))
-    assert api._recording is None
+    assert getattr(api._tls, "recording", None) is None
+
+
+def test_prepared_records_only_on_its_own_thread():
+    """While one thread prepares a call, a call issued on another thread is
+    not captured by it (the recording is per thread)."""
+    import threading
+    from linear_attention_recurrent_kda_amd import api
+    seen = {}
+
+    def other():
+        seen["other"] = getattr(api._tls, "recording", None)
+
+    def entry():
+        t = threading.Thread(target=other)
+        t.start()
+        t.join()
+        seen["own"] = list(getattr(api._tls, "recording", None))
+        api._call("kda_abi_version")   # recorded, not issued
+
+    call = api.prepared(entry)
+    assert seen["other"] is None and seen["own"] == []
+    assert callable(call)
