@@ -74,8 +74,17 @@ struct RecGeo {
 
 // Per-token values shared through LDS.  conv[] holds the conv outputs
 // q | k | v; the norm pass overwrites q and k with q^ and k^ in place.
-template <int DK, int DV>
-struct TokenLds {
+// With LR, rows[0..2] hold alpha, k^ and q^ again, ordered for the
+// recurrence: the RPT rows a lane owns (rg, rg + RG, ...) are consecutive,
+// at rg * RPT, so a lane reads them with 16-byte loads.  Verify kernels of
+// 2 to 8 tokens use it (its token chain is the critical path there); for 16
+// tokens the extra 1.5 KB per token would cost a workgroup per CU, and the
+// one-token decode measured no faster with it.
+constexpr bool lane_rows(int tmax) { return tmax > 1 && tmax <= 8; }
+
+template <int DK, int DV, bool LR>
+struct alignas(16) TokenLds {
+    float rows[LR ? 3 : 1][LR ? DK : 4];
     float conv[2 * DK + DV + 1];   // + 1: sink for lanes without a channel
     float alpha[DK];
     float gate[DV];   // norm_w * sigmoid(z)
@@ -174,7 +183,7 @@ __device__ __forceinline__ void conv_fetch(const RecParams &p, int tid, int b, i
 template <int DK, int DV, int NT, typename Tin, int TMAX, bool VERIFY, bool DELTA>
 __device__ __forceinline__ void conv_compute(const RecParams &p, int tid, int b, int h, int slot, int T,
                                              const ConvRegs<DK, DV, NT, Tin, TMAX> &cr,
-                                             TokenLds<DK, DV> *tok) {
+                                             TokenLds<DK, DV, lane_rows(TMAX)> *tok) {
     constexpr int CH = 2 * DK + DV;
 #pragma unroll
     for (int k = 0; k < cr.CPT; ++k) {
@@ -243,10 +252,10 @@ __device__ __forceinline__ void prep_fetch(const RecParams &p, int wave, int lan
 }
 
 // L2 norms, k^.q^ and gates of one token, by one whole wave.
-template <int DK, int DV, typename Tin, int TPW>
+template <int DK, int DV, typename Tin, int TPW, int RG, int RPT, bool LR>
 __device__ __forceinline__ void prep_token(const RecParams &p, int lane, int j,
                                            const PrepRegs<DK, DV, Tin, TPW> &pr,
-                                           TokenLds<DK, DV> &tk) {
+                                           TokenLds<DK, DV, LR> &tk) {
     constexpr int EK = DK / kWave, EV = DV / kWave;
     float qv[EK], kv[EK];
     float sq = 0.f, sk = 0.f;
@@ -269,11 +278,20 @@ __device__ __forceinline__ void prep_token(const RecParams &p, int lane, int j,
         kq = fmaf(qv[e], kv[e], kq);
         tk.conv[lane + kWave * e] = qv[e];
         tk.conv[DK + lane + kWave * e] = kv[e];
+        if (LR) {
+            const int r = lane + kWave * e, pos = (r % RG) * RPT + r / RG;
+            tk.rows[1][pos] = kv[e];
+            tk.rows[2][pos] = qv[e];
+        }
     }
     kq = wave_sum(kq);
 #pragma unroll
-    for (int e = 0; e < EK; ++e)
-        tk.alpha[lane + kWave * e] = expf(-expf(pr.A[e]) * softplus(to_f32(pr.g[j][e])));
+    for (int e = 0; e < EK; ++e) {
+        const float a = expf(-expf(pr.A[e]) * softplus(to_f32(pr.g[j][e])));
+        const int r = lane + kWave * e;
+        tk.alpha[r] = a;
+        if (LR) tk.rows[0][(r % RG) * RPT + r / RG] = a;
+    }
 #pragma unroll
     for (int e = 0; e < EV; ++e)
         tk.gate[lane + kWave * e] = pr.w[e] * sigmoid(to_f32(pr.z[j][e]));
@@ -314,7 +332,8 @@ struct RecShared {
     using G = RecGeo<DK, DV, NT>;
     static constexpr int NRB = TMAX <= 8 ? 2 : 1;
     static constexpr bool DEFER = TMAX > 1;
-    TokenLds<DK, DV> tok[TMAX];
+    static constexpr bool LR = lane_rows(TMAX);
+    TokenLds<DK, DV, LR> tok[TMAX];
     float4 red[NRB][G::NW][2][G::CG];
     float4 obuf[DEFER ? TMAX : 1][G::CG];
 };
@@ -412,7 +431,8 @@ __device__ __forceinline__ void rec_run(const RecParams &p, RecItem<DK, DV, NT, 
     constexpr bool VERIFY = MODE != kDecode;
     constexpr bool DELTA = MODE == kVerifyDelta;
     constexpr int TPW = RecItem<DK, DV, NT, Tin, TMAX>::TPW;
-    TokenLds<DK, DV> *tok = sh.tok;
+    constexpr bool LR = SH::LR;
+    TokenLds<DK, DV, LR> *tok = sh.tok;
     const int tid = threadIdx.x;
     const int lane = tid % kWave, wave = tid / kWave;
     const int cg = tid % G::CG, rg = tid / G::CG;
@@ -427,7 +447,7 @@ __device__ __forceinline__ void rec_run(const RecParams &p, RecItem<DK, DV, NT, 
 #pragma unroll
     for (int j = 0; j < TPW; ++j) {
         const int t = wave + G::NW * j;
-        if (t < T) prep_token<DK, DV, Tin, TPW>(p, lane, j, it.pr, tok[t]);
+        if (t < T) prep_token<DK, DV, Tin, TPW, G::RG, G::RPT, LR>(p, lane, j, it.pr, tok[t]);
     }
     __syncthreads();
     // delta mode: alpha and k^ of every token into its record
@@ -450,14 +470,34 @@ __device__ __forceinline__ void rec_run(const RecParams &p, RecItem<DK, DV, NT, 
 
     // 4. the recurrence, tokens in order, state in registers
     for (int t = 0; t < T; ++t) {
-        const TokenLds<DK, DV> &tk = tok[t];
+        const TokenLds<DK, DV, LR> &tk = tok[t];
         float4 u = make_float4(0.f, 0.f, 0.f, 0.f), pq = u;
+        static_assert(!LR || G::RPT % 4 == 0, "a lane's rows are read four at a time");
+        const float4 *rk = reinterpret_cast<const float4 *>(&tk.rows[LR ? 1 : 0][LR ? rg * G::RPT : 0]);
+        if (LR) {
+            const float4 *ra = reinterpret_cast<const float4 *>(&tk.rows[0][rg * G::RPT]);
+            const float4 *rq = reinterpret_cast<const float4 *>(&tk.rows[LR ? 2 : 0][LR ? rg * G::RPT : 0]);
 #pragma unroll
-        for (int i = 0; i < G::RPT; ++i) {
-            const int r = rg + G::RG * i;
-            s[i] = s[i] * tk.alpha[r];
-            u = fma4(tk.conv[DK + r], s[i], u);
-            pq = fma4(tk.conv[r], s[i], pq);
+            for (int i4 = 0; i4 < G::RPT / 4; ++i4) {
+                const float4 a4 = ra[i4], k4 = rk[i4], q4 = rq[i4];
+                const float av[4] = {a4.x, a4.y, a4.z, a4.w}, kv[4] = {k4.x, k4.y, k4.z, k4.w},
+                            qv[4] = {q4.x, q4.y, q4.z, q4.w};
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int i = 4 * i4 + c;   // row rg + RG * i
+                    s[i] = s[i] * av[c];
+                    u = fma4(kv[c], s[i], u);
+                    pq = fma4(qv[c], s[i], pq);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < G::RPT; ++i) {
+                const int r = rg + G::RG * i;
+                s[i] = s[i] * tk.alpha[r];
+                u = fma4(tk.conv[DK + r], s[i], u);
+                pq = fma4(tk.conv[r], s[i], pq);
+            }
         }
         // sum over the row groups inside the wave, then across waves
 #pragma unroll
@@ -481,8 +521,19 @@ __device__ __forceinline__ void rec_run(const RecParams &p, RecItem<DK, DV, NT, 
         const float4 v = *reinterpret_cast<const float4 *>(&tk.conv[2 * DK + 4 * cg]);
         const float4 d = make_float4(beta * (v.x - U.x), beta * (v.y - U.y),
                                      beta * (v.z - U.z), beta * (v.w - U.w));
+        if (LR) {
 #pragma unroll
-        for (int i = 0; i < G::RPT; ++i) s[i] = fma4(tk.conv[DK + rg + G::RG * i], d, s[i]);
+            for (int i4 = 0; i4 < G::RPT / 4; ++i4) {
+                const float4 k4 = rk[i4];
+                s[4 * i4] = fma4(k4.x, d, s[4 * i4]);
+                s[4 * i4 + 1] = fma4(k4.y, d, s[4 * i4 + 1]);
+                s[4 * i4 + 2] = fma4(k4.z, d, s[4 * i4 + 2]);
+                s[4 * i4 + 3] = fma4(k4.w, d, s[4 * i4 + 3]);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < G::RPT; ++i) s[i] = fma4(tk.conv[DK + rg + G::RG * i], d, s[i]);
+        }
 
         if (DELTA) {
             if (tid < G::CG)
