@@ -27,7 +27,8 @@
 namespace kda {
 
 // State tile traffic: read once, written once per launch, as float4 at float
-// offset `off` of the d_k x d_v tile at `tile` (a workgroup-uniform base).
+// offset row + col of the d_k x d_v tile at `tile` (a workgroup-uniform
+// base; row a multiple of d_v, col the lane's column).
 // With STREAM the accesses are raw buffer operations carrying the
 // non-temporal policy (stores also the device-scope bit sc1), so a working
 // set larger than the caches does not thrash them (and a small, re-used one
@@ -39,26 +40,28 @@ constexpr int kPolicyNT = 2, kPolicySC1 = 16;   // CDNA3/4 cache-policy bits
 constexpr int kBufferWord3 = 0x00020000;        // raw 32-bit buffer resource
 
 template <bool STREAM, int TILE>
-__device__ __forceinline__ float4 load_state4(const float *tile, size_t off) {
+__device__ __forceinline__ float4 load_state4(const float *tile, size_t row, int col) {
     if (STREAM) {
+        const size_t off = row + col;
         typedef float v4 __attribute__((ext_vector_type(4)));
         const __amdgpu_buffer_rsrc_t r =
             __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(tile), 0, TILE * 4, kBufferWord3);
         const v4 x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(off * 4), 0, kPolicyNT);
         return make_float4(x[0], x[1], x[2], x[3]);
     }
-    return *reinterpret_cast<const float4 *>(tile + off);
+    return *reinterpret_cast<const float4 *>(tile + row + col);
 }
 template <bool STREAM, int TILE>
-__device__ __forceinline__ void store_state4(float *tile, size_t off, float4 v) {
+__device__ __forceinline__ void store_state4(float *tile, size_t row, int col, float4 v) {
     if (STREAM) {
+        const size_t off = row + col;
         typedef float v4 __attribute__((ext_vector_type(4)));
         const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(tile, 0, TILE * 4, kBufferWord3);
         const v4 x = {v.x, v.y, v.z, v.w};
         __builtin_amdgcn_raw_buffer_store_b128(x, r, (int)(off * 4), 0, kPolicyNT | kPolicySC1);
         return;
     }
-    *reinterpret_cast<float4 *>(tile + off) = v;
+    *reinterpret_cast<float4 *>(tile + row + col) = v;
 }
 
 template <int DK, int DV, int NT>
@@ -415,7 +418,7 @@ __device__ __forceinline__ void rec_loads(const RecParams &p, RecItem<DK, DV, NT
     // in issue order, so the conv/gate math then waits only for them)
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < G::RPT; ++i) it.s[i] = load_state4<STREAM, DK * DV>(it.S, (size_t)(rg + G::RG * i) * DV + 4 * cg);
+    for (int i = 0; i < G::RPT; ++i) it.s[i] = load_state4<STREAM, DK * DV>(it.S, (size_t)(rg + G::RG * i) * DV, 4 * cg);
     // and nothing that waits for them is scheduled above them
     __builtin_amdgcn_sched_barrier(0);
 }
@@ -544,7 +547,7 @@ __device__ __forceinline__ void rec_run(const RecParams &p, RecItem<DK, DV, NT, 
             if (ss >= 0 && ss < p.n_slots) {
                 float *D = p.state + ((size_t)ss * p.H + h) * DK * DV;
 #pragma unroll
-                for (int i = 0; i < G::RPT; ++i) store_state4<STREAM, DK * DV>(D, (size_t)(rg + G::RG * i) * DV + 4 * cg, s[i]);
+                for (int i = 0; i < G::RPT; ++i) store_state4<STREAM, DK * DV>(D, (size_t)(rg + G::RG * i) * DV, 4 * cg, s[i]);
             } else if (ss != -1 && tid == 0) {
                 flag_error(p.err_flag);
             }
@@ -570,7 +573,7 @@ __device__ __forceinline__ void rec_run(const RecParams &p, RecItem<DK, DV, NT, 
     // 5. the single write of the state tile (decode only: verify leaves S0)
     if (!VERIFY) {
 #pragma unroll
-        for (int i = 0; i < G::RPT; ++i) store_state4<STREAM, DK * DV>(it.S, (size_t)(rg + G::RG * i) * DV + 4 * cg, s[i]);
+        for (int i = 0; i < G::RPT; ++i) store_state4<STREAM, DK * DV>(it.S, (size_t)(rg + G::RG * i) * DV, 4 * cg, s[i]);
     }
 }
 
@@ -635,7 +638,7 @@ __global__ __launch_bounds__(NT) void kda_commit_delta_kernel(CommitDeltaParams 
     float *S = p.state + ((size_t)dst * p.H + h) * DK * DV;
     float4 s[G::RPT];
 #pragma unroll
-    for (int i = 0; i < G::RPT; ++i) s[i] = load_state4<STREAM, DK * DV>(S, (size_t)(rg + G::RG * i) * DV + 4 * cg);
+    for (int i = 0; i < G::RPT; ++i) s[i] = load_state4<STREAM, DK * DV>(S, (size_t)(rg + G::RG * i) * DV, 4 * cg);
 
     // the float part of the L records into LDS (16-byte loads)
     for (int i = tid; i < L * (NF / 4); i += NT) {
@@ -669,7 +672,7 @@ __global__ __launch_bounds__(NT) void kda_commit_delta_kernel(CommitDeltaParams 
         }
     }
 #pragma unroll
-    for (int i = 0; i < G::RPT; ++i) store_state4<STREAM, DK * DV>(S, (size_t)(rg + G::RG * i) * DV + 4 * cg, s[i]);
+    for (int i = 0; i < G::RPT; ++i) store_state4<STREAM, DK * DV>(S, (size_t)(rg + G::RG * i) * DV, 4 * cg, s[i]);
 }
 
 // ---------------------------------------------------------------------------
