@@ -283,6 +283,21 @@ def extras(torch, api, synth, layer, cache, step_inputs, y, slots, B, H, dk, dv,
         s = a.elapsed_time(b) / 1e3 / steps
         ex[name] = {"us_per_step": s * 1e6, "token_heads_per_s": B * H / s,
                     "algorithmic_gbs": bl / s / 1e9, "frac_of_8tbs": bl / s / 8e12}
+    # DRAM-bound large batch: every slot of the pool in one call (n_slots
+    # sequences; 2 GiB of state at H=32, d=128, eight times the Infinity
+    # Cache, so the call streams by itself)
+    Bl = n_slots
+    gl = synth.rng(11)
+    linp = synth.token_inputs(gl, (Bl,), H, dk, dv, "bf16")
+    LI = api.Inputs(*(torch.from_numpy(np.ascontiguousarray(linp[k])).to("cuda:0").to(torch.bfloat16)
+                      for k in ("x_q", "x_k", "x_v", "g", "b", "z")))
+    yl = torch.empty((Bl, H, dv), device="cuda:0")
+    s = timed(torch, stream, api.prepared(api.kda_decode, layer, cache, perm, LI, yl), 10)
+    bll = decode_bytes_per_token_head(H, dk, dv, Bl) * Bl * H
+    ex["decode_b%d_dram" % Bl] = {"us_per_step": s * 1e6, "token_heads_per_s": Bl * H / s,
+                                  "algorithmic_gbs": bll / s / 1e9, "frac_of_8tbs": bll / s / 8e12,
+                                  "state_bytes": Bl * H * dk * dv * 4}
+    del LI, yl
     # copy ceiling (1 GiB each way)
     n = 1 << 28
     src = torch.empty(n, dtype=torch.float32, device="cuda:0").fill_(1.0)
