@@ -79,11 +79,11 @@ struct RecGeo {
 // q | k | v; the norm pass overwrites q and k with q^ and k^ in place.
 // With LR, rows[0..2] hold alpha, k^ and q^ again, ordered for the
 // recurrence: the RPT rows a lane owns (rg, rg + RG, ...) are consecutive,
-// at rg * RPT, so a lane reads them with 16-byte loads.  Verify kernels of
-// 2 to 8 tokens use it (its token chain is the critical path there); for 16
-// tokens the extra 1.5 KB per token would cost a workgroup per CU, and the
-// one-token decode measured no faster with it.
-constexpr bool lane_rows(int tmax) { return tmax > 1 && tmax <= 8; }
+// at rg * RPT, so a lane reads them with 16-byte loads.  Verify launches of
+// 2 to 8 tokens whose grid fits the GPU at once use it (the token chain is
+// then the critical path); larger grids measured slower with the extra LDS,
+// 16 tokens would lose a workgroup per CU to it, and the one-token decode
+// measured no faster with it.
 
 template <int DK, int DV, bool LR>
 struct alignas(16) TokenLds {
@@ -183,10 +183,10 @@ __device__ __forceinline__ void conv_fetch(const RecParams &p, int tid, int b, i
 // window rows after each token go to the live slot (decode) or to the
 // token's snapshot slot (verify); delta mode keeps the raw inputs in the
 // token's record instead.
-template <int DK, int DV, int NT, typename Tin, int TMAX, bool VERIFY, bool DELTA>
+template <int DK, int DV, int NT, typename Tin, int TMAX, bool VERIFY, bool DELTA, bool LR>
 __device__ __forceinline__ void conv_compute(const RecParams &p, int tid, int b, int h, int slot, int T,
                                              const ConvRegs<DK, DV, NT, Tin, TMAX> &cr,
-                                             TokenLds<DK, DV, lane_rows(TMAX)> *tok) {
+                                             TokenLds<DK, DV, LR> *tok) {
     constexpr int CH = 2 * DK + DV;
 #pragma unroll
     for (int k = 0; k < cr.CPT; ++k) {
@@ -330,12 +330,13 @@ enum RecMode { kDecode = 0, kVerify = 1, kVerifyDelta = 2 };
 // obuf[]: unnormalised outputs of a multi-token call, normalised after the
 // recurrence (one wave per token) so the RMSNorm reduction is not on the
 // token chain.
-template <int DK, int DV, int NT, int TMAX>
+template <int DK, int DV, int NT, int TMAX, bool LR_>
 struct RecShared {
     using G = RecGeo<DK, DV, NT>;
     static constexpr int NRB = TMAX <= 8 ? 2 : 1;
     static constexpr bool DEFER = TMAX > 1;
-    static constexpr bool LR = lane_rows(TMAX);
+    static constexpr bool LR = LR_;
+    static_assert(!LR || TMAX <= 8, "lane-ordered rows are for up to 8 tokens");
     TokenLds<DK, DV, LR> tok[TMAX];
     float4 red[NRB][G::NW][2][G::CG];
     float4 obuf[DEFER ? TMAX : 1][G::CG];
@@ -426,11 +427,11 @@ __device__ __forceinline__ void rec_loads(const RecParams &p, RecItem<DK, DV, NT
 // The computation of a fetched item (it.run must be true; uniform over the
 // workgroup): conv, norms and gates, the recurrence with the state in
 // registers, the outputs and the state write.
-template <int DK, int DV, int NT, typename Tin, int TMAX, int MODE, bool STREAM>
+template <int DK, int DV, int NT, typename Tin, int TMAX, int MODE, bool STREAM, bool LR_>
 __device__ __forceinline__ void rec_run(const RecParams &p, RecItem<DK, DV, NT, Tin, TMAX> &it,
-                                        RecShared<DK, DV, NT, TMAX> &sh) {
+                                        RecShared<DK, DV, NT, TMAX, LR_> &sh) {
     using G = RecGeo<DK, DV, NT>;
-    using SH = RecShared<DK, DV, NT, TMAX>;
+    using SH = RecShared<DK, DV, NT, TMAX, LR_>;
     constexpr bool VERIFY = MODE != kDecode;
     constexpr bool DELTA = MODE == kVerifyDelta;
     constexpr int TPW = RecItem<DK, DV, NT, Tin, TMAX>::TPW;
@@ -444,7 +445,7 @@ __device__ __forceinline__ void rec_run(const RecParams &p, RecItem<DK, DV, NT, 
     float4 *s = it.s;
 
     // 2. conv (+ window update / window snapshots)
-    conv_compute<DK, DV, NT, Tin, TMAX, VERIFY, DELTA>(p, tid, b, h, slot, T, it.cr, tok);
+    conv_compute<DK, DV, NT, Tin, TMAX, VERIFY, DELTA, LR>(p, tid, b, h, slot, T, it.cr, tok);
     __syncthreads();
     // 3. norms and gates, one wave per token
 #pragma unroll
@@ -581,15 +582,15 @@ __device__ __forceinline__ void rec_run(const RecParams &p, RecItem<DK, DV, NT, 
 // workgroups per CU (its registers would allow four): with four, the
 // batch-64 step measured about 2% slower (more tiles contending for the same
 // bandwidth), while single-round launches gain nothing from the fourth.
-template <int DK, int DV, int NT, typename Tin, int TMAX, int MODE, bool STREAM>
+template <int DK, int DV, int NT, typename Tin, int TMAX, int MODE, bool STREAM, bool LR>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, MODE == kDecode ? 3 : 8)))
 void kda_recurrent_kernel(RecParams p) {
-    __shared__ RecShared<DK, DV, NT, TMAX> sh;
+    __shared__ RecShared<DK, DV, NT, TMAX, LR> sh;
     RecItem<DK, DV, NT, Tin, TMAX> it;
     rec_resolve<DK, DV, NT, Tin, TMAX, MODE>(p, blockIdx.x, it);
     rec_side<DK, DV, NT, Tin, TMAX, MODE>(p, it);
     rec_loads<DK, DV, NT, Tin, TMAX, MODE, STREAM>(p, it);
-    if (it.run) rec_run<DK, DV, NT, Tin, TMAX, MODE, STREAM>(p, it, sh);
+    if (it.run) rec_run<DK, DV, NT, Tin, TMAX, MODE, STREAM, LR>(p, it, sh);
 }
 
 // Commit: copy the snapshot of the last accepted token into the live slot.
@@ -683,18 +684,25 @@ __global__ __launch_bounds__(NT) void kda_commit_delta_kernel(CommitDeltaParams 
 #endif
 constexpr int kRecThreads = KDA_REC_THREADS;   // lanes per (sequence, head) workgroup
 
+// Workgroups resident at once on the 256 CUs at three per CU: a verify grid
+// up to this size is one round, and takes the lane-ordered token rows.
+constexpr long long kOneRoundWorkgroups = 3 * 256;
+
 template <int DK, int DV, typename Tin, bool STREAM, int MODE>
 static void launch_rec_mode(const RecParams &p, hipStream_t stream) {
     const dim3 grid((unsigned)(p.B * p.H)), block(kRecThreads);
     if (MODE == kDecode) {
-        hipLaunchKernelGGL((kda_recurrent_kernel<DK, DV, kRecThreads, Tin, 1, kDecode, STREAM>), grid, block,
+        hipLaunchKernelGGL((kda_recurrent_kernel<DK, DV, kRecThreads, Tin, 1, kDecode, STREAM, false>), grid,
+                           block, 0, stream, p);
+    } else if (p.T <= 8 && (long long)p.B * p.H <= kOneRoundWorkgroups) {
+        hipLaunchKernelGGL((kda_recurrent_kernel<DK, DV, kRecThreads, Tin, 8, MODE, STREAM, true>), grid, block,
                            0, stream, p);
     } else if (p.T <= 8) {
-        hipLaunchKernelGGL((kda_recurrent_kernel<DK, DV, kRecThreads, Tin, 8, MODE, STREAM>), grid, block,
-                           0, stream, p);
-    } else {
-        hipLaunchKernelGGL((kda_recurrent_kernel<DK, DV, kRecThreads, Tin, kMaxDraft, MODE, STREAM>), grid,
+        hipLaunchKernelGGL((kda_recurrent_kernel<DK, DV, kRecThreads, Tin, 8, MODE, STREAM, false>), grid,
                            block, 0, stream, p);
+    } else {
+        hipLaunchKernelGGL((kda_recurrent_kernel<DK, DV, kRecThreads, Tin, kMaxDraft, MODE, STREAM, false>),
+                           grid, block, 0, stream, p);
     }
 }
 

@@ -61,10 +61,10 @@ def test_verify_matches_oracle_outputs_and_snapshots():
     assert cache.err_flag.item() == 0
 
 
+@pytest.mark.parametrize("B,H", [(12, 8), (40, 32)])
 @pytest.mark.parametrize("T", [8, 3, 16])
-def test_verify_commit_equals_decode_bitwise(T):
-    B = 12
-    dl, _, cache, live, snaps, s0, w0, inp, g = setup_case(B, T, H=8, seed=800 + T)
+def test_verify_commit_equals_decode_bitwise(T, B, H):
+    dl, _, cache, live, snaps, s0, w0, inp, g = setup_case(B, T, H=H, seed=800 + T + B)
     acc = g.integers(0, T + 1, size=B).astype(np.int32)
     acc[0], acc[1] = 0, T
     ref = api.Cache(cache.state.clone(), cache.conv_state.clone(), torch.zeros_like(cache.err_flag))
@@ -196,11 +196,13 @@ def test_verify_delta_matches_oracle_and_records():
         assert np.array_equal(host(cache.conv_state[int(live[b])]), orc["snap_window"][b, L - 1])
 
 
+# (12, 8): a grid within one round (lane-ordered token rows for T <= 8);
+# (40, 32): 1280 workgroups, more than one round (per-row reads)
+@pytest.mark.parametrize("B,H", [(12, 8), (40, 32)])
 @pytest.mark.parametrize("T", [8, 3, 16])
 @pytest.mark.parametrize("stream_state", [False, True])
-def test_verify_delta_commit_equals_decode_bitwise(T, stream_state):
-    B = 12
-    dl, _, cache, live, snaps, s0, w0, inp, g = setup_case(B, T, H=8, seed=900 + T)
+def test_verify_delta_commit_equals_decode_bitwise(T, stream_state, B, H):
+    dl, _, cache, live, snaps, s0, w0, inp, g = setup_case(B, T, H=H, seed=900 + T + B)
     dl.stream_state = stream_state
     acc = g.integers(0, T + 1, size=B).astype(np.int32)
     acc[0], acc[1] = 0, T
