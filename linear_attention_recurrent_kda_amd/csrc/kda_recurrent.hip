@@ -79,11 +79,11 @@ struct RecGeo {
 // q | k | v; the norm pass overwrites q and k with q^ and k^ in place.
 // With LR, rows[0..2] hold alpha, k^ and q^ again, ordered for the
 // recurrence: the RPT rows a lane owns (rg, rg + RG, ...) are consecutive,
-// at rg * RPT, so a lane reads them with 16-byte loads.  Verify launches of
-// 2 to 8 tokens whose grid fits the GPU at once use it (the token chain is
-// then the critical path); larger grids measured slower with the extra LDS,
-// 16 tokens would lose a workgroup per CU to it, and the one-token decode
-// measured no faster with it.
+// at rg * RPT, so a lane reads them with 16-byte loads.  Verify launches
+// whose grid fits the GPU at once use it (the token chain is then the
+// critical path): up to 8 tokens at three workgroups per CU, 16 tokens at
+// two (its LDS allows no more).  Larger grids measured slower with the extra
+// LDS, and the one-token decode no faster.
 
 template <int DK, int DV, bool LR>
 struct alignas(16) TokenLds {
@@ -336,7 +336,6 @@ struct RecShared {
     static constexpr int NRB = TMAX <= 8 ? 2 : 1;
     static constexpr bool DEFER = TMAX > 1;
     static constexpr bool LR = LR_;
-    static_assert(!LR || TMAX <= 8, "lane-ordered rows are for up to 8 tokens");
     TokenLds<DK, DV, LR> tok[TMAX];
     float4 red[NRB][G::NW][2][G::CG];
     float4 obuf[DEFER ? TMAX : 1][G::CG];
@@ -684,9 +683,10 @@ __global__ __launch_bounds__(NT) void kda_commit_delta_kernel(CommitDeltaParams 
 #endif
 constexpr int kRecThreads = KDA_REC_THREADS;   // lanes per (sequence, head) workgroup
 
-// Workgroups resident at once on the 256 CUs at three per CU: a verify grid
-// up to this size is one round, and takes the lane-ordered token rows.
-constexpr long long kOneRoundWorkgroups = 3 * 256;
+// Workgroups resident at once on the 256 CUs: three per CU for verify
+// kernels of up to 8 tokens, two for 16 tokens with the lane-ordered rows.
+// A grid up to that size is one round and takes the lane-ordered rows.
+constexpr long long kOneRoundWorkgroups = 3 * 256, kOneRoundWorkgroups16 = 2 * 256;
 
 template <int DK, int DV, typename Tin, bool STREAM, int MODE>
 static void launch_rec_mode(const RecParams &p, hipStream_t stream) {
@@ -700,6 +700,9 @@ static void launch_rec_mode(const RecParams &p, hipStream_t stream) {
     } else if (p.T <= 8) {
         hipLaunchKernelGGL((kda_recurrent_kernel<DK, DV, kRecThreads, Tin, 8, MODE, STREAM, false>), grid,
                            block, 0, stream, p);
+    } else if ((long long)p.B * p.H <= kOneRoundWorkgroups16) {
+        hipLaunchKernelGGL((kda_recurrent_kernel<DK, DV, kRecThreads, Tin, kMaxDraft, MODE, STREAM, true>),
+                           grid, block, 0, stream, p);
     } else {
         hipLaunchKernelGGL((kda_recurrent_kernel<DK, DV, kRecThreads, Tin, kMaxDraft, MODE, STREAM, false>),
                            grid, block, 0, stream, p);
