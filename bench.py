@@ -228,10 +228,11 @@ def load_traffic():
     return rec.get("hbm_bytes_per_launch")
 
 
-def timed(torch, stream, fn, reps):
+def timed(torch, stream, fn, reps, warm=1):
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
-    fn()
+    for _ in range(warm):
+        fn()
     torch.cuda.synchronize()
     a.record(stream)
     for _ in range(reps):
@@ -326,8 +327,8 @@ def extras(torch, api, synth, layer, cache, step_inputs, y, slots, B, H, dk, dv,
                             .astype(np.int32)).to("cuda:0").reshape(Bv, T)
     yv = torch.empty((Bv, T, H, dv), device="cuda:0")
     acc = td(synth.accepted_lengths(g, Bv, T), torch.int32)
-    sv = timed(torch, stream, api.prepared(api.kda_spec_verify, layer, cache, live, rest, vinp, yv), 20)
-    sc = timed(torch, stream, api.prepared(api.kda_spec_commit, layer, cache, live, rest, acc), 20)
+    sv = timed(torch, stream, api.prepared(api.kda_spec_verify, layer, cache, live, rest, vinp, yv), 100, warm=10)
+    sc = timed(torch, stream, api.prepared(api.kda_spec_commit, layer, cache, live, rest, acc), 100, warm=10)
     vb = verify_bytes_per_seq_head(T, dk, dv, Bv) * Bv * H
     Lm = float(acc.float().mean().item())
     cb = Bv * H * (dk * dv * 4 + 3 * (2 * dk + dv) * 2) * 2
@@ -335,15 +336,15 @@ def extras(torch, api, synth, layer, cache, step_inputs, y, slots, B, H, dk, dv,
                                 "algorithmic_gbs": vb / sv / 1e9, "frac_of_8tbs": vb / sv / 8e12}
     # the snapshots are written once and read at most once (by the commit):
     # the same call with non-temporal state traffic
-    svs = timed(torch, stream, api.prepared(api.kda_spec_verify, sl_layer, cache, live, rest, vinp, yv), 20)
+    svs = timed(torch, stream, api.prepared(api.kda_spec_verify, sl_layer, cache, live, rest, vinp, yv), 100, warm=10)
     ex["spec_verify_b16_t8_stream"] = {"us_per_call": svs * 1e6, "token_heads_per_s": Bv * T * H / svs,
                                        "algorithmic_gbs": vb / svs / 1e9, "frac_of_8tbs": vb / svs / 8e12}
     ex["spec_commit_b16"] = {"us_per_call": sc * 1e6, "mean_accepted": Lm,
                              "algorithmic_gbs": cb / sc / 1e9}
     # replayable deltas instead of snapshots (same workload, same accepted lengths)
     delta = api.new_spec_delta(layer, Bv, T, torch.bfloat16, "cuda:0")
-    svd = timed(torch, stream, api.prepared(api.kda_spec_verify_delta, layer, cache, live, vinp, yv, delta), 20)
-    scd = timed(torch, stream, api.prepared(api.kda_spec_commit_delta, layer, cache, live, delta, acc), 20)
+    svd = timed(torch, stream, api.prepared(api.kda_spec_verify_delta, layer, cache, live, vinp, yv, delta), 100, warm=10)
+    scd = timed(torch, stream, api.prepared(api.kda_spec_commit_delta, layer, cache, live, delta, acc), 100, warm=10)
     vdb = verify_delta_bytes_per_seq_head(T, dk, dv, Bv) * Bv * H
     cdb = sum(commit_delta_bytes_per_seq_head(int(L), dk, dv) for L in acc.cpu().tolist()) * H
     ex["spec_verify_delta_b16_t8"] = {"us_per_call": svd * 1e6, "token_heads_per_s": Bv * T * H / svd,
