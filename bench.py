@@ -6,11 +6,21 @@ sequences, H = 32 heads, d_k = d_v = 128, bf16 inputs, fp32 states in a
 SiLU, L2 norms, gates, the state read / delta update / write, RMSNorm and the
 output gate.  Inputs for every step are resident in HBM before timing starts.
 
-Prints ONE JSON line: the metric (token·heads/s), the roofline object of the
-decode kernel (algorithmic bytes per launch over the mean launch duration from
-HIP events on the launch stream), the fp64 oracle timed on the host cores on a
-bounded sample, and side measurements (MALL-defeating cold variant, copy
-ceiling, spec-verify/commit, chunked prefill).
+The timed steps rotate over 16 disjoint 64-slot sets of the pool (step t uses
+set t mod 16), so every step's 128 MiB of state was last touched 15 steps
+(about 2 GiB of state traffic) earlier and has left the 256 MB Infinity
+Cache: each step streams its states from HBM, as a serving step over many
+KDA layers does.  The decode runs with its default flags (state traffic
+streamed).  The same 64 slots re-used every step (cache-resident) are timed
+as a side measurement.
+
+Prints ONE JSON line: the metric (token·heads/s over the median of 5 timed
+repetitions of K steps), the roofline object of the decode kernel
+(algorithmic bytes per launch over the mean launch duration from HIP events
+on the launch stream, beside the rocprofv3 mean of the committed profile),
+the fp64 oracle timed on the host cores on bounded samples, and side
+measurements (cache-resident variant, copy ceilings, spec-verify/commit,
+chunked prefill, batch-1 decode, mixed batches).
 
   python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--no-cpu-baseline]
                   [--no-extras]
@@ -134,7 +144,11 @@ def main():
     state = (torch.randn((n_slots, H, dk, dv), generator=gen, device=dev) * 0.05)
     win = torch.randn((n_slots, H, 3, 2 * dk + dv), generator=gen, device=dev).to(torch.bfloat16)
     cache = api.Cache(state, win, torch.zeros(1, dtype=torch.int32, device=dev))
-    slots = td(synth.slot_table(g, B, n_slots), torch.int32)
+    # the random slot table of every step: a seeded permutation of the pool
+    # cut into n_slots / B disjoint sets, step t on set t mod n_sets
+    perm = synth.slot_table(g, n_slots, n_slots)
+    n_sets = n_slots // B
+    sets = td(perm.reshape(n_sets, B), torch.int32)
     # inputs of every step, resident in HBM before timing
     nsteps = W + K
     inp = synth.token_inputs(g, (nsteps, B), H, dk, dv, "bf16")
@@ -144,24 +158,27 @@ def main():
     y = torch.empty((B, H, dv), device=dev)
     stream = torch.cuda.current_stream()
     # every launch's arguments are marshalled before timing starts
-    calls = [api.kda_decode_prepared(layer, cache, slots, step_inputs[t], y) for t in range(nsteps)]
+    calls = [api.kda_decode_prepared(layer, cache, sets[t % n_sets], step_inputs[t], y) for t in range(nsteps)]
 
     for t in range(W):
         calls[t]()
     torch.cuda.synchronize()
-    # timed region: K back-to-back launches between two events on the launch
-    # stream; the mean launch duration is their span / K (launch gaps included)
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for i in range(K):
-        calls[W + i]()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    mean_kern_s = e0.elapsed_time(e1) / 1e3 / K
+    # REPS timed regions of K back-to-back launches each, between two events
+    # on the launch stream (the mean launch duration is their span / K, launch
+    # gaps included) and a synchronised wall clock; the median one is reported
+    reps = []
+    for _ in range(REPS):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for i in range(K):
+            calls[W + i]()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        reps.append((time.perf_counter() - t0, e0.elapsed_time(e1) / 1e3 / K))
+    wall, mean_kern_s = sorted(reps)[len(reps) // 2]
     bytes_launch = decode_bytes_per_token_head(H, dk, dv, B) * B * H
     achieved = bytes_launch / mean_kern_s / 1e9
     value = B * H * K / wall
@@ -181,7 +198,12 @@ def main():
         "data": "synthetic",
         "config": {"workload": "decode_b64", "B": B, "H": H, "d_k": dk, "d_v": dv,
                    "n_slots": n_slots, "input_dtype": "bf16", "state_dtype": "f32",
-                   "seed": cfg["seed"], "parallelism": "single-gpu"},
+                   "seed": cfg["seed"], "parallelism": "single-gpu",
+                   "slot_tables": f"{n_sets} disjoint {B}-slot sets of a seeded permutation of the pool, "
+                                  f"step t on set t mod {n_sets}: every step's states come from HBM",
+                   "flags": "default (state traffic streamed)"},
+        "repetitions": {"count": REPS, "ms_per_step_wall": [r[0] / K * 1e3 for r in reps],
+                        "mean_launch_us_events": [r[1] * 1e6 for r in reps], "reported": "median by wall"},
         "achieved_gbs_wall": bytes_launch * K / wall / 1e9,
         "roofline": {
             "bound": "hbm",
@@ -190,16 +212,24 @@ def main():
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": None,
-            "kernel": "kda_recurrent_kernel<128,128,256,bf16,1,decode>",
+            "kernel": DECODE_KERNEL,
             "bytes_per_launch": bytes_launch,
             "mean_launch_us": mean_kern_s * 1e6,
+            "residency": "states not cache-resident (slot sets rotated; 2 GiB pool > 256 MB Infinity Cache)",
         },
     }
-    traffic = load_traffic()
+    prof = load_profile("decode_b64_kernel_trace.json")
+    if prof is not None:
+        # the committed rocprofv3 trace of this command's decode launches
+        out["roofline"]["rocprof_mean_launch_us"] = prof["mean_ns"] / 1e3
+        out["roofline"]["frac_rocprof"] = bytes_launch / (prof["mean_ns"] * 1e-9) / 1e9 / HBM_PEAK_GBS
+    traffic = load_profile("decode_b64_traffic.json")
     if traffic is not None:
         # counter bytes per launch over the same mean launch duration (GB/s)
-        out["roofline"]["traffic"] = traffic / mean_kern_s / 1e9
-        out["roofline"]["traffic_bytes_per_launch"] = traffic
+        tb = traffic["fabric_bytes_per_launch"]
+        out["roofline"]["traffic"] = tb / mean_kern_s / 1e9
+        out["roofline"]["traffic_bytes_per_launch"] = tb
+        out["roofline"]["traffic_over_algorithmic"] = tb / bytes_launch
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -209,23 +239,31 @@ def main():
         del src, dst
 
     if not args.no_extras:
-        out["extras"] = extras(torch, api, synth, layer, cache, step_inputs, y, slots, B, H, dk, dv,
+        out["extras"] = extras(torch, api, synth, layer, cache, step_inputs, y, sets, B, H, dk, dv,
                                n_slots, W, K, stream)
+        ceil = out["extras"]["inplace_probe_2gib"]["gbs"]
+        out["roofline"]["inplace_ceiling_gbs"] = ceil
+        out["roofline"]["frac_of_inplace_ceiling"] = achieved / ceil
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(synth, p, inp, B, H, dk, dv)
     print(json.dumps(out), flush=True)
 
 
-def load_traffic():
-    """HBM bytes per launch of the decode kernel from the committed rocprofv3
-    counter summary, if it was taken on the current kernel source."""
-    path = os.path.join(ROOT, "profiles", "decode_b64_traffic.json")
+# the decode instance the timed steps launch (streamed state traffic)
+DECODE_KERNEL = "kda::kda_recurrent_kernel<128, 128, 256, unsigned short, 1, 0, true, false>"
+REPS = 5
+
+
+def load_profile(name):
+    """A committed profile summary (JSON under profiles/) if it was taken on
+    the current decode kernel source, else None."""
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
     if rec.get("kernel_source_hash") != kernel_source_hash():
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec
 
 
 def timed(torch, stream, fn, reps, warm=1):
@@ -242,78 +280,69 @@ def timed(torch, stream, fn, reps, warm=1):
     return a.elapsed_time(b) / 1e3 / reps
 
 
-def extras(torch, api, synth, layer, cache, step_inputs, y, slots, B, H, dk, dv, n_slots, W, K, stream):
+def extras(torch, api, synth, layer, cache, step_inputs, y, sets, B, H, dk, dv, n_slots, W, K, stream):
     ex = {}
-    # cold variant: 16 disjoint 64-slot sets rotated per step (2 GiB working
-    # set, larger than the 256 MB Infinity Cache)
-    perm = torch.from_numpy(np.random.default_rng(7).permutation(n_slots).astype(np.int32)).to("cuda:0")
-    sets = perm.reshape(n_slots // B, B)
-    nrot = sets.shape[0]
-    steps = min(K, len(step_inputs) - W)
-    warm = [api.kda_decode_prepared(layer, cache, sets[t], step_inputs[t % len(step_inputs)], y)
-            for t in range(nrot)]
-    calls = [api.kda_decode_prepared(layer, cache, sets[i % nrot], step_inputs[W + i], y)
-             for i in range(steps)]
-    for c in warm:
-        c()
-    torch.cuda.synchronize()
-    a = torch.cuda.Event(enable_timing=True)
-    b = torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for c in calls:
-        c()
-    b.record(stream)
-    torch.cuda.synchronize()
-    s = a.elapsed_time(b) / 1e3 / steps
     bl = decode_bytes_per_token_head(H, dk, dv, B) * B * H
-    ex["decode_b64_cold"] = {"us_per_step": s * 1e6, "token_heads_per_s": B * H / s,
-                             "algorithmic_gbs": bl / s / 1e9, "frac_of_8tbs": bl / s / 8e12}
-    # the same two workloads with non-temporal state traffic (KDA_STREAM_STATE)
-    sl_layer = api.Layer(layer.A, layer.conv_wt, layer.norm_w, layer.q_scale, layer.l2_eps,
-                         layer.rms_eps, layer.conv_silu, stream_state=True)
-    for name, sl_fn in (("decode_b64_stream", lambda i: slots), ("decode_b64_cold_stream", lambda i: sets[i % nrot])):
-        cl = [api.kda_decode_prepared(sl_layer, cache, sl_fn(i), step_inputs[W + i], y) for i in range(steps)]
-        for c in cl[:nrot]:
+    steps = min(K, len(step_inputs) - W)
+    n_sets = sets.shape[0]
+
+    def decode_leg(lay, slot_fn, note):
+        cl = [api.kda_decode_prepared(lay, cache, slot_fn(i), step_inputs[W + i], y) for i in range(steps)]
+        for c in cl[:n_sets]:
             c()
         torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
         a.record(stream)
         for c in cl:
             c()
         b.record(stream)
         torch.cuda.synchronize()
         s = a.elapsed_time(b) / 1e3 / steps
-        ex[name] = {"us_per_step": s * 1e6, "token_heads_per_s": B * H / s,
-                    "algorithmic_gbs": bl / s / 1e9, "frac_of_8tbs": bl / s / 8e12}
+        return {"us_per_step": s * 1e6, "token_heads_per_s": B * H / s, "algorithmic_gbs": bl / s / 1e9,
+                "frac_of_8tbs": bl / s / 8e12, "residency": note}
+
+    resident = api.Layer(layer.A, layer.conv_wt, layer.norm_w, layer.q_scale, layer.l2_eps,
+                         layer.rms_eps, layer.conv_silu, state_resident=True)
+    hot = sets[0]
+    # the same 64 slots every step: their 128 MiB of state stays in the 256 MB
+    # Infinity Cache between steps, so these figures are cache bandwidth, not HBM
+    ex["decode_b64_hot_resident_flag"] = decode_leg(
+        resident, lambda i: hot, "Infinity-Cache resident (same slots every step), KDA_STATE_RESIDENT")
+    ex["decode_b64_hot_default"] = decode_leg(
+        layer, lambda i: hot, "Infinity-Cache resident (same slots every step), default flags (streamed)")
+    # the headline's rotation with the resident hint given wrongly
+    ex["decode_b64_cold_resident_flag"] = decode_leg(
+        resident, lambda i: sets[i % n_sets], "from HBM (rotated slot sets), KDA_STATE_RESIDENT")
     # DRAM-bound large batch: every slot of the pool in one call (n_slots
-    # sequences; 2 GiB of state at H=32, d=128, eight times the Infinity
-    # Cache, so the call streams by itself)
+    # sequences; 2 GiB of state at H=32, d=128, eight times the Infinity Cache)
     Bl = n_slots
     gl = synth.rng(11)
     linp = synth.token_inputs(gl, (Bl,), H, dk, dv, "bf16")
     LI = api.Inputs(*(torch.from_numpy(np.ascontiguousarray(linp[k])).to("cuda:0").to(torch.bfloat16)
                       for k in ("x_q", "x_k", "x_v", "g", "b", "z")))
     yl = torch.empty((Bl, H, dv), device="cuda:0")
-    s = timed(torch, stream, api.prepared(api.kda_decode, layer, cache, perm, LI, yl), 10)
+    s = timed(torch, stream, api.prepared(api.kda_decode, layer, cache, sets.reshape(-1), LI, yl), 10)
     bll = decode_bytes_per_token_head(H, dk, dv, Bl) * Bl * H
     ex["decode_b%d_dram" % Bl] = {"us_per_step": s * 1e6, "token_heads_per_s": Bl * H / s,
                                   "algorithmic_gbs": bll / s / 1e9, "frac_of_8tbs": bll / s / 8e12,
                                   "state_bytes": Bl * H * dk * dv * 4}
     del LI, yl
-    # copy ceiling (1 GiB each way)
+    # memory ceilings: the probe copies n floats with 16-byte non-temporal
+    # buffer loads and stores, a one-round grid, 8 loads in flight per lane.
+    # In place (dst = src: read then rewrite the same bytes, the decode's
+    # pattern) over 2 GiB, and as a copy between two 1 GiB buffers
+    n = 1 << 29
+    buf = torch.empty(n, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    s = timed(torch, stream, lambda: api.kda_copy_probe(buf, buf), 10)
+    ex["inplace_probe_2gib"] = {"gbs": 2 * n * 4 / s / 1e9, "us": s * 1e6,
+                                "note": "read + rewrite of 2 GiB in place (HBM)"}
+    del buf
     n = 1 << 28
     src = torch.empty(n, dtype=torch.float32, device="cuda:0").fill_(1.0)
     dst = torch.empty_like(src)
     s = timed(torch, stream, lambda: api.kda_copy_probe(dst, src), 10)
-    ex["copy_probe_1gib"] = {"gbs": 2 * n * 4 / s / 1e9, "us": s * 1e6}
-    del src, dst
-    # the same copy over 128 MiB each way, repeated: the size of the decode's
-    # state traffic per step, resident in the 256 MB Infinity Cache like the
-    # hot decode's state
-    n = 1 << 25
-    src = torch.empty(n, dtype=torch.float32, device="cuda:0").fill_(1.0)
-    dst = torch.empty_like(src)
-    s = timed(torch, stream, lambda: api.kda_copy_probe(dst, src), 50)
-    ex["copy_probe_128mib_hot"] = {"gbs": 2 * n * 4 / s / 1e9, "us": s * 1e6}
+    ex["copy_probe_1gib"] = {"gbs": 2 * n * 4 / s / 1e9, "us": s * 1e6, "note": "1 GiB copied to another 1 GiB (HBM)"}
     del src, dst
     # spec-verify B=16 x T=8 and commit
     cfg = synth.WORKLOADS["spec_verify_b16_t8"]
@@ -322,9 +351,8 @@ def extras(torch, api, synth, layer, cache, step_inputs, y, slots, B, H, dk, dv,
     vin = synth.token_inputs(g, (Bv, T), H, dk, dv, "bf16")
     td = lambda a, dt=torch.bfloat16: torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0").to(dt)
     vinp = api.Inputs(*(td(vin[k]) for k in ("x_q", "x_k", "x_v", "g", "b", "z")))
-    live = slots[:Bv].contiguous()
-    rest = torch.from_numpy(np.setdiff1d(np.arange(n_slots), slots.cpu().numpy())[:Bv * T]
-                            .astype(np.int32)).to("cuda:0").reshape(Bv, T)
+    live = sets[0, :Bv].contiguous()
+    rest = sets[1:1 + (Bv * T + B - 1) // B].reshape(-1)[:Bv * T].reshape(Bv, T).contiguous()
     yv = torch.empty((Bv, T, H, dv), device="cuda:0")
     acc = td(synth.accepted_lengths(g, Bv, T), torch.int32)
     sv = timed(torch, stream, api.prepared(api.kda_spec_verify, layer, cache, live, rest, vinp, yv), 100, warm=10)
@@ -336,6 +364,8 @@ def extras(torch, api, synth, layer, cache, step_inputs, y, slots, B, H, dk, dv,
                                 "algorithmic_gbs": vb / sv / 1e9, "frac_of_8tbs": vb / sv / 8e12}
     # the snapshots are written once and read at most once (by the commit):
     # the same call with non-temporal state traffic
+    sl_layer = api.Layer(layer.A, layer.conv_wt, layer.norm_w, layer.q_scale, layer.l2_eps,
+                         layer.rms_eps, layer.conv_silu, stream_state=True)
     svs = timed(torch, stream, api.prepared(api.kda_spec_verify, sl_layer, cache, live, rest, vinp, yv), 100, warm=10)
     ex["spec_verify_b16_t8_stream"] = {"us_per_call": svs * 1e6, "token_heads_per_s": Bv * T * H / svs,
                                        "algorithmic_gbs": vb / svs / 1e9, "frac_of_8tbs": vb / svs / 8e12}
@@ -356,7 +386,37 @@ def extras(torch, api, synth, layer, cache, step_inputs, y, slots, B, H, dk, dv,
     ex["chunk_prefill_t32k"] = prefill_extra(torch, api, synth, stream)
     ex["decode_b1"] = decode_b1_extra(torch, api, synth)
     ex["mixed_batch"] = mixed_extra(torch, api, synth)
+    ex["metadata_build"] = metadata_extra(torch, api, stream)
     return ex
+
+
+def metadata_extra(torch, api, stream, calls=1000):
+    """kda_build_metadata at batch 1, 64 and 1024 (one-token and prompt
+    requests mixed): mean per call between events over `calls` back-to-back
+    prepared launches, and replayed from a HIP graph of 100 launches."""
+    dev = "cuda:0"
+    out = {}
+    g = np.random.default_rng(5)
+    for n in (1, 64, 1024):
+        nt = torch.from_numpy(g.choice([1, 1, 1, 500], size=n).astype(np.int32)).to(dev)
+        rs = torch.from_numpy(g.permutation(4096)[:n].astype(np.int32)).to(dev)
+        cu = torch.empty(n + 1, dtype=torch.int32, device=dev)
+        si = torch.empty(n, dtype=torch.int32, device=dev)
+        cs = torch.empty(n + 1, dtype=torch.int32, device=dev)
+        ct = torch.empty(4, dtype=torch.int32, device=dev)
+        call = api.prepared(api.kda_build_metadata, nt, rs, 4096, cu, si, cs, ct)
+        ev = timed(torch, stream, call, calls, warm=10)
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph, stream=side):
+                for _ in range(100):
+                    api.kda_build_metadata(nt, rs, 4096, cu, si, cs, ct)
+        stream.wait_stream(side)
+        gs = timed(torch, stream, graph.replay, 10, warm=1) / 100
+        out[f"batch_{n}"] = {"us_per_call_events": ev * 1e6, "us_per_call_graph": gs * 1e6}
+    return out
 
 
 def mixed_extra(torch, api, synth, prompt=4096, n_one=64):
@@ -393,17 +453,25 @@ def mixed_extra(torch, api, synth, prompt=4096, n_one=64):
 
 
 def decode_b1_extra(torch, api, synth, steps=1000, graph_steps=100):
-    """The batch-1 decode (latency-bound): B=1, H=32, d=128, one slot of a
-    256-slot pool.  Times `steps` back-to-back launches with events (launch
-    gaps included), and the same launches captured `graph_steps` at a time in
-    a HIP graph and replayed (host launch cost removed)."""
+    """The batch-1 decode (latency-bound) with default flags and with the
+    residency hint (a single sequence's 2 MiB of state per layer can stay in
+    the Infinity Cache across many layers)."""
+    return {"default": decode_b1_leg(torch, api, synth, False, steps, graph_steps),
+            "resident_flag": decode_b1_leg(torch, api, synth, True, steps, graph_steps)}
+
+
+def decode_b1_leg(torch, api, synth, resident, steps=1000, graph_steps=100):
+    """B=1, H=32, d=128, one slot of a 256-slot pool.  Times `steps`
+    back-to-back launches with events (launch gaps included), and the same
+    launches captured `graph_steps` at a time in a HIP graph and replayed
+    (host launch cost removed)."""
     dev = "cuda:0"
     cfg = synth.WORKLOADS["decode_b1"]
     H, dk, dv, n_slots = cfg["H"], cfg["d_k"], cfg["d_v"], cfg["n_slots"]
     g = synth.rng(cfg["seed"])
     p = synth.layer_params(g, H, dk, dv)
     td = lambda a, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(dt)
-    layer = api.Layer(td(p["A"]), td(p["conv_wt"]), td(p["norm_w"]))
+    layer = api.Layer(td(p["A"]), td(p["conv_wt"]), td(p["norm_w"]), state_resident=resident)
     gen = torch.Generator(device=dev)
     gen.manual_seed(cfg["seed"])
     cache = api.Cache(torch.randn((n_slots, H, dk, dv), generator=gen, device=dev) * 0.05,
@@ -556,7 +624,52 @@ def cpu_baseline(synth, p, inp, B, H, dk, dv):
                       f"over sequence x head), {el:.1f} s",
             "one_core_value": q * H * n / el1,
             "one_core_sample": f"{n} steps x {q} sequences x {H} heads on one thread, {el1:.1f} s",
-            "cpu_model": model}
+            "cpu_model": model,
+            "spec_verify_b16_t8": cpu_verify(synth, kda_oracle, OLayer, cores),
+            "chunk_prefill_t32k": cpu_prefill(synth, kda_oracle, OLayer, cores)}
+
+
+def cpu_verify(synth, kda_oracle, OLayer, cores):
+    """The oracle on one spec-verify call of the verification workload
+    (16 sequences x 8 draft tokens x 32 heads, a snapshot per token)."""
+    cfg = synth.WORKLOADS["spec_verify_b16_t8"]
+    B, T, H, dk, dv = cfg["B"], cfg["T"], cfg["H"], cfg["d_k"], cfg["d_v"]
+    g = synth.rng(cfg["seed"])
+    p = synth.layer_params(g, H, dk, dv)
+    ol = OLayer(p["A"], p["conv_wt"], p["norm_w"])
+    inp = synth.token_inputs(g, (B, T), H, dk, dv, "bf16")
+    s0 = synth.random_state(g, (B, H, dk, dv), 0.05)
+    w0 = synth.window_inputs(g, (B,), H, dk, dv, "bf16")
+    t0 = time.perf_counter()
+    kda_oracle.run(ol, s0, w0, inp["x_q"], inp["x_k"], inp["x_v"], inp["g"], inp["b"], inp["z"], snapshots=True)
+    el = time.perf_counter() - t0
+    return {"us_per_call": el * 1e6, "token_heads_per_s": B * T * H / el, "cores": cores, "kind": "oracle",
+            "sample": f"one call: {B} sequences x {T} tokens x {H} heads with a state snapshot per token"}
+
+
+def cpu_prefill(synth, kda_oracle, OLayer, cores, seg=8192):
+    """The oracle's full sequential run of the long-prompt workload (1 x 32768
+    tokens x 32 heads, every output and the final state), in segments of
+    `seg` tokens carrying the state (to bound host memory)."""
+    cfg = synth.WORKLOADS["prefill_t32k"]
+    H, dk, dv, T = cfg["H"], cfg["d_k"], cfg["d_v"], cfg["T"]
+    g = synth.rng(cfg["seed"])
+    p = synth.layer_params(g, H, dk, dv)
+    ol = OLayer(p["A"], p["conv_wt"], p["norm_w"])
+    inp = synth.token_inputs(g, (T,), H, dk, dv, "bf16")
+    st, win = np.zeros((1, H, dk, dv)), np.zeros((1, H, 3, 2 * dk + dv))
+    el = 0.0
+    for a in range(0, T, seg):
+        sub = {k: v[None, a:a + seg] for k, v in inp.items()}
+        t0 = time.perf_counter()
+        o = kda_oracle.run(ol, st, win, sub["x_q"], sub["x_k"], sub["x_v"], sub["g"], sub["b"], sub["z"])
+        el += time.perf_counter() - t0
+        st, win = o["state"], o["window"]
+        del o, sub
+    return {"us_per_call": el * 1e6, "tokens_per_s": T / el, "token_heads_per_s": T * H / el, "cores": cores,
+            "kind": "oracle",
+            "sample": f"the whole workload: {T} tokens x {H} heads token by token, in {T // seg} calls of "
+                      f"{seg} tokens carrying the state (each call's fp64 input conversion included)"}
 
 
 if __name__ == "__main__":

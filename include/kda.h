@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
 
 typedef enum kda_status {
     KDA_OK = 0,
@@ -80,16 +80,33 @@ typedef enum kda_dtype {
 
 /* flags */
 #define KDA_CONV_SILU 1u     /* SiLU after the conv (the usual setting)        */
-#define KDA_STREAM_STATE 2u  /* decode / verify: non-temporal state loads and
-                                stores.  Faster when the states a call touches
-                                do not stay cache-resident until the next call
-                                (many layers, large batches); slower when they
-                                do (a 128 MiB working set re-used call after
-                                call fits the 256 MB Infinity Cache).  Results
-                                are bitwise identical either way.  Without the
-                                flag, kda_decode streams by itself when a call
-                                touches more than 256 MiB of state
-                                (B * H * d_k * d_v * 4 bytes).                 */
+#define KDA_STREAM_STATE 2u  /* decode, verify, delta commit: non-temporal
+                                state loads and stores (raw buffer operations
+                                with the streaming cache policy).  Results are
+                                bitwise identical under every cache policy.
+                                Verify and the delta commit stream only when
+                                it is set; for kda_decode see below.          */
+#define KDA_STATE_RESIDENT 4u /* decode only, a residency hint: the states of
+                                the call stay cache-resident until the same
+                                slots are decoded again (e.g. one layer re-run
+                                back to back whose state fits the 256 MB
+                                Infinity Cache), so keep them in the caches.
+                                kda_decode's cache policy for the state tiles:
+                                  - KDA_STREAM_STATE set: streamed;
+                                  - else a call of at most 4 MiB of state
+                                    (B * H * d_k * d_v * 4 bytes; one or two
+                                    sequences at H = 32, d = 128, whose states
+                                    across all layers of a model fit the
+                                    Infinity Cache together): cached;
+                                  - else KDA_STATE_RESIDENT set and at most
+                                    256 MiB of state: cached;
+                                  - else streamed: in a serving step over many
+                                    KDA layers each layer's states are evicted
+                                    before its next step.
+                                On MI355X at B = 64, H = 32, d = 128 a step
+                                over evicted states took 51 us streamed and
+                                61 us cached; a cache-resident one 44 us
+                                cached and 51 us streamed.                     */
 
 /* Parameters of one KDA layer (device pointers, fp32). */
 typedef struct kda_layer {
@@ -100,7 +117,7 @@ typedef struct kda_layer {
     float q_scale;           /* usually d_k^-1/2                                */
     float l2_eps;            /* usually 1e-6                                    */
     float rms_eps;           /* usually 1e-6                                    */
-    uint32_t flags;          /* KDA_CONV_SILU | KDA_STREAM_STATE                */
+    uint32_t flags;          /* KDA_CONV_SILU | KDA_STREAM_STATE | KDA_STATE_RESIDENT */
 } kda_layer;
 
 /* The recurrent-state pools (device pointers). */
@@ -153,12 +170,20 @@ kda_status kda_spec_verify(const kda_layer *layer, const kda_cache *cache,
                            const kda_inputs *inputs, float *y, void *hip_stream);
 
 /*
- * kda_spec_commit -- keep the accepted prefix of a verification.
+ * kda_spec_commit -- keep the accepted prefix of a verification: after the
+ * target model has checked the draft tokens ("vLLM Kimi K3 support", section
+ * "Speculative decoding with DSpark"), the KDA state of each sequence must be
+ * the state after its accepted tokens (the pages do not say how a rejected
+ * suffix is undone; here the accepted token's snapshot is copied back).
  *   accepted_len [B] int32 (device), each in [0, T]: copies the state and
  *   window snapshot of token accepted_len[b]-1 (snap_slots[b*T + L-1]) into
  *   slot_idx[b]; L = 0 keeps the pre-verify state (no copy).  A length
  *   outside [0, T], or a needed snapshot slot of -1 / out of range, sets
  *   err_flag and leaves that sequence untouched.
+ *   L must not exceed the draft_len[b] the verification ran with: snapshots
+ *   past it were not written by that verification, and the copy cannot tell
+ *   (it would copy whatever the slot holds).  snap_slots and T must be the
+ *   ones the verification used; window_dtype is the conv_state dtype.
  */
 kda_status kda_spec_commit(const kda_layer *layer, const kda_cache *cache,
                            const int32_t *slot_idx, const int32_t *snap_slots,
@@ -278,12 +303,56 @@ kda_status kda_chunk_prefill_ckpt(const kda_layer *layer, const kda_cache *cache
                                   int32_t ckpt_per_seq, void *workspace,
                                   size_t workspace_bytes, void *hip_stream);
 
-/* Bytes of device workspace kda_chunk_prefill needs (0 on invalid sizes). */
+/* Bytes of device workspace kda_chunk_prefill and kda_chunk_prefill_ckpt
+ * need for total_T tokens in N_seq sequences (0 on invalid sizes: chunk must
+ * be 64, total_T >= 0, N_seq >= 1, a valid layer).  The workspace holds the
+ * per-chunk factors of the chunked form of the prefill ("vLLM Kimi K3
+ * support", section "Fused kernels and metadata optimisation", KDA prefill
+ * bullet) between its kernels; its contents need no initialisation and are
+ * of no use after the call. */
 size_t kda_chunk_prefill_workspace_bytes(const kda_layer *layer, int32_t total_T,
                                          int32_t N_seq, int32_t chunk);
 
-/* Measurement helper: dst[i] = src[i] for n floats (a plain streaming copy,
- * used to calibrate memory-traffic counters and the practical HBM ceiling). */
+/*
+ * kda_build_metadata -- the per-step tables of a batch, built on the device
+ * in one launch ("vLLM Kimi K3 support", section "Fused kernels and metadata
+ * optimisation", metadata builder bullet: one fused kernel instead of a chain
+ * of eager tensor operations).  The tables depend on the batch only, so one
+ * build serves every KDA layer of the step.  Inputs, per request r of the
+ * step (device int32 [n_req]):
+ *   num_tokens[r]  tokens scheduled for r this step (0: none; below 0 is a
+ *                  caller error, taken as 0);
+ *   req_slot[r]    r's state / conv-window slot, or -1.
+ * Outputs (device int32, written in full):
+ *   cu_seqlens[n_req + 1]   packed token offsets: cu_seqlens[0] = 0,
+ *                           cu_seqlens[r + 1] = cu_seqlens[r] + tokens of r
+ *                           (the kda_chunk_prefill argument);
+ *   slot_idx[n_req]         req_slot[r] when r has tokens and its slot is in
+ *                           [0, n_slots), else -1 (a padding row: its tokens'
+ *                           outputs are zeroed, no state is touched);
+ *   chunk_start[n_req + 1]  first 64-token chunk of r in the chunked prefill:
+ *                           requests of two or more tokens with a slot take
+ *                           ceil(tokens / 64) chunks, all others none;
+ *   counts[4]               total tokens, one-token requests with a slot (the
+ *                           decode rows of a mixed batch), requests of two or
+ *                           more tokens with a slot, total chunks.
+ * A negative count or a slot outside [-1, n_slots) stores 1 to err_flag
+ * (optional device int32).  The total token count must fit in int32.
+ * n_req = 0 writes cu_seqlens[0] = chunk_start[0] = 0 and zero counts (the
+ * input pointers and slot_idx may then be NULL).  Errors: KDA_ERR_SHAPE for
+ * n_req < 0 or n_slots <= 0, KDA_ERR_NULL, KDA_ERR_ALIGN (4-byte tables).
+ */
+kda_status kda_build_metadata(const int32_t *num_tokens, const int32_t *req_slot, int32_t n_req,
+                              int32_t n_slots, int32_t *cu_seqlens, int32_t *slot_idx,
+                              int32_t *chunk_start, int32_t *counts, int32_t *err_flag,
+                              void *hip_stream);
+
+/* Measurement helper: dst[i] = src[i] for n floats, with 16-byte
+ * non-temporal loads and stores from a grid that is resident at once (a
+ * streaming copy of known size: it calibrates memory-traffic counters and
+ * bounds what HBM delivers next to the KDA kernels).  dst may equal src: the
+ * data is then read and rewritten in place, the decode's own access pattern.
+ * Other overlaps are undefined.  n = 0 is a no-op. */
 kda_status kda_copy_probe(float *dst, const float *src, size_t n, void *hip_stream);
 
 /* Static text for a status code. */

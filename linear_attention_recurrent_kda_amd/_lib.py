@@ -14,6 +14,7 @@ KDA_F32 = 0
 KDA_BF16 = 1
 KDA_CONV_SILU = 1
 KDA_STREAM_STATE = 2
+KDA_STATE_RESIDENT = 4
 
 STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE",
           4: "KDA_ERR_ALIGN", 5: "KDA_ERR_UNSUPPORTED", 6: "KDA_ERR_WORKSPACE",
@@ -22,8 +23,8 @@ STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE"
 # every function include/kda.h declares
 EXPORTS = ("kda_decode", "kda_spec_verify", "kda_spec_commit", "kda_spec_delta_bytes",
            "kda_spec_verify_delta", "kda_spec_commit_delta", "kda_chunk_prefill", "kda_chunk_prefill_ckpt",
-           "kda_chunk_prefill_workspace_bytes", "kda_copy_probe", "kda_status_string",
-           "kda_abi_version")
+           "kda_chunk_prefill_workspace_bytes", "kda_build_metadata", "kda_copy_probe",
+           "kda_status_string", "kda_abi_version")
 
 
 class KdaLayer(ctypes.Structure):
@@ -89,6 +90,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                            ctypes.c_size_t, P]
     lib.kda_chunk_prefill_workspace_bytes.restype = ctypes.c_size_t
     lib.kda_chunk_prefill_workspace_bytes.argtypes = [ctypes.POINTER(KdaLayer), i32, i32, i32]
+    lib.kda_build_metadata.restype = ctypes.c_int
+    lib.kda_build_metadata.argtypes = [P, P, i32, i32, P, P, P, P, P, P]
     lib.kda_copy_probe.restype = ctypes.c_int
     lib.kda_copy_probe.argtypes = [P, P, ctypes.c_size_t, P]
     lib.kda_status_string.restype = ctypes.c_char_p

@@ -37,6 +37,7 @@ class Layer:
     rms_eps: float = 1e-6
     conv_silu: bool = True
     stream_state: bool = False          # non-temporal state traffic (KDA_STREAM_STATE)
+    state_resident: bool = False        # decode: states stay cache-resident (KDA_STATE_RESIDENT)
 
     @property
     def H(self):
@@ -65,7 +66,8 @@ class Layer:
         return _lib.KdaLayer(H, dk, dv, self.conv_w, self.A.data_ptr(), self.conv_wt.data_ptr(),
                              self.norm_w.data_ptr(), qs, self.l2_eps, self.rms_eps,
                              (_lib.KDA_CONV_SILU if self.conv_silu else 0)
-                             | (_lib.KDA_STREAM_STATE if self.stream_state else 0))
+                             | (_lib.KDA_STREAM_STATE if self.stream_state else 0)
+                             | (_lib.KDA_STATE_RESIDENT if self.state_resident else 0))
 
 
 @dataclass
@@ -84,6 +86,8 @@ class Cache:
     def c_struct(self, layer: Layer) -> _lib.KdaCache:
         _check(self.state, "state", torch.float32)
         _check(self.conv_state, "conv_state")
+        if self.conv_state.dtype not in (torch.float32, torch.bfloat16):
+            raise TypeError(f"conv_state must be float32 or bfloat16, not {self.conv_state.dtype}")
         H, dk, dv, W = layer.H, layer.d_k, layer.d_v, layer.conv_w
         if tuple(self.state.shape) != (self.n_slots, H, dk, dv):
             raise ValueError(f"state shape {tuple(self.state.shape)} != [n_slots, {H}, {dk}, {dv}]")
@@ -167,7 +171,8 @@ def _call(name: str, *args, keep=None) -> None:
 def prepared(entry, *args, **kwargs):
     """Check and marshal one call of a launching entry point of this module
     (kda_decode, kda_spec_verify, kda_spec_commit, kda_spec_verify_delta,
-    kda_spec_commit_delta, kda_chunk_prefill, kda_chunk_prefill_ckpt) once,
+    kda_spec_commit_delta, kda_chunk_prefill, kda_chunk_prefill_ckpt,
+    kda_build_metadata) once,
     without launching it; return a zero-argument callable that issues exactly
     that C call again each time (for launch loops where per-call Python
     overhead would leave the GPU idle).  The callable keeps the arguments
@@ -253,7 +258,7 @@ def kda_spec_commit(layer: Layer, cache: Cache, slot_idx: torch.Tensor, snap_slo
         raise ValueError("snap_slots must be [B, T] and accepted_len [B]")
     T = snap_slots.shape[1]
     L, C = layer.c_struct(), cache.c_struct(layer)
-    wdt = _lib.KDA_BF16 if cache.conv_state.dtype == torch.bfloat16 else _lib.KDA_F32
+    wdt = _dtype_code(cache.conv_state.dtype)
     _call("kda_spec_commit",
           ctypes.byref(L), ctypes.byref(C), slot_idx.data_ptr(), snap_slots.data_ptr(),
           accepted_len.data_ptr(), B, T, wdt, _stream(stream))
@@ -389,7 +394,30 @@ def kda_chunk_prefill_ckpt(layer: Layer, cache: Cache, slot_idx: torch.Tensor, c
           int(ckpt_slots.shape[1]), wp, wb, _stream(stream), keep=keep)
 
 
+def kda_build_metadata(num_tokens: torch.Tensor, req_slot: torch.Tensor, n_slots: int,
+                       cu_seqlens: torch.Tensor, slot_idx: torch.Tensor, chunk_start: torch.Tensor,
+                       counts: torch.Tensor, err_flag: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Per-step batch tables from per-request token counts and slots (all
+    int32 device tensors): cu_seqlens [n + 1], slot_idx [n], chunk_start
+    [n + 1], counts [4] (total tokens, one-token rows, prompts, chunks)."""
+    for name, t in (("num_tokens", num_tokens), ("req_slot", req_slot), ("cu_seqlens", cu_seqlens),
+                    ("slot_idx", slot_idx), ("chunk_start", chunk_start), ("counts", counts)):
+        _check(t, name, torch.int32)
+    n = num_tokens.numel()
+    if req_slot.numel() != n or slot_idx.numel() != n or cu_seqlens.numel() != n + 1 \
+            or chunk_start.numel() != n + 1 or counts.numel() != 4:
+        raise ValueError("table sizes must be [n], [n], [n + 1], [n], [n + 1], [4]")
+    ef = None
+    if err_flag is not None:
+        _check(err_flag, "err_flag", torch.int32)
+        ef = err_flag.data_ptr()
+    _call("kda_build_metadata", num_tokens.data_ptr(), req_slot.data_ptr(), n, int(n_slots),
+          cu_seqlens.data_ptr(), slot_idx.data_ptr(), chunk_start.data_ptr(), counts.data_ptr(), ef,
+          _stream(stream))
+
+
 def kda_copy_probe(dst: torch.Tensor, src: torch.Tensor, stream=None) -> None:
+    """dst[i] = src[i]; dst may be src itself (an in-place read and rewrite)."""
     _check(dst, "dst", torch.float32)
     _check(src, "src", torch.float32)
     if dst.numel() != src.numel():

@@ -1,11 +1,15 @@
 """Compile libkda.so (all HIP sources under csrc/) for gfx950 with hipcc.
 
-Runs on a machine without a GPU: hipcc cross-compiles the device code."""
+Runs on a machine without a GPU: hipcc cross-compiles the device code.  Each
+source is compiled to an object of its own (in parallel), then the objects
+are linked into the shared library."""
 from __future__ import annotations
 
 import glob
 import os
 import subprocess
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -13,7 +17,7 @@ LIB = os.path.join(HERE, "libkda.so")
 ARCH = "gfx950"
 
 FLAGS = [
-    "-O3", "-std=c++17", "-fPIC", "-shared", "-fvisibility=hidden",
+    "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
     f"--offload-arch={ARCH}",
     # packed fp32 arithmetic stays off: plain scalar/float4 code only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -25,16 +29,29 @@ def sources():
     return sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    hipcc = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
-    tmp = LIB + ".tmp"
-    cmd = [hipcc, *FLAGS, *extra, "-I", os.path.join(ROOT, "include"),
-           "-I", os.path.join(HERE, "csrc"), *sources(), "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+def hipcc() -> str:
+    return os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
+
+
+def build(verbose: bool = False, extra=(), out: str = LIB, jobs: int = 0) -> str:
+    """Compile every source with FLAGS + `extra` and link them into `out`."""
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc")]
+    srcs = sources()
+    with tempfile.TemporaryDirectory(prefix="kda_build_") as tmpd:
+        objs = [os.path.join(tmpd, os.path.basename(s) + ".o") for s in srcs]
+        cmds = [[hipcc(), *FLAGS, *extra, *inc, "-c", s, "-o", o] for s, o in zip(srcs, objs)]
+
+        def run(cmd):
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            subprocess.run(cmd, check=True)
+
+        with ThreadPoolExecutor(max_workers=jobs or min(len(cmds), os.cpu_count() or 1)) as ex:
+            list(ex.map(run, cmds))
+        tmp = out + ".tmp"
+        run([hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp])
+        os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -23,8 +23,13 @@ bool finite_nonneg(float x) { return isfinite(x) && x >= 0.f; }
 
 size_t elem_size(kda_dtype dt) { return dt == KDA_BF16 ? 2 : 4; }
 
-// kda_decode streams its state traffic above this many state bytes per call
-constexpr size_t kStreamAutoBytes = (size_t)256 << 20;
+// states of one call above this size cannot stay in the 256 MB Infinity
+// Cache: kda_decode streams them even under KDA_STATE_RESIDENT
+constexpr size_t kResidentMaxBytes = (size_t)256 << 20;
+// kda_decode keeps calls of at most this many state bytes cached by default:
+// a few sequences' states of every layer of a model fit the Infinity Cache
+// together (256 MB holds 128 layers of one sequence at H = 32, d = 128)
+constexpr size_t kCachedDefaultBytes = (size_t)4 << 20;
 
 kda_status check_layer(const kda_layer *L) {
     if (!L) return KDA_ERR_NULL;
@@ -32,7 +37,7 @@ kda_status check_layer(const kda_layer *L) {
     if (L->H <= 0 || L->d_k <= 0 || L->d_v <= 0 || L->conv_w <= 0) return KDA_ERR_SHAPE;
     if (!((L->d_k == 64 || L->d_k == 128) && (L->d_v == 64 || L->d_v == 128))) return KDA_ERR_UNSUPPORTED;
     if (L->conv_w != 4) return KDA_ERR_UNSUPPORTED;
-    if (L->flags & ~(KDA_CONV_SILU | KDA_STREAM_STATE)) return KDA_ERR_UNSUPPORTED;
+    if (L->flags & ~(KDA_CONV_SILU | KDA_STREAM_STATE | KDA_STATE_RESIDENT)) return KDA_ERR_UNSUPPORTED;
     if (!isfinite(L->q_scale) || !finite_nonneg(L->l2_eps) || !finite_nonneg(L->rms_eps))
         return KDA_ERR_SHAPE;
     if (!aligned(L->A, 16) || !aligned(L->conv_wt, 16) || !aligned(L->norm_w, 16)) return KDA_ERR_ALIGN;
@@ -141,10 +146,14 @@ KDA_EXPORT kda_status kda_decode(const kda_layer *layer, const kda_cache *cache,
     p.slot_idx = slot_idx;
     p.B = B;
     p.T = 1;
-    // a call whose states exceed the 256 MB Infinity Cache cannot find them
-    // cached on its next call: stream them (measured faster from 384 MiB up,
-    // slower at 256 MiB and below)
-    if ((size_t)B * layer->H * layer->d_k * layer->d_v * sizeof(float) > kStreamAutoBytes) p.stream_state = 1;
+    // cached for small calls or when the caller says its states stay
+    // cache-resident (a call over more than the Infinity Cache holds streams
+    // anyway); streamed otherwise, and always under KDA_STREAM_STATE
+    const size_t sbytes = (size_t)B * layer->H * layer->d_k * layer->d_v * sizeof(float);
+    const bool cached = !(layer->flags & KDA_STREAM_STATE) &&
+                        (sbytes <= kCachedDefaultBytes ||
+                         ((layer->flags & KDA_STATE_RESIDENT) && sbytes <= kResidentMaxBytes));
+    p.stream_state = cached ? 0 : 1;
     return launch_recurrent(p, layer->d_k, layer->d_v, inputs->dtype, RecKind::decode,
                             static_cast<hipStream_t>(hip_stream));
 }
@@ -357,6 +366,30 @@ KDA_EXPORT kda_status kda_copy_probe(float *dst, const float *src, size_t n, voi
     if (!dst || !src) return KDA_ERR_NULL;
     if (!aligned(dst, 16) || !aligned(src, 16)) return KDA_ERR_ALIGN;
     return launch_copy_probe(dst, src, n, static_cast<hipStream_t>(hip_stream));
+}
+
+KDA_EXPORT kda_status kda_build_metadata(const int32_t *num_tokens, const int32_t *req_slot, int32_t n_req,
+                                         int32_t n_slots, int32_t *cu_seqlens, int32_t *slot_idx,
+                                         int32_t *chunk_start, int32_t *counts, int32_t *err_flag,
+                                         void *hip_stream) {
+    if (n_req < 0 || n_slots <= 0) return KDA_ERR_SHAPE;
+    if (!cu_seqlens || !chunk_start || !counts) return KDA_ERR_NULL;
+    if (n_req > 0 && (!num_tokens || !req_slot || !slot_idx)) return KDA_ERR_NULL;
+    for (const void *q : {(const void *)num_tokens, (const void *)req_slot, (const void *)cu_seqlens,
+                          (const void *)slot_idx, (const void *)chunk_start, (const void *)counts,
+                          (const void *)err_flag})
+        if (q && !aligned(q, 4)) return KDA_ERR_ALIGN;
+    MetaParams p{};
+    p.num_tokens = num_tokens;
+    p.req_slot = req_slot;
+    p.n_req = n_req;
+    p.n_slots = n_slots;
+    p.cu_seqlens = cu_seqlens;
+    p.slot_idx = slot_idx;
+    p.chunk_start = chunk_start;
+    p.counts = counts;
+    p.err_flag = err_flag;
+    return launch_build_metadata(p, static_cast<hipStream_t>(hip_stream));
 }
 
 KDA_EXPORT const char *kda_status_string(kda_status s) {

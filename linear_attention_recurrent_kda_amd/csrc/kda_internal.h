@@ -84,6 +84,17 @@ struct PrefillParams {
     int ckpt_interval, ckpt_per_seq;
 };
 
+// Per-step batch metadata (kda_build_metadata).
+struct MetaParams {
+    const int32_t *num_tokens, *req_slot;   // [n_req]
+    int n_req, n_slots;
+    int32_t *cu_seqlens;    // [n_req + 1]
+    int32_t *slot_idx;      // [n_req]
+    int32_t *chunk_start;   // [n_req + 1]
+    int32_t *counts;        // [4]
+    int32_t *err_flag;      // optional
+};
+
 // most draft tokens per verification
 constexpr int kMaxDraft = 16;
 
@@ -100,5 +111,6 @@ kda_status launch_prefill(const PrefillParams &p, int d_k, int d_v, kda_dtype dt
                           hipStream_t stream);
 size_t prefill_workspace_bytes(int H, int d_k, int d_v, int total_T, int N_seq, int chunk);
 kda_status launch_copy_probe(float *dst, const float *src, size_t n, hipStream_t stream);
+kda_status launch_build_metadata(const MetaParams &p, hipStream_t stream);
 
 }  // namespace kda

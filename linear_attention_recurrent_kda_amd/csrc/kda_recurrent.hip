@@ -577,12 +577,15 @@ __device__ __forceinline__ void rec_run(const RecParams &p, RecItem<DK, DV, NT, 
     }
 }
 
+#ifndef KDA_DECODE_WPE
+#define KDA_DECODE_WPE 3
+#endif
 // One workgroup per (sequence, head) item.  Decode is held to three
 // workgroups per CU (its registers would allow four): with four, the
 // batch-64 step measured about 2% slower (more tiles contending for the same
 // bandwidth), while single-round launches gain nothing from the fourth.
 template <int DK, int DV, int NT, typename Tin, int TMAX, int MODE, bool STREAM, bool LR>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, MODE == kDecode ? 3 : 8)))
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, MODE == kDecode ? KDA_DECODE_WPE : 8)))
 void kda_recurrent_kernel(RecParams p) {
     __shared__ RecShared<DK, DV, NT, TMAX, LR> sh;
     RecItem<DK, DV, NT, Tin, TMAX> it;

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.kda_abi_version() == 1
+    assert lib.kda_abi_version() == 2
     for code in range(9):
         s = lib.kda_status_string(code)
         assert s and s != b"unknown status"
@@ -75,7 +75,7 @@ def test_decode_validation(lib):
     L.conv_w = 3
     assert decode(lib, layer=L) == 5
     L = good_layer()
-    L.flags = 6
+    L.flags = 8   # no such flag (1, 2 and 4 are defined)
     assert decode(lib, layer=L) == 5
     L = good_layer()
     L.H = 0
@@ -234,3 +234,18 @@ def test_prepared_records_only_on_its_own_thread():
     call = api.prepared(entry)
     assert seen["other"] is None and seen["own"] == []
     assert callable(call)
+
+
+def test_build_metadata_validation(lib):
+    P = ctypes.c_void_p
+    args = lambda n=4, ns=8, nt=FAKE, rs=FAKE, cu=FAKE, si=FAKE, cs=FAKE, ct=FAKE, ef=None: \
+        (P(nt) if nt else None, P(rs) if rs else None, n, ns, P(cu) if cu else None, P(si) if si else None,
+         P(cs) if cs else None, P(ct) if ct else None, P(ef) if ef else None, None)
+    assert lib.kda_build_metadata(*args(n=-1)) == 2
+    assert lib.kda_build_metadata(*args(ns=0)) == 2
+    assert lib.kda_build_metadata(*args(cu=0)) == 1
+    assert lib.kda_build_metadata(*args(ct=0)) == 1
+    assert lib.kda_build_metadata(*args(nt=0)) == 1
+    assert lib.kda_build_metadata(*args(si=0)) == 1
+    assert lib.kda_build_metadata(*args(cs=FAKE + 2)) == 4
+    assert lib.kda_build_metadata(*args(ef=FAKE + 1)) == 4

@@ -310,20 +310,23 @@ def test_repeated_runs_bitwise_identical():
 
 
 @pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (64, 128), (128, 64)])
-def test_stream_state_flag_is_bitwise_identical(dk, dv):
-    """KDA_STREAM_STATE only changes cache policy (buffer operations sized to
-    the d_k x d_v tile): decode and verify results are bitwise the same with
-    and without it, for every supported head size."""
+def test_cache_policy_flags_are_bitwise_identical(dk, dv):
+    """The cache-policy flags change only how state traffic is cached: decode
+    (streaming by default, cached under KDA_STATE_RESIDENT) and verify
+    (cached by default, streaming under KDA_STREAM_STATE) give bitwise the
+    same results under every setting, for every supported head size."""
     g = synth.rng(740 + dk + 2 * dv)
     H, B, T = 4, 6, 5
     params = synth.layer_params(g, H, dk, dv)
-    dl, _ = layer_pair(params)
-    ds, _ = layer_pair(params)
-    ds.stream_state = True
+    layers = []
+    for stream, resident in ((False, False), (True, False), (False, True), (True, True)):
+        layer, _ = layer_pair(params)
+        layer.stream_state, layer.state_resident = stream, resident
+        layers.append(layer)
     inp = synth.token_inputs(g, (B,), H, dk, dv, "bf16")
     vin = synth.token_inputs(g, (B, T), H, dk, dv, "bf16")
     outs = []
-    for layer in (dl, ds):
+    for layer in layers:
         cache = new_cache(B + B * T, H, dk, dv, "bf16", fill_seed=12)
         live = torch.arange(B, dtype=torch.int32, device=DEV)
         snaps = torch.arange(B, B + B * T, dtype=torch.int32, device=DEV).reshape(B, T)
@@ -333,8 +336,9 @@ def test_stream_state_flag_is_bitwise_identical(dk, dv):
         api.kda_spec_verify(layer, cache, live, snaps, inputs_dev(vin, "bf16"), yv)
         torch.cuda.synchronize()
         outs.append((y, yv, cache.state.clone(), cache.conv_state.clone()))
-    for a, b in zip(*outs):
-        assert torch.equal(a, b)
+    for other in outs[1:]:
+        for a, b in zip(outs[0], other):
+            assert torch.equal(a, b)
 
 
 def test_decode_in_a_hip_graph_matches_eager():
@@ -426,3 +430,34 @@ def test_large_batch_sampled_sequences():
     assert torch.equal(cache.state[untouched], before_s[untouched])
     assert torch.equal(cache.conv_state[untouched], before_w[untouched])
     assert cache.err_flag.item() == 0
+
+
+@pytest.mark.parametrize("resident", [False, True])
+def test_multi_round_batch_equals_small_batches_bitwise(resident):
+    """A batch of more (sequence, head) items than the GPU holds at once
+    (here 2560 workgroups, several rounds) gives bitwise the results of the
+    same rows decoded 16 sequences at a time, with padding and bad rows,
+    under both cache policies."""
+    g = synth.rng(1500 + int(resident))
+    B, H, dk, dv, n_slots = 80, 32, 128, 128, 200
+    params = synth.layer_params(g, H, dk, dv)
+    dl, _ = layer_pair(params)
+    dl.state_resident = resident
+    inp = synth.token_inputs(g, (B,), H, dk, dv, "bf16")
+    slots = synth.slot_table(g, B, n_slots)
+    slots[3] = -1        # padding
+    slots[41] = n_slots  # out of range
+    big = new_cache(n_slots, H, dk, dv, "bf16", fill_seed=21)
+    small = new_cache(n_slots, H, dk, dv, "bf16", fill_seed=21)
+    yb = torch.full((B, H, dv), 9.0, device=DEV)
+    api.kda_decode(dl, big, torch.from_numpy(slots).to(DEV), inputs_dev(inp, "bf16"), yb)
+    ys = torch.full((B, H, dv), 9.0, device=DEV)
+    for a in range(0, B, 16):
+        sl = slice(a, a + 16)
+        api.kda_decode(dl, small, torch.from_numpy(slots[sl].copy()).to(DEV), inputs_dev(inp, "bf16", sl),
+                       ys[a:a + 16])
+    torch.cuda.synchronize()
+    assert big.err_flag.item() == 1 and small.err_flag.item() == 1
+    assert torch.count_nonzero(yb[3]) == 0 and torch.count_nonzero(yb[41]) == 0
+    assert torch.equal(yb, ys)
+    assert torch.equal(big.state, small.state) and torch.equal(big.conv_state, small.conv_state)

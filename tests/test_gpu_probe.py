@@ -1,5 +1,5 @@
-"""The measurement copy probe moves every element (the bulk loop, the
-remainder of the grid stride and the last n % 4 floats)."""
+"""The measurement copy probe moves every element (whole and partial
+workgroup ranges, several passes per workgroup and the last n % 4 floats)."""
 import pytest
 import torch
 
@@ -9,7 +9,7 @@ from linear_attention_recurrent_kda_amd import api
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("n", [1, 7, 4096, (1 << 20) + 3, (1 << 23) + 1])
+@pytest.mark.parametrize("n", [1, 7, 4096, (1 << 20) + 3, (1 << 23) + 1, (1 << 25) + 13])
 def test_copy_probe_copies_everything(n):
     src = torch.arange(n, dtype=torch.float32, device=DEV)
     dst = torch.full_like(src, -1.0)
