@@ -28,7 +28,8 @@
  * Conventions for every call
  *   - Tensor pointers are DEVICE pointers to row-major, contiguous arrays;
  *     the caller owns them.  The library allocates nothing, keeps no pointer
- *     after a call returns and holds no mutable global state (reentrant).
+ *     after a call returns and holds no mutable global state (reentrant),
+ *     except for kda_chunk_prefill_static and its static workspace.
  *   - Calls are asynchronous on `hip_stream` (a hipStream_t; NULL = the
  *     default stream).  The returned status covers host-side validation,
  *     done before any HIP call, and the launch itself; it never waits for
@@ -302,6 +303,28 @@ kda_status kda_chunk_prefill_ckpt(const kda_layer *layer, const kda_cache *cache
                                   const int32_t *ckpt_slots, int32_t ckpt_interval,
                                   int32_t ckpt_per_seq, void *workspace,
                                   size_t workspace_bytes, void *hip_stream);
+
+/*
+ * kda_chunk_prefill_static -- kda_chunk_prefill for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  It takes no workspace: the call runs in
+ * a device array of KDA_STATIC_WORKSPACE_BYTES inside the library (one per
+ * GPU the library runs on, held until the process ends; its address is
+ * looked up on the first call on each device, which must be the current
+ * device).  Nothing is allocated or freed.  A call whose workspace
+ * (kda_chunk_prefill_workspace_bytes) exceeds the array returns
+ * KDA_ERR_WORKSPACE before any HIP call (at H = 32, d_k = d_v = 128 the array
+ * holds one sequence of up to 2048 tokens, or somewhat fewer tokens over
+ * several sequences).  Every call on one GPU shares that GPU's array: calls
+ * that overlap on one GPU (several streams, several host threads) race and
+ * must be serialised by the caller.  Arguments, results and errors are
+ * otherwise exactly those of kda_chunk_prefill.
+ */
+#define KDA_STATIC_WORKSPACE_BYTES ((size_t)256 << 20)
+kda_status kda_chunk_prefill_static(const kda_layer *layer, const kda_cache *cache,
+                                    const int32_t *slot_idx, const int32_t *cu_seqlens,
+                                    int32_t N_seq, int32_t total_T, int32_t chunk,
+                                    const kda_inputs *inputs, float *y, void *hip_stream);
 
 /* Bytes of device workspace kda_chunk_prefill and kda_chunk_prefill_ckpt
  * need for total_T tokens in N_seq sequences (0 on invalid sizes: chunk must

@@ -15,6 +15,7 @@ KDA_BF16 = 1
 KDA_CONV_SILU = 1
 KDA_STREAM_STATE = 2
 KDA_STATE_RESIDENT = 4
+KDA_STATIC_WORKSPACE_BYTES = 256 << 20
 
 STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE",
           4: "KDA_ERR_ALIGN", 5: "KDA_ERR_UNSUPPORTED", 6: "KDA_ERR_WORKSPACE",
@@ -23,6 +24,7 @@ STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE"
 # every function include/kda.h declares
 EXPORTS = ("kda_decode", "kda_spec_verify", "kda_spec_commit", "kda_spec_delta_bytes",
            "kda_spec_verify_delta", "kda_spec_commit_delta", "kda_chunk_prefill", "kda_chunk_prefill_ckpt",
+           "kda_chunk_prefill_static",
            "kda_chunk_prefill_workspace_bytes", "kda_build_metadata", "kda_copy_probe",
            "kda_status_string", "kda_abi_version")
 
@@ -88,6 +90,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_chunk_prefill_ckpt.argtypes = [ctypes.POINTER(KdaLayer), ctypes.POINTER(KdaCache), P, P,
                                            i32, i32, i32, ctypes.POINTER(KdaInputs), P, P, i32, i32, P,
                                            ctypes.c_size_t, P]
+    lib.kda_chunk_prefill_static.restype = ctypes.c_int
+    lib.kda_chunk_prefill_static.argtypes = [ctypes.POINTER(KdaLayer), ctypes.POINTER(KdaCache), P, P,
+                                             i32, i32, i32, ctypes.POINTER(KdaInputs), P, P]
     lib.kda_chunk_prefill_workspace_bytes.restype = ctypes.c_size_t
     lib.kda_chunk_prefill_workspace_bytes.argtypes = [ctypes.POINTER(KdaLayer), i32, i32, i32]
     lib.kda_build_metadata.restype = ctypes.c_int

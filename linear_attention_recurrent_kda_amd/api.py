@@ -172,7 +172,7 @@ def prepared(entry, *args, **kwargs):
     """Check and marshal one call of a launching entry point of this module
     (kda_decode, kda_spec_verify, kda_spec_commit, kda_spec_verify_delta,
     kda_spec_commit_delta, kda_chunk_prefill, kda_chunk_prefill_ckpt,
-    kda_build_metadata) once,
+    kda_chunk_prefill_static, kda_build_metadata) once,
     without launching it; return a zero-argument callable that issues exactly
     that C call again each time (for launch loops where per-call Python
     overhead would leave the GPU idle).  The callable keeps the arguments
@@ -375,6 +375,29 @@ def kda_chunk_prefill(layer: Layer, cache: Cache, slot_idx: torch.Tensor, cu_seq
     _call("kda_chunk_prefill",
           ctypes.byref(L), ctypes.byref(C), slot_idx.data_ptr(), cu_seqlens.data_ptr(), N, total_T,
           chunk, ctypes.byref(I), y.data_ptr(), wp, wb, _stream(stream), keep=keep)
+
+
+def kda_chunk_prefill_static(layer: Layer, cache: Cache, slot_idx: torch.Tensor, cu_seqlens: torch.Tensor,
+                             inputs: Inputs, y: torch.Tensor, chunk: int = 64, stream=None) -> None:
+    """kda_chunk_prefill in the library's static workspace: nothing is
+    allocated (for callers under graph capture or that may not allocate);
+    calls whose workspace exceeds KDA_STATIC_WORKSPACE_BYTES raise
+    KdaError (KDA_ERR_WORKSPACE).  Calls overlapping on one GPU race."""
+    _check(slot_idx, "slot_idx", torch.int32)
+    _check(cu_seqlens, "cu_seqlens", torch.int32)
+    N = slot_idx.numel()
+    if cu_seqlens.numel() != N + 1:
+        raise ValueError("cu_seqlens must be [N_seq + 1]")
+    total_T = inputs.x_q.shape[0]
+    _check(y, "y", torch.float32)
+    if tuple(y.shape) != (total_T, layer.H, layer.d_v):
+        raise ValueError("y must be [total_T, H, d_v]")
+    L, C, I = layer.c_struct(), cache.c_struct(layer), inputs.c_struct(layer, (total_T,))
+    if cache.conv_state.dtype != inputs.dtype:
+        raise TypeError("conv_state dtype must equal the input dtype")
+    _call("kda_chunk_prefill_static",
+          ctypes.byref(L), ctypes.byref(C), slot_idx.data_ptr(), cu_seqlens.data_ptr(), N, total_T,
+          chunk, ctypes.byref(I), y.data_ptr(), _stream(stream))
 
 
 def kda_chunk_prefill_ckpt(layer: Layer, cache: Cache, slot_idx: torch.Tensor, cu_seqlens: torch.Tensor,

@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "kda_internal.h"
@@ -22,6 +23,9 @@ bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 bool finite_nonneg(float x) { return isfinite(x) && x >= 0.f; }
 
 size_t elem_size(kda_dtype dt) { return dt == KDA_BF16 ? 2 : 4; }
+
+// size of the static workspace of kda_chunk_prefill_static (KDA_STATIC_WORKSPACE_BYTES)
+constexpr size_t kStaticWorkspaceBytes = KDA_STATIC_WORKSPACE_BYTES;
 
 // states of one call above this size cannot stay in the 256 MB Infinity
 // Cache: kda_decode streams them even under KDA_STATE_RESIDENT
@@ -285,11 +289,15 @@ KDA_EXPORT size_t kda_chunk_prefill_workspace_bytes(const kda_layer *layer, int3
 
 namespace {
 
+kda_status static_workspace(void **ptr, size_t *bytes);
+
+// With use_static the workspace arguments are ignored: the call runs in the
+// library's static workspace (looked up after every other check passed).
 kda_status prefill_common(const kda_layer *layer, const kda_cache *cache, const int32_t *slot_idx,
                           const int32_t *cu_seqlens, int32_t N_seq, int32_t total_T, int32_t chunk,
                           const kda_inputs *inputs, float *y, const int32_t *ckpt_slots,
                           int32_t ckpt_interval, int32_t ckpt_per_seq, void *workspace,
-                          size_t workspace_bytes, void *hip_stream) {
+                          size_t workspace_bytes, void *hip_stream, bool use_static = false) {
     KDA_TRY(check_layer(layer));
     KDA_TRY(check_cache(cache));
     if (N_seq < 1 || total_T < 0 || chunk <= 0) return KDA_ERR_SHAPE;
@@ -309,11 +317,16 @@ kda_status prefill_common(const kda_layer *layer, const kda_cache *cache, const 
     if (!slot_idx || !cu_seqlens) return KDA_ERR_NULL;
     if (!aligned(slot_idx, 4) || !aligned(cu_seqlens, 4)) return KDA_ERR_ALIGN;
     const size_t need = prefill_workspace_bytes(layer->H, layer->d_k, layer->d_v, total_T, N_seq, chunk);
-    if (need && !workspace) return KDA_ERR_NULL;
-    if (workspace_bytes < need) return KDA_ERR_WORKSPACE;
-    if (workspace && !aligned(workspace, 16)) return KDA_ERR_ALIGN;
+    if (use_static) {
+        if (need > kStaticWorkspaceBytes) return KDA_ERR_WORKSPACE;
+    } else {
+        if (need && !workspace) return KDA_ERR_NULL;
+        if (workspace_bytes < need) return KDA_ERR_WORKSPACE;
+        if (workspace && !aligned(workspace, 16)) return KDA_ERR_ALIGN;
+    }
     KDA_TRY(debug_check(slot_idx, N_seq, ckpt_slots, ckpt_slots ? (size_t)N_seq * ckpt_per_seq : 0,
                         cache->n_slots, hip_stream));
+    if (use_static) KDA_TRY(static_workspace(&workspace, &workspace_bytes));
     PrefillParams p{};
     p.A = layer->A; p.conv_wt = layer->conv_wt; p.norm_w = layer->norm_w;
     p.q_scale = layer->q_scale; p.l2_eps = layer->l2_eps; p.rms_eps = layer->rms_eps;
@@ -359,6 +372,46 @@ KDA_EXPORT kda_status kda_chunk_prefill_ckpt(const kda_layer *layer, const kda_c
     return prefill_common(layer, cache, slot_idx, cu_seqlens, N_seq, total_T, chunk, inputs, y,
                           ckpt_slots, ckpt_interval, ckpt_per_seq, workspace, workspace_bytes,
                           hip_stream);
+}
+
+// ---------------------------------------------------------------------------
+// The static workspace of kda_chunk_prefill_static: a device array of the
+// library, one copy per GPU (each device holds its own instance of the code
+// object's globals), alive until the process ends.  Host code never uses the
+// array's name as an address: the first call on a device, with that device
+// current, looks its device address up and keeps it per device.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[KDA_STATIC_WORKSPACE_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+kda_status static_workspace(void **ptr, size_t *bytes) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return KDA_ERR_LAUNCH;
+    if (dev < 0 || dev >= kMaxDevices) return KDA_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return KDA_ERR_LAUNCH;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    *bytes = kStaticWorkspaceBytes;
+    return KDA_OK;
+}
+
+}  // namespace
+
+KDA_EXPORT kda_status kda_chunk_prefill_static(const kda_layer *layer, const kda_cache *cache,
+                                               const int32_t *slot_idx, const int32_t *cu_seqlens,
+                                               int32_t N_seq, int32_t total_T, int32_t chunk,
+                                               const kda_inputs *inputs, float *y, void *hip_stream) {
+    return prefill_common(layer, cache, slot_idx, cu_seqlens, N_seq, total_T, chunk, inputs, y, nullptr, 0, 0,
+                          nullptr, 0, hip_stream, true);
 }
 
 KDA_EXPORT kda_status kda_copy_probe(float *dst, const float *src, size_t n, void *hip_stream) {

@@ -249,3 +249,17 @@ def test_build_metadata_validation(lib):
     assert lib.kda_build_metadata(*args(si=0)) == 1
     assert lib.kda_build_metadata(*args(cs=FAKE + 2)) == 4
     assert lib.kda_build_metadata(*args(ef=FAKE + 1)) == 4
+
+
+def test_prefill_static_validation(lib):
+    """kda_chunk_prefill_static rejects a call whose workspace exceeds the
+    static array before any HIP call, and checks its other arguments like
+    kda_chunk_prefill."""
+    L, C, I = good_layer(H=32), good_cache(), good_inputs()
+    call = lambda total_T, N=1, slots=FAKE, cu=FAKE, y=FAKE: lib.kda_chunk_prefill_static(
+        ctypes.byref(L), ctypes.byref(C), slots, cu, N, total_T, 64, ctypes.byref(I), y, None)
+    assert lib.kda_chunk_prefill_workspace_bytes(ctypes.byref(L), 4096, 1, 64) > _lib.KDA_STATIC_WORKSPACE_BYTES
+    assert call(4096) == 6
+    assert call(100, slots=None) == 1
+    assert call(100, y=FAKE + 4) == 4
+    assert call(100, N=0) == 2
