@@ -38,7 +38,6 @@ struct PrefillWs {
     int32_t *meta;            // [0]: 1 if cu_seqlens is valid; [1 + s]: first chunk of s, s <= N;
                               // [N + 2]: number of chunk-path sequences; [N + 3 + k]: the k-th;
                               // [2N + 3]: number of one-token sequences (decode kernel)
-    float *vv;                // [G, 64, H, d_v]  conv'd v, rows past a chunk's end unused
     uint16_t *Wn_hi, *Wn_lo;  // [G, H] x (64 x d_k)  -W
     uint16_t *Q_hi, *Q_lo;    // [G, H] x (64 x d_k)  Q^ e^G
     uint16_t *K_hi, *K_lo;    // [G, H] x (d_k x 64)  (K^ e^(G_C - G))^T
@@ -59,7 +58,7 @@ __device__ __forceinline__ size_t opnd_off(int row, int k) {
 }
 
 struct WsLayout {
-    size_t meta, vv, Wn_hi, Wn_lo, Q_hi, Q_lo, K_hi, K_lo, P_hi, P_lo, Ut, gC, total;
+    size_t meta, Wn_hi, Wn_lo, Q_hi, Q_lo, K_hi, K_lo, P_hi, P_lo, Ut, gC, total;
 };
 
 static size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
@@ -71,7 +70,6 @@ static WsLayout ws_layout(int H, int dk, int dv, int total_T, int N_seq) {
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes); return o; };
     l.meta = take(sizeof(int32_t) * (2 * (size_t)N_seq + 4));
-    l.vv = take(4 * GH * kChunk * dv);
     l.Wn_hi = take(2 * GH * kChunk * dk);
     l.Wn_lo = take(2 * GH * kChunk * dk);
     l.Q_hi = take(2 * GH * kChunk * dk);
@@ -175,9 +173,10 @@ __global__ __launch_bounds__(64) void kda_prefill_meta_kernel(PrefillParams p, P
 // exponential per term.
 //
 // LDS holds q^, k^ (rows, zero past the chunk's end), the decay prefix sums,
-// A and T: about 143 KiB at d_k = 128, one workgroup per CU.  Only v goes
-// through the workspace (L2).  The factors for the scan (P, Q^ e^G, Kd^T,
-// -W as bf16 hi/lo; U~ in fp32) are written in the order its loads read.
+// A and T: about 143 KiB at d_k = 128, one workgroup per CU.  v is convolved
+// from its raw inputs where [W | U~] needs it (no workspace round trip).  The
+// factors for the scan (P, Q^ e^G, Kd^T, -W as bf16 hi/lo; U~ in fp32) are
+// written in the order its loads read.
 // ---------------------------------------------------------------------------
 constexpr int kIntraThreads = 512;
 constexpr int kIntraWaves = kIntraThreads / kWave;
@@ -253,12 +252,11 @@ template <> struct ChRaw<float, 1> {
     __device__ static float get(T r, int) { return r; }
 };
 
-// Conv + SiLU over one of q, k, v for rows 32*HALF .. 32*HALF + 31 of a
-// chunk, one wave; the lane owns channels NC*lane .. NC*lane + NC - 1.
-// MODE 0: q (L2 norm and q scale), 1: k (L2 norm), both into LDS rows (zero
-// past n); MODE 2: v, to the chunk-padded workspace rows (all 64 rows are
-// written; rows past n hold values of no meaning).  The three inputs before
-// the chunk come from the conv window at chunk 0, else from the sequence.
+// Conv + SiLU over q or k for rows 32*HALF .. 32*HALF + 31 of a chunk, one
+// wave; the lane owns channels NC*lane .. NC*lane + NC - 1.  MODE 0: q (L2
+// norm and q scale), 1: k (L2 norm), into LDS rows (zero past n).  The three
+// inputs before the chunk come from the conv window at chunk 0, else from the
+// sequence.
 template <int NC, int MODE, int HALF, typename Tin>
 __device__ __forceinline__ void prep_rows(const PrefillParams &p, const Tin *x, const Tin *win, int choff, int CH,
                                           int c, int t0, int n, int h, int lane, float *out, size_t ostride) {
@@ -297,7 +295,7 @@ __device__ __forceinline__ void prep_rows(const PrefillParams &p, const Tin *x, 
             acc = fmaf(w[e][3], R::get(raw[j + 3], e), acc);
             y[e] = p.silu ? silu_hw(acc) : acc;
         }
-        if (MODE < 2) {
+        {
             float ss = 0.f;
 #pragma unroll
             for (int e = 0; e < NC; ++e) ss = fmaf(y[e], y[e], ss);
@@ -416,29 +414,49 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
     const int t0 = p.cu_seqlens[s] + c * kChunk;
     const int n = min(kChunk, p.cu_seqlens[s + 1] - t0);
     const size_t gh = (size_t)gidx * H + h;
-    const size_t row0 = (size_t)gidx * kChunk * H + h;   // workspace row of the chunk's first token
-    const size_t rstride = (size_t)H;                    // rows between consecutive tokens
+    constexpr int CH = 2 * DK + DV;
+    const Tin *win = static_cast<const Tin *>(p.window) + ((size_t)slot * H + h) * 3 * CH;
 
-    // 1. the chunk's tokens: waves 0-1 q^ and 2-3 k^ (LDS), 4-5 v (workspace),
-    //    a row half each; waves 6-7 the decay prefix sums (64 channels each)
-    //    and beta
+    // the raw inputs of the V operand of step 6, requested with the chunk's
+    // other inputs (the compiler widens them to fp32 right away, so a later
+    // request would stall the phase it lands in): a lane's v channel
+    // col = 16 ct + lr - d_k for rows 32 k2 + 8 lk .. + 7, plus the three rows
+    // before each run (from the conv window at chunk 0); rows past the
+    // chunk's end repeat its last row (their beta is 0)
+    constexpr int NCT = (DK + DV) / 16;          // column tiles of [W | U~]
+    Tin vraw[2][2][11];
+    float4 vwt[2];
+#pragma unroll
+    for (int ci = 0; ci < 2; ++ci) {
+        const int ct = wave + kIntraWaves * ci;
+        const int col = 16 * ct + lr - DK;
+        if (ct < DK / 16 || ct >= NCT) continue;   // wave-uniform
+        const Tin *xv = static_cast<const Tin *>(p.x_v) + (size_t)h * DV + col;
+        vwt[ci] = *reinterpret_cast<const float4 *>(p.conv_wt + ((size_t)h * CH + 2 * DK + col) * 4);
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+            for (int j = 0; j < 11; ++j) {
+                const int q = 32 * k2 + 8 * lk + j - 3;   // chunk row of the input
+                const Tin *src = q < 0 && c == 0 ? win + (q + 3) * CH + 2 * DK + col
+                                                 : xv + (size_t)(t0 + min(c == 0 ? max(q, 0) : q, n - 1)) * H * DV;
+                vraw[ci][k2][j] = *src;
+            }
+    }
+
+    // 1. the chunk's tokens: waves 0-1 q^ and 2-3 k^ (LDS), a row half each;
+    //    waves 6-7 the decay prefix sums (64 channels each) and beta.  v is
+    //    convolved where step 6 needs it (its raw inputs are fetched below).
     {
-        constexpr int CH = 2 * DK + DV, RW = IntraLds<DK, DV>::RW;
-        const Tin *win = static_cast<const Tin *>(p.window) + ((size_t)slot * H + h) * 3 * CH;
+        constexpr int RW = IntraLds<DK, DV>::RW;
         const Tin *xq = static_cast<const Tin *>(p.x_q), *xk = static_cast<const Tin *>(p.x_k);
-        const Tin *xv = static_cast<const Tin *>(p.x_v);
-        float *vrow = ws.vv + row0 * DV;   // the chunk's first row of this head
         switch (wave) {
         case 0: prep_rows<DK / 64, 0, 0>(p, xq, win, 0, CH, c, t0, n, h, lane, &L.Q[0][0], RW); break;
         case 1: prep_rows<DK / 64, 0, 1>(p, xq, win, 0, CH, c, t0, n, h, lane, &L.Q[0][0], RW); break;
         case 2: prep_rows<DK / 64, 1, 0>(p, xk, win, DK, CH, c, t0, n, h, lane, &L.K[0][0], RW); break;
         case 3: prep_rows<DK / 64, 1, 1>(p, xk, win, DK, CH, c, t0, n, h, lane, &L.K[0][0], RW); break;
         case 4:
-            prep_rows<DV / 64, 2, 0>(p, xv, win, 2 * DK, CH, c, t0, n, h, lane, vrow, rstride * DV);
-            break;
-        case 5:
-            prep_rows<DV / 64, 2, 1>(p, xv, win, 2 * DK, CH, c, t0, n, h, lane, vrow, rstride * DV);
-            break;
+        case 5: break;
         default: {
             const int gw = wave - 6;
             if (64 * gw < DK) prep_gates<DK, Tin>(p, t0, n, h, lane, 64 * gw, L.G);
@@ -450,23 +468,6 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
         }
     }
     __syncthreads();
-
-    // the V operand of step 6 is read now, so its latency hides behind steps 2-5
-    constexpr int NCT = (DK + DV) / 16;          // column tiles of [W | U~]
-    float vpre[2][2][8];
-#pragma unroll
-    for (int ci = 0; ci < 2; ++ci) {
-        const int ct = wave + kIntraWaves * ci;
-        const int col = 16 * ct + lr - DK;
-        if (ct < DK / 16 || ct >= NCT) continue;   // wave-uniform
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int sv = 32 * k2 + 8 * lk + e;
-                vpre[ci][k2][e] = ws.vv[(row0 + sv * rstride) * DV + col];
-            }
-    }
 
     // 2. per 16-token block: may the diagonal tile use the scaled factors?
     if (wave < 4) {
@@ -484,9 +485,10 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
     //    read there) go to the other waves.
     uint16_t *Ph = ws.P_hi + gh * kChunk * kChunk, *Pl = ws.P_lo + gh * kChunk * kChunk;
     for (int tile = wave; tile < 16; tile += kIntraWaves) {
-        const int lbt[16] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3, 0, 0, 0, 1, 1, 2};
-        const int lbs[16] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3, 1, 2, 3, 2, 3, 3};
-        const int bt = lbt[tile], bs = lbs[tile];
+        // tile -> (bt, bs), 2 bits per tile: bt = 0 1 1 2 2 2 3 3 3 3 0 0 0 1 1 2,
+        // bs = 0 0 1 0 1 2 0 1 2 3 1 2 3 2 3 3 (register constants: a table in
+        // memory would cost a load and a wait per tile)
+        const int bt = (int)((0x940ffa94u >> (2 * tile)) & 3u), bs = (int)((0xfb9e4910u >> (2 * tile)) & 3u);
         f32x4 aA = {0.f, 0.f, 0.f, 0.f}, aP = aA;
         if (bs > bt) {
             if (lane < 32) {
@@ -672,7 +674,17 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int sv = 32 * k2 + 8 * lk + e;
-                x[e] = isw ? L.beta[sv] * L.K[sv][col] * exp2_hw(L.G[sv][col]) : L.beta[sv] * vpre[ci][k2][e];
+                if (isw) {
+                    x[e] = L.beta[sv] * L.K[sv][col] * exp2_hw(L.G[sv][col]);
+                } else {
+                    // conv (+ SiLU) of v, as the q and k rows were formed
+                    const float4 w = vwt[ci];
+                    float acc = w.x * to_f32(vraw[ci][k2][e]);
+                    acc = fmaf(w.y, to_f32(vraw[ci][k2][e + 1]), acc);
+                    acc = fmaf(w.z, to_f32(vraw[ci][k2][e + 2]), acc);
+                    acc = fmaf(w.w, to_f32(vraw[ci][k2][e + 3]), acc);
+                    x[e] = L.beta[sv] * (p.silu ? silu_hw(acc) : acc);
+                }
             }
             rb[k2] = split8(x);
         }
@@ -1042,7 +1054,6 @@ static kda_status launch_prefill_typed(const PrefillParams &p, hipStream_t strea
     unsigned char *base = static_cast<unsigned char *>(p.workspace);
     PrefillWs ws{};
     ws.meta = reinterpret_cast<int32_t *>(base + l.meta);
-    ws.vv = reinterpret_cast<float *>(base + l.vv);
     ws.Wn_hi = reinterpret_cast<uint16_t *>(base + l.Wn_hi);
     ws.Wn_lo = reinterpret_cast<uint16_t *>(base + l.Wn_lo);
     ws.Q_hi = reinterpret_cast<uint16_t *>(base + l.Q_hi);
