@@ -314,8 +314,8 @@ kda_status kda_chunk_prefill_ckpt(const kda_layer *layer, const kda_cache *cache
  * device).  Nothing is allocated or freed.  A call whose workspace
  * (kda_chunk_prefill_workspace_bytes) exceeds the array returns
  * KDA_ERR_WORKSPACE before any HIP call (at H = 32, d_k = d_v = 128 the array
- * holds one sequence of up to 2048 tokens, or somewhat fewer tokens over
- * several sequences).  Every call on one GPU shares that GPU's array: calls
+ * holds one sequence of up to about 3500 tokens, or somewhat fewer tokens
+ * over several sequences).  Every call on one GPU shares that GPU's array: calls
  * that overlap on one GPU (several streams, several host threads) race and
  * must be serialised by the caller.  Arguments, results and errors are
  * otherwise exactly those of kda_chunk_prefill.
