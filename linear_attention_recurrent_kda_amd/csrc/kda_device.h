@@ -22,13 +22,42 @@ __device__ __forceinline__ float softplus(float x) {
     return fmaxf(x, 0.0f) + log1pf(expf(-fabsf(x)));
 }
 
-// Butterfly sum over the 64 lanes of a wave; every lane ends with the same
-// value (each pairwise add is commutative, so mirrored lanes agree bitwise).
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
-    return v;
+// Cross-lane sums on the VALU: DPP moves (a few cycles each) instead of LDS
+// permutes.  dpp_add adds the value of the lane the DPP control selects
+// (0 where that lane is masked off by the row mask).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_add(float v) {
+    const int x = __builtin_bit_cast(int, v);
+    return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, x, CTRL, ROWS, 0xF, false));
 }
+
+// Sum of v over lanes 0 .. N-1 of the wave (N = 16, 32 or 64; those lanes
+// active), returned as one wave-uniform value: pair and quad sums inside
+// each row of 16 lanes (quad permutes, half-row and row mirrors), then row
+// broadcasts carry the row sums up to lane N-1, which is read back.
+template <int N>
+__device__ __forceinline__ float lane_sum(float v) {
+    static_assert(N == 16 || N == 32 || N == 64, "rows of 16 lanes");
+    v = dpp_add<0xB1, 0xF>(v);    // quad_perm [1,0,3,2]
+    v = dpp_add<0x4E, 0xF>(v);    // quad_perm [2,3,0,1]
+    v = dpp_add<0x141, 0xF>(v);   // row_half_mirror
+    v = dpp_add<0x140, 0xF>(v);   // row_mirror
+    if (N >= 32) v = dpp_add<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
+    if (N == 64) v = dpp_add<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), N - 1));
+}
+
+// x[l] + x[l + 32] in lanes l = 0..31 (a VALU lane swap between the two
+// halves of the wave; lanes 32..63 get 2 x[l], for callers that read only
+// the lower half).  The same sum as x + __shfl_xor(x, 32) there.
+__device__ __forceinline__ float add_upper_half(float x) {
+    const unsigned v = __float_as_uint(x);
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return x + __uint_as_float(r[1]);
+}
+
+// Sum over the 64 lanes of a wave (all active); every lane gets the same value.
+__device__ __forceinline__ float wave_sum(float v) { return lane_sum<kWave>(v); }
 
 __device__ __forceinline__ float4 operator*(float4 a, float s) {
     return make_float4(a.x * s, a.y * s, a.z * s, a.w * s);

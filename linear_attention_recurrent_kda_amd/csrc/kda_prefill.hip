@@ -197,23 +197,8 @@ struct __align__(16) IntraLds {
 };
 
 // Sum over the 64 lanes of a wave (all lanes active), every lane receiving
-// the same value: DPP adds inside each row of 16 lanes (pair, quad, half-row
-// and row mirrors), row broadcasts carry the row sums up to lane 63, which is
-// read back as a scalar.
-template <int CTRL, int ROWS>
-__device__ __forceinline__ float dpp_add(float v) {
-    const int x = __builtin_bit_cast(int, v);
-    return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, x, CTRL, ROWS, 0xF, false));
-}
-__device__ __forceinline__ float wave_sum_dpp(float v) {
-    v = dpp_add<0xB1, 0xF>(v);    // quad_perm [1,0,3,2]
-    v = dpp_add<0x4E, 0xF>(v);    // quad_perm [2,3,0,1]
-    v = dpp_add<0x141, 0xF>(v);   // row_half_mirror
-    v = dpp_add<0x140, 0xF>(v);   // row_mirror
-    v = dpp_add<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
-    v = dpp_add<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
-    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
-}
+// the same value (the DPP form of kda_device.h).
+__device__ __forceinline__ float wave_sum_dpp(float v) { return lane_sum<kWave>(v); }
 
 // Hardware exp2 / log2 / reciprocal forms for the per-token preparation
 // (about 1 ulp each; the chunk algebra's bf16x3 contractions are ~1e-5).

@@ -254,58 +254,66 @@ __device__ __forceinline__ void prep_fetch(const RecParams &p, int wave, int lan
     }
 }
 
-// L2 norms, k^.q^ and gates of one token, by one whole wave.
-template <int DK, int DV, typename Tin, int TPW, int RG, int RPT, bool LR>
+// L2 norms, k^.q^ and gates of one token, by one whole wave (PART < 0), or
+// one independent part of them (PART 0: norms and k^.q^, 1: the decay
+// alpha, 2: the output gate and beta), so that a single token's preparation
+// runs on three waves at once.  Either way every value is formed by the same
+// operations.
+template <int DK, int DV, typename Tin, int TPW, int RG, int RPT, bool LR, int PART = -1>
 __device__ __forceinline__ void prep_token(const RecParams &p, int lane, int j,
                                            const PrepRegs<DK, DV, Tin, TPW> &pr,
                                            TokenLds<DK, DV, LR> &tk) {
     constexpr int EK = DK / kWave, EV = DV / kWave;
-    float qv[EK], kv[EK];
-    float sq = 0.f, sk = 0.f;
+    if (PART < 0 || PART == 0) {
+        float qv[EK], kv[EK];
+        float sq = 0.f, sk = 0.f;
 #pragma unroll
-    for (int e = 0; e < EK; ++e) {
-        qv[e] = tk.conv[lane + kWave * e];
-        kv[e] = tk.conv[DK + lane + kWave * e];
-        sq = fmaf(qv[e], qv[e], sq);
-        sk = fmaf(kv[e], kv[e], sk);
+        for (int e = 0; e < EK; ++e) {
+            qv[e] = tk.conv[lane + kWave * e];
+            kv[e] = tk.conv[DK + lane + kWave * e];
+            sq = fmaf(qv[e], qv[e], sq);
+            sk = fmaf(kv[e], kv[e], sk);
+        }
+        sq = wave_sum(sq);
+        sk = wave_sum(sk);
+        const float rq = p.q_scale / sqrtf(sq + p.l2_eps);
+        const float rk = 1.0f / sqrtf(sk + p.l2_eps);
+        float kq = 0.f;
+#pragma unroll
+        for (int e = 0; e < EK; ++e) {
+            qv[e] *= rq;
+            kv[e] *= rk;
+            kq = fmaf(qv[e], kv[e], kq);
+            tk.conv[lane + kWave * e] = qv[e];
+            tk.conv[DK + lane + kWave * e] = kv[e];
+            if (LR) {
+                const int r = lane + kWave * e, pos = (r % RG) * RPT + r / RG;
+                tk.rows[1][pos] = kv[e];
+                tk.rows[2][pos] = qv[e];
+            }
+        }
+        kq = wave_sum(kq);
+        if (lane == 0) tk.kq = kq;
     }
-    sq = wave_sum(sq);
-    sk = wave_sum(sk);
-    const float rq = p.q_scale / sqrtf(sq + p.l2_eps);
-    const float rk = 1.0f / sqrtf(sk + p.l2_eps);
-    float kq = 0.f;
+    if (PART < 0 || PART == 1) {
 #pragma unroll
-    for (int e = 0; e < EK; ++e) {
-        qv[e] *= rq;
-        kv[e] *= rk;
-        kq = fmaf(qv[e], kv[e], kq);
-        tk.conv[lane + kWave * e] = qv[e];
-        tk.conv[DK + lane + kWave * e] = kv[e];
-        if (LR) {
-            const int r = lane + kWave * e, pos = (r % RG) * RPT + r / RG;
-            tk.rows[1][pos] = kv[e];
-            tk.rows[2][pos] = qv[e];
+        for (int e = 0; e < EK; ++e) {
+            const float a = expf(-expf(pr.A[e]) * softplus(to_f32(pr.g[j][e])));
+            const int r = lane + kWave * e;
+            tk.alpha[r] = a;
+            if (LR) tk.rows[0][(r % RG) * RPT + r / RG] = a;
         }
     }
-    kq = wave_sum(kq);
+    if (PART < 0 || PART == 2) {
 #pragma unroll
-    for (int e = 0; e < EK; ++e) {
-        const float a = expf(-expf(pr.A[e]) * softplus(to_f32(pr.g[j][e])));
-        const int r = lane + kWave * e;
-        tk.alpha[r] = a;
-        if (LR) tk.rows[0][(r % RG) * RPT + r / RG] = a;
-    }
-#pragma unroll
-    for (int e = 0; e < EV; ++e)
-        tk.gate[lane + kWave * e] = pr.w[e] * sigmoid(to_f32(pr.z[j][e]));
-    if (lane == 0) {
-        tk.beta = sigmoid(to_f32(pr.b[j]));
-        tk.kq = kq;
+        for (int e = 0; e < EV; ++e)
+            tk.gate[lane + kWave * e] = pr.w[e] * sigmoid(to_f32(pr.z[j][e]));
+        if (lane == 0) tk.beta = sigmoid(to_f32(pr.b[j]));
     }
 }
 
 // y = o / sqrt(mean(o^2) + eps_r) * gate for the 4 columns 4c..4c+3 of one
-// token, by lanes 0 .. d_v/4 - 1 of one wave (a butterfly over those lanes).
+// token, by lanes 0 .. d_v/4 - 1 of one wave (a DPP sum over those lanes).
 template <int DV>
 __device__ __forceinline__ void output_row(const RecParams &p, float4 o, const float *gate, int c,
                                            float *yrow) {
@@ -313,8 +321,7 @@ __device__ __forceinline__ void output_row(const RecParams &p, float4 o, const f
     ss2 = fmaf(o.y, o.y, ss2);
     ss2 = fmaf(o.z, o.z, ss2);
     ss2 = fmaf(o.w, o.w, ss2);
-#pragma unroll
-    for (int m = 1; m < DV / 4; m <<= 1) ss2 += __shfl_xor(ss2, m, kWave);
+    ss2 = lane_sum<DV / 4>(ss2);
     const float r = 1.0f / sqrtf(ss2 * (1.0f / DV) + p.rms_eps);
     const float4 gt = make_float4(gate[4 * c], gate[4 * c + 1], gate[4 * c + 2], gate[4 * c + 3]);
     *reinterpret_cast<float4 *>(yrow + 4 * c) =
@@ -446,11 +453,19 @@ __device__ __forceinline__ void rec_run(const RecParams &p, RecItem<DK, DV, NT, 
     // 2. conv (+ window update / window snapshots)
     conv_compute<DK, DV, NT, Tin, TMAX, VERIFY, DELTA, LR>(p, tid, b, h, slot, T, it.cr, tok);
     __syncthreads();
-    // 3. norms and gates, one wave per token
+    // 3. norms and gates: one wave per token, or for a single token its
+    //    three independent parts on three waves (every wave fetched the gate
+    //    operands of token 0)
+    if (TMAX == 1 && G::NW >= 3) {
+        if (wave == 0) prep_token<DK, DV, Tin, TPW, G::RG, G::RPT, LR, 0>(p, lane, 0, it.pr, tok[0]);
+        else if (wave == 1) prep_token<DK, DV, Tin, TPW, G::RG, G::RPT, LR, 1>(p, lane, 0, it.pr, tok[0]);
+        else if (wave == 2) prep_token<DK, DV, Tin, TPW, G::RG, G::RPT, LR, 2>(p, lane, 0, it.pr, tok[0]);
+    } else {
 #pragma unroll
-    for (int j = 0; j < TPW; ++j) {
-        const int t = wave + G::NW * j;
-        if (t < T) prep_token<DK, DV, Tin, TPW, G::RG, G::RPT, LR>(p, lane, j, it.pr, tok[t]);
+        for (int j = 0; j < TPW; ++j) {
+            const int t = wave + G::NW * j;
+            if (t < T) prep_token<DK, DV, Tin, TPW, G::RG, G::RPT, LR>(p, lane, j, it.pr, tok[t]);
+        }
     }
     __syncthreads();
     // delta mode: alpha and k^ of every token into its record
@@ -502,13 +517,21 @@ __device__ __forceinline__ void rec_run(const RecParams &p, RecItem<DK, DV, NT, 
                 pq = fma4(tk.conv[r], s[i], pq);
             }
         }
-        // sum over the row groups inside the wave, then across waves
+        // sum over the row groups inside the wave (into lanes 0 .. CG-1),
+        // then across waves
 #pragma unroll
         for (int m = G::CG; m < kWave; m <<= 1) {
-            u.x += __shfl_xor(u.x, m, kWave); u.y += __shfl_xor(u.y, m, kWave);
-            u.z += __shfl_xor(u.z, m, kWave); u.w += __shfl_xor(u.w, m, kWave);
-            pq.x += __shfl_xor(pq.x, m, kWave); pq.y += __shfl_xor(pq.y, m, kWave);
-            pq.z += __shfl_xor(pq.z, m, kWave); pq.w += __shfl_xor(pq.w, m, kWave);
+            if (m == 32) {
+                u.x = add_upper_half(u.x); u.y = add_upper_half(u.y);
+                u.z = add_upper_half(u.z); u.w = add_upper_half(u.w);
+                pq.x = add_upper_half(pq.x); pq.y = add_upper_half(pq.y);
+                pq.z = add_upper_half(pq.z); pq.w = add_upper_half(pq.w);
+            } else {
+                u.x += __shfl_xor(u.x, m, kWave); u.y += __shfl_xor(u.y, m, kWave);
+                u.z += __shfl_xor(u.z, m, kWave); u.w += __shfl_xor(u.w, m, kWave);
+                pq.x += __shfl_xor(pq.x, m, kWave); pq.y += __shfl_xor(pq.y, m, kWave);
+                pq.z += __shfl_xor(pq.z, m, kWave); pq.w += __shfl_xor(pq.w, m, kWave);
+            }
         }
         const int rb = SH::NRB == 2 ? (t & 1) : 0;
         if (lane < G::CG) { sh.red[rb][wave][0][cg] = u; sh.red[rb][wave][1][cg] = pq; }
