@@ -241,9 +241,15 @@ def main():
     if not args.no_extras:
         out["extras"] = extras(torch, api, synth, layer, cache, step_inputs, y, sets, B, H, dk, dv,
                                n_slots, W, K, stream)
+        # two measured ceilings: the copy probe (in place over 2 GiB) and the
+        # decode itself on every slot of the pool in one call (2 GiB of state
+        # read and written, the best DRAM-bound rate measured here)
         ceil = out["extras"]["inplace_probe_2gib"]["gbs"]
         out["roofline"]["inplace_ceiling_gbs"] = ceil
         out["roofline"]["frac_of_inplace_ceiling"] = achieved / ceil
+        dram = out["extras"]["decode_b%d_dram" % n_slots]["algorithmic_gbs"]
+        out["roofline"]["decode_dram_ceiling_gbs"] = dram
+        out["roofline"]["frac_of_decode_dram_ceiling"] = achieved / dram
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(synth, p, inp, B, H, dk, dv)
     print(json.dumps(out), flush=True)
@@ -328,8 +334,8 @@ def extras(torch, api, synth, layer, cache, step_inputs, y, sets, B, H, dk, dv, 
                                   "algorithmic_gbs": bll / s / 1e9, "frac_of_8tbs": bll / s / 8e12,
                                   "state_bytes": Bl * H * dk * dv * 4}
     del LI, yl
-    # memory ceilings: the probe copies n floats with 16-byte non-temporal
-    # buffer loads and stores, a one-round grid, 8 loads in flight per lane.
+    # memory ceilings: the probe copies n floats the way the decode moves its
+    # tiles (64 KiB per workgroup, 16-byte non-temporal loads and stores).
     # In place (dst = src: read then rewrite the same bytes, the decode's
     # pattern) over 2 GiB, and as a copy between two 1 GiB buffers
     n = 1 << 29

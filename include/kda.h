@@ -370,12 +370,14 @@ kda_status kda_build_metadata(const int32_t *num_tokens, const int32_t *req_slot
                               int32_t *chunk_start, int32_t *counts, int32_t *err_flag,
                               void *hip_stream);
 
-/* Measurement helper: dst[i] = src[i] for n floats, with 16-byte
- * non-temporal loads and stores from a grid that is resident at once (a
- * streaming copy of known size: it calibrates memory-traffic counters and
- * bounds what HBM delivers next to the KDA kernels).  dst may equal src: the
- * data is then read and rewritten in place, the decode's own access pattern.
- * Other overlaps are undefined.  n = 0 is a no-op. */
+/* Measurement helper: dst[i] = src[i] for n floats, moved the way the
+ * decode moves its state tiles (64 KiB per workgroup, 16-byte non-temporal
+ * loads and stores, at most three workgroups per CU, 2 MiB granules in a
+ * scrambled order): a streaming copy of known size that calibrates
+ * memory-traffic counters and gives a copy ceiling next to the KDA kernels.
+ * dst may equal src: the data is then read and rewritten in place, the
+ * decode's own access pattern.  Other overlaps are undefined.  n = 0 is a
+ * no-op. */
 kda_status kda_copy_probe(float *dst, const float *src, size_t n, void *hip_stream);
 
 /* Static text for a status code. */

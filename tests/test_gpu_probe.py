@@ -1,5 +1,5 @@
-"""The measurement copy probe moves every element (whole and partial
-workgroup ranges, several passes per workgroup and the last n % 4 floats)."""
+"""The measurement copy probe moves every element (whole and partial tiles,
+scrambled and in-order granules, the last n % 4 floats), also in place."""
 import pytest
 import torch
 
@@ -16,3 +16,12 @@ def test_copy_probe_copies_everything(n):
     api.kda_copy_probe(dst, src)
     torch.cuda.synchronize()
     assert torch.equal(dst, src)
+
+
+@pytest.mark.parametrize("n", [4099, (1 << 21) + 1029, (1 << 23)])
+def test_copy_probe_in_place_keeps_every_element(n):
+    buf = torch.arange(n, dtype=torch.float32, device=DEV)
+    ref = buf.clone()
+    api.kda_copy_probe(buf, buf)
+    torch.cuda.synchronize()
+    assert torch.equal(buf, ref)
