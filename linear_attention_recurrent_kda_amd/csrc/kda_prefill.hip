@@ -183,13 +183,25 @@ constexpr int kIntraWaves = kIntraThreads / kWave;
 
 template <int DK, int DV>
 struct __align__(16) IntraLds {
-    static constexpr int KW = DK + 1;   // odd pitch: column reads hit distinct banks
-    static constexpr int RW = DK + 4;   // 16-byte rows for vector reads
-    float G[kChunk][KW];                // log2-decay prefix sums
-    float Q[kChunk][RW];                // q^
-    float K[kChunk][RW];                // k^
+    static constexpr int RW = DK + 4;   // row pitch: 16-byte rows
+    static constexpr int NPAIR = 10;    // token-block pairs (bt, bs), bs <= bt
+    // Token rows.  Phase 1 writes q^, k^ and the log2-decay prefix sums G in
+    // fp32; the conversion then rewrites each row in place: Q and K hold
+    // q^ e^(G - G_r) and k^ e^(G - G_r) (r: the row's block start) split into
+    // bf16 pairs, for each 8 channels their 8 hi halves then their 8 lo halves
+    // (the 32 bytes the 8 fp32 values held), and G holds the fp32
+    // k^ e^(G_e - G) (e: the row's block end).
+    float Q[kChunk][RW];
+    float K[kChunk][RW];
+    float G[kChunk][RW];
+    float M[NPAIR][DK];                 // e^(G_{16 bt} - G_{16 bs + 15}) per block pair
+    float Fq[4][DK];                    // e^(G_{16 b}): block start -> chunk start
+    float Fk[4][DK];                    // e^(G_last - G_{16 b + 15}): block end -> chunk end
     float A[kChunk][kChunk + 1];        // beta_t (K K^T * decay), strictly lower part used
-    float T[kChunk][kChunk + 4];        // (I + A)^-1
+    union {
+        float T[kChunk][kChunk + 4];    // (I + A)^-1
+        float Gb[9][DK];                // before T: G at the block starts, block ends and the last token
+    };
     float Z[3][16][17];                 // block-inverse scratch
     float D[kIntraWaves][16][17];       // per-wave scratch: direct tiles, tile stores
     float beta[kChunk];
@@ -302,7 +314,7 @@ __device__ __forceinline__ void prep_rows(const PrefillParams &p, const Tin *x, 
 // turns its channel's column of G into prefix sums, adding in token order.
 template <int DK, typename Tin>
 __device__ __forceinline__ void prep_gates(const PrefillParams &p, int t0, int n, int h, int lane, int ch0,
-                                           float (*G)[DK + 1]) {
+                                           float (*G)[DK + 4]) {
     typedef Tin V8 __attribute__((ext_vector_type(8)));
     constexpr int LPR = 64 / 8;          // lanes per row of 64 channels
     constexpr int RPI = kWave / LPR;     // rows per wave-wide load
@@ -454,62 +466,47 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
     }
     __syncthreads();
 
-    // 2. per 16-token block: may the diagonal tile use the scaled factors?
+    // 2. per 16-token block: may its diagonal tile use scaled factors
+    //    (waves 0-3)?  G at the block starts, block ends and the last token
+    //    (waves 4-7).
+    const int last = max(n - 1, 0);
+    constexpr int NPAIR = IntraLds<DK, DV>::NPAIR;
     if (wave < 4) {
         float span = 0.f;
         for (int i = lane; i < DK; i += kWave) span = fmaxf(span, L.G[16 * wave][i] - L.G[16 * wave + 15][i]);
 #pragma unroll
         for (int m = 32; m >= 1; m >>= 1) span = fmaxf(span, __shfl_xor(span, m, kWave));
         if (lane == 0) L.safe[wave] = span <= kSafeSpan ? 1 : 0;
+    } else {
+        for (int e = tid - kIntraThreads / 2; e < 9 * DK; e += kIntraThreads / 2) {
+            const int j = e / DK, i = e % DK;
+            const int row = j < 4 ? 16 * j : j < 8 ? 16 * (j - 4) + 15 : last;
+            L.Gb[j][i] = L.G[row][i];
+        }
     }
     __syncthreads();
 
-    // 3. A and P in 16 x 16 tiles; tile (bt, bs) covers t in block bt, s in
-    //    block bs.  The 10 tiles on or below the diagonal come first (two
-    //    waves take two of them); the 6 above it (P = 0 there, A is never
-    //    read there) go to the other waves.
+    // A (times beta, strictly lower) to LDS and P (lower, diagonal included)
+    // split to the workspace, from a tile pair in the MFMA result layout
     uint16_t *Ph = ws.P_hi + gh * kChunk * kChunk, *Pl = ws.P_lo + gh * kChunk * kChunk;
-    for (int tile = wave; tile < 16; tile += kIntraWaves) {
-        // tile -> (bt, bs), 2 bits per tile: bt = 0 1 1 2 2 2 3 3 3 3 0 0 0 1 1 2,
-        // bs = 0 0 1 0 1 2 0 1 2 3 1 2 3 2 3 3 (register constants: a table in
-        // memory would cost a load and a wait per tile)
-        const int bt = (int)((0x940ffa94u >> (2 * tile)) & 3u), bs = (int)((0xfb9e4910u >> (2 * tile)) & 3u);
-        f32x4 aA = {0.f, 0.f, 0.f, 0.f}, aP = aA;
-        if (bs > bt) {
-            if (lane < 32) {
-                const bf16x8 z = {};
-                const size_t o = opnd_off<kChunk>(16 * bt + lane % 16, 16 * bs + 8 * (lane / 16));
-                *reinterpret_cast<bf16x8 *>(Ph + o) = z;
-                *reinterpret_cast<bf16x8 *>(Pl + o) = z;
-            }
-            continue;
+    auto gram_out = [&](int bt, int bs, f32x4 aA, f32x4 aP) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int t = 16 * bt + 4 * lk + rr, sv = 16 * bs + lr;
+            L.A[t][sv] = sv < t ? L.beta[t] * aA[rr] : 0.f;
+            aP[rr] = sv <= t ? aP[rr] : 0.f;
         }
-        const int r = 16 * bt;
-        if (bs < bt || L.safe[bt]) {
-            const int t = 16 * bt + lr, sr = 16 * bs + lr;
-#pragma unroll
-            for (int kk = 0; kk < KS; ++kk) {
-                const int c0 = 32 * kk + 8 * lk;
-                float ka[8], qa[8], kb[8];
-                lds8(&L.K[t][c0], ka);
-                lds8(&L.Q[t][c0], qa);
-                lds8(&L.K[sr][c0], kb);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float gr = L.G[r][c0 + e];
-                    const float et = exp2_hw(L.G[t][c0 + e] - gr);
-                    ka[e] *= et;
-                    qa[e] *= et;
-                    kb[e] *= exp2_hw(gr - L.G[sr][c0 + e]);
-                }
-                const Split8 b = split8(kb);
-                aA = mma3(split8(ka), b, aA);
-                aP = mma3(split8(qa), b, aP);
-            }
-        } else {
-            // direct: lane owns row t = r + lr and columns s = r + 4 lk + j
+        store_tile_split<kChunk>(L.D[wave], aP, lane, Ph, Pl, 16 * bt, 16 * bs);
+    };
+
+    // 2b. a block whose decay span is too wide for scaled factors has its
+    //     diagonal tiles summed directly (one exponential per term), from the
+    //     plain rows, before they are rewritten: lane owns row t = r + lr and
+    //     columns s = r + 4 lk + j
+    if (!(L.safe[0] & L.safe[1] & L.safe[2] & L.safe[3])) {
+        if (wave < 4 && !L.safe[wave]) {
+            const int r = 16 * wave, t = r + lr;
             float da[4] = {0.f, 0.f, 0.f, 0.f}, dp[4] = {0.f, 0.f, 0.f, 0.f};
-            const int t = r + lr;
             for (int ch = 0; ch < DK; ++ch) {
                 const float kv = L.K[t][ch], qv = L.Q[t][ch], gt = L.G[t][ch];
 #pragma unroll
@@ -521,6 +518,7 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
                 }
             }
             // to the MFMA result layout through this wave's scratch
+            f32x4 aA, aP;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 L.A[t][r + 4 * lk + j] = da[j];
@@ -533,55 +531,121 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
                 aP[rr] = L.D[wave][4 * lk + rr][lr];
             }
             __builtin_amdgcn_wave_barrier();
+            gram_out(wave, wave, aA, aP);
         }
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const int t = 16 * bt + 4 * lk + rr, sv = 16 * bs + lr;
-            L.A[t][sv] = sv < t ? L.beta[t] * aA[rr] : 0.f;
-            aP[rr] = sv <= t ? aP[rr] : 0.f;
-        }
-        store_tile_split<kChunk>(L.D[wave], aP, lane, Ph, Pl, 16 * bt, 16 * bs);
+        __syncthreads();
     }
-    // 4. decayed factors for the scan: Q^ e^G (rows), (K^ e^(G_C - G))^T, e^(G_C)
+
+    // 3. the rows rewritten for the Gram operands, each lane converting the
+    //    8-channel groups it reads (e^(G - G_r) and e^(G_e - G) are <= 1:
+    //    G falls along the chunk); then the per-channel block factors
+    for (int u = tid; u < kChunk * DK / 8; u += kIntraThreads) {
+        const int t = u / (DK / 8), c0 = 8 * (u % (DK / 8)), b = t / 16;
+        float q[8], k[8], g[8], gr[8], ge[8], ko[8];
+        lds8(&L.Q[t][c0], q);
+        lds8(&L.K[t][c0], k);
+        lds8(&L.G[t][c0], g);
+        lds8(&L.Gb[b][c0], gr);
+        lds8(&L.Gb[4 + b][c0], ge);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float ein = exp2_hw(g[e] - gr[e]);
+            ko[e] = k[e] * exp2_hw(ge[e] - g[e]);
+            q[e] *= ein;
+            k[e] *= ein;
+        }
+        const Split8 sq = split8(q), sk = split8(k);
+        bf16x8 *dq = reinterpret_cast<bf16x8 *>(&L.Q[t][c0]), *dk = reinterpret_cast<bf16x8 *>(&L.K[t][c0]);
+        dq[0] = sq.hi;
+        dq[1] = sq.lo;
+        dk[0] = sk.hi;
+        dk[1] = sk.lo;
+        float4 *dg = reinterpret_cast<float4 *>(&L.G[t][c0]);
+        dg[0] = make_float4(ko[0], ko[1], ko[2], ko[3]);
+        dg[1] = make_float4(ko[4], ko[5], ko[6], ko[7]);
+    }
+    for (int e = tid; e < (NPAIR + 8) * DK; e += kIntraThreads) {
+        const int j = e / DK, i = e % DK;
+        if (j < NPAIR) {
+            // pair j = bt (bt + 1) / 2 + bs; on the diagonal the factor is
+            // >= 1 (<= 2^60 where it is used: the block passed the span check)
+            const int bt = j < 1 ? 0 : j < 3 ? 1 : j < 6 ? 2 : 3, bs = j - bt * (bt + 1) / 2;
+            L.M[j][i] = exp2_hw(L.Gb[bt][i] - L.Gb[4 + bs][i]);
+        } else if (j < NPAIR + 4) {
+            L.Fq[j - NPAIR][i] = exp2_hw(L.Gb[j - NPAIR][i]);
+        } else {
+            L.Fk[j - NPAIR - 4][i] = exp2_hw(L.Gb[8][i] - L.Gb[j - NPAIR][i]);
+        }
+    }
+    if (tid < DK) ws.gC[gh * DK + tid] = exp2_hw(L.Gb[8][tid]);
+    __syncthreads();
+
+    // 4. A and P by token-block pair (bt, bs), bs <= bt: for t in block bt
+    //    and s in block bs, e^(G_t - G_s) = e^(G_t - G_r) M_(bt,bs) e^(G_e - G_s)
+    //    (r = 16 bt, e = 16 bs + 15): the rewritten q and k rows are the A
+    //    operands, the rewritten k rows times the pair's factor the shared B
+    //    operand.  Ten pairs and the six zero P tiles above the diagonal,
+    //    two items per wave.
+    for (int j = wave; j < NPAIR + 6; j += kIntraWaves) {
+        if (j >= NPAIR) {
+            const int u = j - NPAIR, bt = u < 3 ? 0 : u < 5 ? 1 : 2, bs = u < 3 ? u + 1 : u < 5 ? u - 1 : 3;
+            if (lane < 32) {
+                const bf16x8 z = {};
+                const size_t o = opnd_off<kChunk>(16 * bt + lane % 16, 16 * bs + 8 * (lane / 16));
+                *reinterpret_cast<bf16x8 *>(Ph + o) = z;
+                *reinterpret_cast<bf16x8 *>(Pl + o) = z;
+            }
+            continue;
+        }
+        const int bt = j < 1 ? 0 : j < 3 ? 1 : j < 6 ? 2 : 3, bs = j - bt * (bt + 1) / 2;
+        if (bt == bs && !L.safe[bt]) continue;   // summed directly above
+        const int t = 16 * bt + lr, sr = 16 * bs + lr;
+        f32x4 aA = {0.f, 0.f, 0.f, 0.f}, aP = aA;
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+            const int c0 = 32 * kk + 8 * lk;
+            const bf16x8 *ka = reinterpret_cast<const bf16x8 *>(&L.K[t][c0]);
+            const bf16x8 *qa = reinterpret_cast<const bf16x8 *>(&L.Q[t][c0]);
+            float kb[8], m[8];
+            lds8(&L.G[sr][c0], kb);
+            lds8(&L.M[j][c0], m);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) kb[e] *= m[e];
+            const Split8 b = split8(kb);
+            aA = mma3(Split8{ka[0], ka[1]}, b, aA);
+            aP = mma3(Split8{qa[0], qa[1]}, b, aP);
+        }
+        gram_out(bt, bs, aA, aP);
+    }
+    // decayed factors for the scan: Q^ e^G (rows), (K^ e^(G_C - G))^T
     //    Unit e8 (8 elements) is stored at 8 e8 in operand order, so each wave
     //    writes whole lines: tile e8 / 64, lane e8 % 64 of that tile.
-    const int last = max(n - 1, 0);
     for (int e8 = tid; e8 < kChunk * DK / 8; e8 += kIntraThreads) {
         const int tl = e8 / kWave, ln = e8 % kWave;
         const int r = 16 * (tl / KS) + ln % 16, i0 = 32 * (tl % KS) + 8 * (ln / 16);
-        float x[8];
-        lds8(&L.Q[r][i0], x);
-        bf16x8 hv, lv;
+        const bf16x8 *src = reinterpret_cast<const bf16x8 *>(&L.Q[r][i0]);
+        const bf16x8 h8 = src[0], l8 = src[1];
+        float f[8], x[8];
+        lds8(&L.Fq[r / 16][i0], f);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float v = x[e] * exp2_hw(L.G[r][i0 + e]);
-            const __bf16 hb = (__bf16)v;
-            hv[e] = hb;
-            lv[e] = (__bf16)(v - (float)hb);
-        }
+        for (int e = 0; e < 8; ++e) x[e] = ((float)h8[e] + (float)l8[e]) * f[e];
+        const Split8 sx = split8(x);
         const size_t o = gh * kChunk * DK + (size_t)8 * e8;   // = opnd_off<DK>(r, i0)
-        *reinterpret_cast<bf16x8 *>(ws.Q_hi + o) = hv;
-        *reinterpret_cast<bf16x8 *>(ws.Q_lo + o) = lv;
+        *reinterpret_cast<bf16x8 *>(ws.Q_hi + o) = sx.hi;
+        *reinterpret_cast<bf16x8 *>(ws.Q_lo + o) = sx.lo;
     }
     for (int e8 = tid; e8 < kChunk * DK / 8; e8 += kIntraThreads) {
         const int tl = e8 / kWave, ln = e8 % kWave;
         const int i = 16 * (tl / 2) + ln % 16, r0 = 32 * (tl % 2) + 8 * (ln / 16);
-        const float gl = L.G[last][i];
-        bf16x8 hv, lv;
+        const float fk = L.Fk[r0 / 16][i];
+        float x[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int r = r0 + e;
-            // k^ rows past n are zero
-            const float v = L.K[r][i] * exp2_hw(fminf(gl - L.G[r][i], 0.f));
-            const __bf16 hb = (__bf16)v;
-            hv[e] = hb;
-            lv[e] = (__bf16)(v - (float)hb);
-        }
+        for (int e = 0; e < 8; ++e) x[e] = L.G[r0 + e][i] * fk;   // k^ rows past n are zero
+        const Split8 sx = split8(x);
         const size_t o = gh * DK * kChunk + (size_t)8 * e8;   // = opnd_off<kChunk>(i, r0)
-        *reinterpret_cast<bf16x8 *>(ws.K_hi + o) = hv;
-        *reinterpret_cast<bf16x8 *>(ws.K_lo + o) = lv;
+        *reinterpret_cast<bf16x8 *>(ws.K_hi + o) = sx.hi;
+        *reinterpret_cast<bf16x8 *>(ws.K_lo + o) = sx.lo;
     }
-    if (tid < DK) ws.gC[gh * DK + tid] = exp2_hw(L.G[last][tid]);
 
     // 5. T = (I + A)^-1 by 16 x 16 blocks: the diagonal blocks by forward
     //    substitution, then block row b = 1, 2, 3 from
@@ -660,7 +724,10 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
             for (int e = 0; e < 8; ++e) {
                 const int sv = 32 * k2 + 8 * lk + e;
                 if (isw) {
-                    x[e] = L.beta[sv] * L.K[sv][col] * exp2_hw(L.G[sv][col]);
+                    // beta_s k^_s e^(G_s): the rewritten k row (hi + lo) times
+                    // e^(G_r) of its block
+                    const __bf16 *kr = reinterpret_cast<const __bf16 *>(&L.K[sv][0]) + 2 * (col & ~7) + (col & 7);
+                    x[e] = L.beta[sv] * (((float)kr[0] + (float)kr[8]) * L.Fq[sv / 16][col]);
                 } else {
                     // conv (+ SiLU) of v, as the q and k rows were formed
                     const float4 w = vwt[ci];
