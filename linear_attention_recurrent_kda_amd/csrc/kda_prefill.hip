@@ -178,7 +178,7 @@ __global__ __launch_bounds__(64) void kda_prefill_meta_kernel(PrefillParams p, P
 // factors for the scan (P, Q^ e^G, Kd^T, -W as bf16 hi/lo; U~ in fp32) are
 // written in the order its loads read.
 // ---------------------------------------------------------------------------
-constexpr int kIntraThreads = 512;
+constexpr int kIntraThreads = 1024;
 constexpr int kIntraWaves = kIntraThreads / kWave;
 
 template <int DK, int DV>
@@ -197,13 +197,17 @@ struct __align__(16) IntraLds {
     float M[NPAIR][DK];                 // e^(G_{16 bt} - G_{16 bs + 15}) per block pair
     float Fq[4][DK];                    // e^(G_{16 b}): block start -> chunk start
     float Fk[4][DK];                    // e^(G_last - G_{16 b + 15}): block end -> chunk end
-    float A[kChunk][kChunk + 1];        // beta_t (K K^T * decay), strictly lower part used
+    union {
+        float A[kChunk][kChunk + 1];    // beta_t (K K^T * decay), strictly lower part used
+        float Dx[kIntraWaves - 10][16][17];   // after T: tile-store scratch of waves 10..
+    };
     union {
         float T[kChunk][kChunk + 4];    // (I + A)^-1
-        float Gb[9][DK];                // before T: G at the block starts, block ends and the last token
+        float Gb[10][DK];               // before T: G at the block starts, block ends, the last token, row 31
     };
     float Z[3][16][17];                 // block-inverse scratch
-    float D[kIntraWaves][16][17];       // per-wave scratch: direct tiles, tile stores
+    float D[10][16][17];                // per-wave scratch of waves 0..9: direct tiles, tile stores
+    __device__ float (*scratch(int w))[17] { return w < 10 ? D[w] : Dx[w - 10]; }
     float beta[kChunk];
     int safe[4];
 };
@@ -249,17 +253,17 @@ template <> struct ChRaw<float, 1> {
     __device__ static float get(T r, int) { return r; }
 };
 
-// Conv + SiLU over q or k for rows 32*HALF .. 32*HALF + 31 of a chunk, one
+// Conv + SiLU over q or k for rows 16*PART .. 16*PART + 15 of a chunk, one
 // wave; the lane owns channels NC*lane .. NC*lane + NC - 1.  MODE 0: q (L2
 // norm and q scale), 1: k (L2 norm), into LDS rows (zero past n).  The three
 // inputs before the chunk come from the conv window at chunk 0, else from the
 // sequence.
-template <int NC, int MODE, int HALF, typename Tin>
+template <int NC, int MODE, int PART, typename Tin>
 __device__ __forceinline__ void prep_rows(const PrefillParams &p, const Tin *x, const Tin *win, int choff, int CH,
                                           int c, int t0, int n, int h, int lane, float *out, size_t ostride) {
     using R = ChRaw<Tin, NC>;
     using RT = typename R::T;
-    constexpr int D = NC * kWave, NR = kChunk / 2, R0 = NR * HALF;
+    constexpr int D = NC * kWave, NR = kChunk / 4, R0 = NR * PART;
     const int H = p.H, cb = NC * lane;
     float w[NC][4];
 #pragma unroll
@@ -272,7 +276,7 @@ __device__ __forceinline__ void prep_rows(const PrefillParams &p, const Tin *x, 
     for (int j = 0; j < NR + 3; ++j) {
         const int q = R0 - 3 + j;
         const Tin *src;
-        if (HALF == 0 && j < 3) {
+        if (PART == 0 && j < 3) {
             src = c == 0 ? win + j * CH + choff + cb : x + ((size_t)(t0 + q) * H + h) * D + cb;
         } else {
             // rows past the chunk repeat its last row
@@ -307,19 +311,22 @@ __device__ __forceinline__ void prep_rows(const PrefillParams &p, const Tin *x, 
     }
 }
 
-// log2(alpha) of the chunk's tokens for channels ch0 .. ch0 + 63 and its
-// prefix sums over the chunk into G (rows past n add nothing); one wave.
-// The gate inputs are fetched 8 channels per lane (8 row loads per lane
-// instead of 64 narrow ones), log2(alpha) goes to G, and then each lane
-// turns its channel's column of G into prefix sums, adding in token order.
-template <int DK, typename Tin>
+// log2(alpha) of the chunk's tokens 32 HALF .. 32 HALF + 31 for channels
+// ch0 .. ch0 + 63 and their prefix sums over those rows into G (rows past n
+// add nothing; the second half's sums start again from 0, the first half's
+// total is added where a block factor spans both halves); one wave.  The gate
+// inputs are fetched 8 channels per lane (row loads instead of narrow ones),
+// log2(alpha) goes to G, and then each lane turns its channel's column into
+// prefix sums, adding in token order.
+template <int DK, int HALF, typename Tin>
 __device__ __forceinline__ void prep_gates(const PrefillParams &p, int t0, int n, int h, int lane, int ch0,
                                            float (*G)[DK + 4]) {
     typedef Tin V8 __attribute__((ext_vector_type(8)));
     constexpr int LPR = 64 / 8;          // lanes per row of 64 channels
     constexpr int RPI = kWave / LPR;     // rows per wave-wide load
-    constexpr int NI = kChunk / RPI;     // loads per lane
-    const int H = p.H, sub = lane % LPR, r0 = lane / LPR, cl = ch0 + 8 * sub;
+    constexpr int NR = kChunk / 2, R0 = NR * HALF;
+    constexpr int NI = NR / RPI;         // loads per lane
+    const int H = p.H, sub = lane % LPR, r0 = R0 + lane / LPR, cl = ch0 + 8 * sub;
     const Tin *g = static_cast<const Tin *>(p.g);
     V8 raw[NI];
 #pragma unroll
@@ -348,7 +355,7 @@ __device__ __forceinline__ void prep_gates(const PrefillParams &p, int t0, int n
     const int ch = ch0 + lane;
     float acc = 0.f;
 #pragma unroll
-    for (int j = 0; j < kChunk; ++j) {
+    for (int j = R0; j < R0 + NR; ++j) {
         acc += G[j][ch];
         G[j][ch] = acc;
     }
@@ -441,34 +448,39 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
             }
     }
 
-    // 1. the chunk's tokens: waves 0-1 q^ and 2-3 k^ (LDS), a row half each;
-    //    waves 6-7 the decay prefix sums (64 channels each) and beta.  v is
-    //    convolved where step 6 needs it (its raw inputs are fetched below).
+    // 1. the chunk's tokens: waves 0-3 q^ and 4-7 k^ (LDS), 16 rows each;
+    //    waves 8-11 the decay prefix sums (64 channels by half the rows
+    //    each); wave 12 beta.  v is convolved where step 6 needs it (its raw
+    //    inputs are fetched above).
     {
         constexpr int RW = IntraLds<DK, DV>::RW;
         const Tin *xq = static_cast<const Tin *>(p.x_q), *xk = static_cast<const Tin *>(p.x_k);
         switch (wave) {
         case 0: prep_rows<DK / 64, 0, 0>(p, xq, win, 0, CH, c, t0, n, h, lane, &L.Q[0][0], RW); break;
         case 1: prep_rows<DK / 64, 0, 1>(p, xq, win, 0, CH, c, t0, n, h, lane, &L.Q[0][0], RW); break;
-        case 2: prep_rows<DK / 64, 1, 0>(p, xk, win, DK, CH, c, t0, n, h, lane, &L.K[0][0], RW); break;
-        case 3: prep_rows<DK / 64, 1, 1>(p, xk, win, DK, CH, c, t0, n, h, lane, &L.K[0][0], RW); break;
-        case 4:
-        case 5: break;
-        default: {
-            const int gw = wave - 6;
-            if (64 * gw < DK) prep_gates<DK, Tin>(p, t0, n, h, lane, 64 * gw, L.G);
-            if (gw == 1) {
-                const Tin bv = static_cast<const Tin *>(p.b)[(size_t)(t0 + min(lane, n - 1)) * H + h];
-                L.beta[lane] = lane < n ? sigmoid(to_f32(bv)) : 0.f;
-            }
+        case 2: prep_rows<DK / 64, 0, 2>(p, xq, win, 0, CH, c, t0, n, h, lane, &L.Q[0][0], RW); break;
+        case 3: prep_rows<DK / 64, 0, 3>(p, xq, win, 0, CH, c, t0, n, h, lane, &L.Q[0][0], RW); break;
+        case 4: prep_rows<DK / 64, 1, 0>(p, xk, win, DK, CH, c, t0, n, h, lane, &L.K[0][0], RW); break;
+        case 5: prep_rows<DK / 64, 1, 1>(p, xk, win, DK, CH, c, t0, n, h, lane, &L.K[0][0], RW); break;
+        case 6: prep_rows<DK / 64, 1, 2>(p, xk, win, DK, CH, c, t0, n, h, lane, &L.K[0][0], RW); break;
+        case 7: prep_rows<DK / 64, 1, 3>(p, xk, win, DK, CH, c, t0, n, h, lane, &L.K[0][0], RW); break;
+        case 8:
+        case 9: if (64 * (wave - 8) < DK) prep_gates<DK, 0, Tin>(p, t0, n, h, lane, 64 * (wave - 8), L.G); break;
+        case 10:
+        case 11: if (64 * (wave - 10) < DK) prep_gates<DK, 1, Tin>(p, t0, n, h, lane, 64 * (wave - 10), L.G); break;
+        case 12: {
+            const Tin bv = static_cast<const Tin *>(p.b)[(size_t)(t0 + min(lane, n - 1)) * H + h];
+            L.beta[lane] = lane < n ? sigmoid(to_f32(bv)) : 0.f;
+            break;
         }
+        default: break;
         }
     }
     __syncthreads();
 
     // 2. per 16-token block: may its diagonal tile use scaled factors
-    //    (waves 0-3)?  G at the block starts, block ends and the last token
-    //    (waves 4-7).
+    //    (waves 0-3)?  G at the block starts, block ends, the last token and
+    //    row 31 (the first half's total) (the other waves).
     const int last = max(n - 1, 0);
     constexpr int NPAIR = IntraLds<DK, DV>::NPAIR;
     if (wave < 4) {
@@ -478,9 +490,9 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
         for (int m = 32; m >= 1; m >>= 1) span = fmaxf(span, __shfl_xor(span, m, kWave));
         if (lane == 0) L.safe[wave] = span <= kSafeSpan ? 1 : 0;
     } else {
-        for (int e = tid - kIntraThreads / 2; e < 9 * DK; e += kIntraThreads / 2) {
+        for (int e = tid - 4 * kWave; e < 10 * DK; e += kIntraThreads - 4 * kWave) {
             const int j = e / DK, i = e % DK;
-            const int row = j < 4 ? 16 * j : j < 8 ? 16 * (j - 4) + 15 : last;
+            const int row = j < 4 ? 16 * j : j < 8 ? 16 * (j - 4) + 15 : j == 8 ? last : kChunk / 2 - 1;
             L.Gb[j][i] = L.G[row][i];
         }
     }
@@ -496,7 +508,7 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
             L.A[t][sv] = sv < t ? L.beta[t] * aA[rr] : 0.f;
             aP[rr] = sv <= t ? aP[rr] : 0.f;
         }
-        store_tile_split<kChunk>(L.D[wave], aP, lane, Ph, Pl, 16 * bt, 16 * bs);
+        store_tile_split<kChunk>(L.scratch(wave), aP, lane, Ph, Pl, 16 * bt, 16 * bs);
     };
 
     // 2b. a block whose decay span is too wide for scaled factors has its
@@ -564,20 +576,25 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
         dg[0] = make_float4(ko[0], ko[1], ko[2], ko[3]);
         dg[1] = make_float4(ko[4], ko[5], ko[6], ko[7]);
     }
+    // (G of rows 32.. restarts from 0: rows of the two halves differ by
+    // the first half's total, Gb[9])
     for (int e = tid; e < (NPAIR + 8) * DK; e += kIntraThreads) {
         const int j = e / DK, i = e % DK;
+        const float g31 = L.Gb[9][i], glast = L.Gb[8][i] + (last >= kChunk / 2 ? g31 : 0.f);
         if (j < NPAIR) {
             // pair j = bt (bt + 1) / 2 + bs; on the diagonal the factor is
             // >= 1 (<= 2^60 where it is used: the block passed the span check)
             const int bt = j < 1 ? 0 : j < 3 ? 1 : j < 6 ? 2 : 3, bs = j - bt * (bt + 1) / 2;
-            L.M[j][i] = exp2_hw(L.Gb[bt][i] - L.Gb[4 + bs][i]);
+            L.M[j][i] = exp2_hw((L.Gb[bt][i] + (bt >= 2 ? g31 : 0.f)) - (L.Gb[4 + bs][i] + (bs >= 2 ? g31 : 0.f)));
         } else if (j < NPAIR + 4) {
-            L.Fq[j - NPAIR][i] = exp2_hw(L.Gb[j - NPAIR][i]);
+            const int b = j - NPAIR;
+            L.Fq[b][i] = exp2_hw(L.Gb[b][i] + (b >= 2 ? g31 : 0.f));
         } else {
-            L.Fk[j - NPAIR - 4][i] = exp2_hw(L.Gb[8][i] - L.Gb[j - NPAIR][i]);
+            const int b = j - NPAIR - 4;
+            L.Fk[b][i] = exp2_hw(glast - (L.Gb[4 + b][i] + (b >= 2 ? g31 : 0.f)));
         }
     }
-    if (tid < DK) ws.gC[gh * DK + tid] = exp2_hw(L.Gb[8][tid]);
+    if (tid < DK) ws.gC[gh * DK + tid] = exp2_hw(L.Gb[8][tid] + (last >= kChunk / 2 ? L.Gb[9][tid] : 0.f));
     __syncthreads();
 
     // 4. A and P by token-block pair (bt, bs), bs <= bt: for t in block bt
@@ -747,7 +764,7 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
             if (rt >= 2) acc = mma3(ta[rt][1], rb[1], acc);   // T is lower triangular
             if (isw) {
                 const f32x4 wn = -acc;
-                store_tile_split<DK>(L.D[wave], wn, lane, ws.Wn_hi + gh * kChunk * DK, ws.Wn_lo + gh * kChunk * DK,
+                store_tile_split<DK>(L.scratch(wave), wn, lane, ws.Wn_hi + gh * kChunk * DK, ws.Wn_lo + gh * kChunk * DK,
                                      16 * rt, 16 * ct);
             } else {
 #pragma unroll
