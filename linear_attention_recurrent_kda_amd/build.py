@@ -25,6 +25,16 @@ FLAGS = [
 ]
 
 
+# Per-source flags.  The chunked-prefill intra kernel is one persistent loop
+# over chunks; with machine-level loop-invariant code motion its hoisted
+# constants and addresses exceed the 128 registers of a 16-wave workgroup
+# and spill to scratch, whose reloads wait on the vector memory counter
+# (and so on every outstanding store).
+SOURCE_FLAGS = {
+    "kda_prefill.hip": ["-mllvm", "-disable-machine-licm"],
+}
+
+
 def sources():
     return sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
 
@@ -39,7 +49,8 @@ def build(verbose: bool = False, extra=(), out: str = LIB, jobs: int = 0) -> str
     srcs = sources()
     with tempfile.TemporaryDirectory(prefix="kda_build_") as tmpd:
         objs = [os.path.join(tmpd, os.path.basename(s) + ".o") for s in srcs]
-        cmds = [[hipcc(), *FLAGS, *extra, *inc, "-c", s, "-o", o] for s, o in zip(srcs, objs)]
+        cmds = [[hipcc(), *FLAGS, *SOURCE_FLAGS.get(os.path.basename(s), []), *extra, *inc, "-c", s, "-o", o]
+                for s, o in zip(srcs, objs)]
 
         def run(cmd):
             if verbose:

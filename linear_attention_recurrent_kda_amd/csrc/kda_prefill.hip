@@ -22,6 +22,8 @@
 //          carried from chunk to chunk (state columns are independent given the
 //          chunk factors), unnormalised outputs O written to y
 //   norm   RMSNorm over d_v, weight, sigmoid gate on the rows of y
+#include <algorithm>
+
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -89,12 +91,20 @@ size_t prefill_workspace_bytes(int H, int d_k, int d_v, int total_T, int N_seq, 
     return ws_layout(H, d_k, d_v, total_T, N_seq).total;
 }
 
+// A load through the scalar unit, for tables no kernel of the call writes
+// after its launch (metadata, cu_seqlens, slot tables): scalar loads keep
+// off the vector memory counter, which also counts outstanding stores.
+__device__ __forceinline__ int32_t ld_const(const int32_t *a) {
+    typedef __attribute__((address_space(4))) const int32_t cint32;
+    return *reinterpret_cast<cint32 *>(reinterpret_cast<uintptr_t>(a));
+}
+
 // Largest s in [0, n) with a[s] <= v (a non-decreasing, a[0] <= v).
 __device__ __forceinline__ int upper_index(const int32_t *a, int n, int v) {
     int lo = 0, hi = n - 1;
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (a[mid] <= v) lo = mid; else hi = mid - 1;
+        if (ld_const(a + mid) <= v) lo = mid; else hi = mid - 1;
     }
     return lo;
 }
@@ -197,19 +207,17 @@ struct __align__(16) IntraLds {
     float M[NPAIR][DK];                 // e^(G_{16 bt} - G_{16 bs + 15}) per block pair
     float Fq[4][DK];                    // e^(G_{16 b}): block start -> chunk start
     float Fk[4][DK];                    // e^(G_last - G_{16 b + 15}): block end -> chunk end
-    union {
-        float A[kChunk][kChunk + 1];    // beta_t (K K^T * decay), strictly lower part used
-        float Dx[kIntraWaves - 10][16][17];   // after T: tile-store scratch of waves 10..
-    };
-    union {
-        float T[kChunk][kChunk + 4];    // (I + A)^-1
-        float Gb[10][DK];               // before T: G at the block starts, block ends, the last token, row 31
-    };
-    float Z[3][16][17];                 // block-inverse scratch
+    float A[kChunk][kChunk + 1];        // beta_t (K K^T * decay), strictly lower part used
+    float T[4][16][20];                 // the diagonal 16 x 16 blocks of (I + A)^-1
+    float Gb[9][DK];                    // G at the block starts, block ends, the last token
     float D[10][16][17];                // per-wave scratch of waves 0..9: direct tiles, tile stores
-    __device__ float (*scratch(int w))[17] { return w < 10 ? D[w] : Dx[w - 10]; }
     float beta[kChunk];
     int safe[4];
+    // the head's constants: conv taps of the q and k channels and of the v
+    // channels, e^A per key channel
+    float4 Cw[2 * DK];
+    float4 Cv[DV];
+    float Cea[DK];
 };
 
 // Sum over the 64 lanes of a wave (all lanes active), every lane receiving
@@ -253,40 +261,53 @@ template <> struct ChRaw<float, 1> {
     __device__ static float get(T r, int) { return r; }
 };
 
-// Conv + SiLU over q or k for rows 16*PART .. 16*PART + 15 of a chunk, one
-// wave; the lane owns channels NC*lane .. NC*lane + NC - 1.  MODE 0: q (L2
-// norm and q scale), 1: k (L2 norm), into LDS rows (zero past n).  The three
-// inputs before the chunk come from the conv window at chunk 0, else from the
-// sequence.
-template <int NC, int MODE, int PART, typename Tin>
-__device__ __forceinline__ void prep_rows(const PrefillParams &p, const Tin *x, const Tin *win, int choff, int CH,
-                                          int c, int t0, int n, int h, int lane, float *out, size_t ostride) {
-    using R = ChRaw<Tin, NC>;
-    using RT = typename R::T;
-    constexpr int D = NC * kWave, NR = kChunk / 4, R0 = NR * PART;
+template <typename Tin> struct Vec8 {
+    typedef Tin T __attribute__((ext_vector_type(8)));
+};
+
+// A workgroup works through the chunks of one head and requests the next
+// chunk's token inputs while it computes the current one; each wave keeps
+// what its role needs of them in registers.
+//
+// q or k rows 8 part .. 8 part + 7 of a chunk and the three inputs before
+// them (from the conv window at chunk 0, else from the sequence; rows past
+// the chunk's end repeat its last row); the lane owns channels NC lane ..
+// NC lane + NC - 1.
+template <typename Tin, int NC>
+__device__ __forceinline__ void rows_issue(const PrefillParams &p, const Tin *x, const Tin *win, int choff, int CH,
+                                           int c, int t0, int n, int h, int lane, int part,
+                                           typename ChRaw<Tin, NC>::T (&raw)[11]) {
+    using RT = typename ChRaw<Tin, NC>::T;
+    constexpr int D = NC * kWave;
     const int H = p.H, cb = NC * lane;
+#pragma unroll
+    for (int j = 0; j < 11; ++j) {
+        const int q = 8 * part - 3 + j;   // chunk row of the input (wave-uniform)
+        const Tin *src;
+        if (q < 0)
+            src = c == 0 ? win + (q + 3) * CH + choff + cb : x + ((size_t)(t0 + q) * H + h) * D + cb;
+        else
+            src = x + ((size_t)(t0 + min(q, n - 1)) * H + h) * D + cb;
+        raw[j] = *reinterpret_cast<const RT *>(src);
+    }
+}
+
+// Conv + SiLU, L2 norm (times `scale`) of those rows into LDS (zero past n).
+template <typename Tin, int NC>
+__device__ __forceinline__ void rows_compute(const PrefillParams &p, const typename ChRaw<Tin, NC>::T (&raw)[11],
+                                             const float4 *wt, float scale, int n, int lane, int part,
+                                             float *out, int ostride) {
+    using R = ChRaw<Tin, NC>;
+    const int cb = NC * lane;
     float w[NC][4];
 #pragma unroll
     for (int e = 0; e < NC; ++e) {
-        const float4 v = *reinterpret_cast<const float4 *>(p.conv_wt + ((size_t)h * CH + choff + cb + e) * 4);
+        const float4 v = wt[e];
         w[e][0] = v.x; w[e][1] = v.y; w[e][2] = v.z; w[e][3] = v.w;
     }
-    RT raw[NR + 3];   // rows R0 - 3 .. R0 + 31, all loads issued first
 #pragma unroll
-    for (int j = 0; j < NR + 3; ++j) {
-        const int q = R0 - 3 + j;
-        const Tin *src;
-        if (PART == 0 && j < 3) {
-            src = c == 0 ? win + j * CH + choff + cb : x + ((size_t)(t0 + q) * H + h) * D + cb;
-        } else {
-            // rows past the chunk repeat its last row
-            src = x + ((size_t)(t0 + min(q, n - 1)) * H + h) * D + cb;
-        }
-        raw[j] = *reinterpret_cast<const RT *>(src);
-    }
-#pragma unroll
-    for (int j = 0; j < NR; ++j) {
-        const int row = R0 + j;
+    for (int j = 0; j < 8; ++j) {
+        const int row = 8 * part + j;
         float y[NC];
 #pragma unroll
         for (int e = 0; e < NC; ++e) {
@@ -296,50 +317,41 @@ __device__ __forceinline__ void prep_rows(const PrefillParams &p, const Tin *x, 
             acc = fmaf(w[e][3], R::get(raw[j + 3], e), acc);
             y[e] = p.silu ? silu_hw(acc) : acc;
         }
-        {
-            float ss = 0.f;
+        float ss = 0.f;
 #pragma unroll
-            for (int e = 0; e < NC; ++e) ss = fmaf(y[e], y[e], ss);
-            ss = wave_sum_dpp(ss);
-            const float sc = row < n ? (MODE == 0 ? p.q_scale : 1.0f) * __builtin_amdgcn_rsqf(ss + p.l2_eps) : 0.f;
-#pragma unroll
-            for (int e = 0; e < NC; ++e) y[e] *= sc;
-        }
+        for (int e = 0; e < NC; ++e) ss = fmaf(y[e], y[e], ss);
+        ss = wave_sum_dpp(ss);
+        const float sc = row < n ? scale * __builtin_amdgcn_rsqf(ss + p.l2_eps) : 0.f;
         float *dst = out + row * ostride + cb;
-        if (NC == 2) *reinterpret_cast<float2 *>(dst) = make_float2(y[0], y[NC - 1]);
-        else dst[0] = y[0];
+        if (NC == 2) *reinterpret_cast<float2 *>(dst) = make_float2(y[0] * sc, y[NC - 1] * sc);
+        else dst[0] = y[0] * sc;
     }
 }
 
-// log2(alpha) of the chunk's tokens 32 HALF .. 32 HALF + 31 for channels
-// ch0 .. ch0 + 63 and their prefix sums over those rows into G (rows past n
-// add nothing; the second half's sums start again from 0, the first half's
-// total is added where a block factor spans both halves); one wave.  The gate
-// inputs are fetched 8 channels per lane (row loads instead of narrow ones),
-// log2(alpha) goes to G, and then each lane turns its channel's column into
-// prefix sums, adding in token order.
-template <int DK, int HALF, typename Tin>
-__device__ __forceinline__ void prep_gates(const PrefillParams &p, int t0, int n, int h, int lane, int ch0,
-                                           float (*G)[DK + 4]) {
-    typedef Tin V8 __attribute__((ext_vector_type(8)));
-    constexpr int LPR = 64 / 8;          // lanes per row of 64 channels
-    constexpr int RPI = kWave / LPR;     // rows per wave-wide load
-    constexpr int NR = kChunk / 2, R0 = NR * HALF;
-    constexpr int NI = NR / RPI;         // loads per lane
-    const int H = p.H, sub = lane % LPR, r0 = R0 + lane / LPR, cl = ch0 + 8 * sub;
+// Gate inputs of the 16 rows of block qt for channels ch0 .. ch0 + 63: the
+// lane fetches 8 channels of rows 16 qt + lane / 8 and 16 qt + lane / 8 + 8.
+template <int DK, typename Tin>
+__device__ __forceinline__ void gates_issue(const PrefillParams &p, int t0, int n, int h, int lane, int ch0, int qt,
+                                            typename Vec8<Tin>::T (&raw)[2]) {
+    using V8 = typename Vec8<Tin>::T;
+    const int row0 = 16 * qt + lane / 8, cl = ch0 + 8 * (lane % 8);
     const Tin *g = static_cast<const Tin *>(p.g);
-    V8 raw[NI];
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-        const int row = r0 + RPI * i;
-        raw[i] = *reinterpret_cast<const V8 *>(g + ((size_t)(t0 + min(row, n - 1)) * H + h) * DK + cl);
-    }
-    float ea[8];
+    for (int i = 0; i < 2; ++i)
+        raw[i] = *reinterpret_cast<const V8 *>(g + ((size_t)(t0 + min(row0 + 8 * i, n - 1)) * p.H + h) * DK + cl);
+}
+
+// log2(alpha) of those tokens into G, then each lane turns its channel's
+// 16 entries into prefix sums from the block's first row (rows past n add
+// nothing).  Block sums start again at each block; the block totals link
+// them where a factor spans blocks.
+template <int DK, typename Tin>
+__device__ __forceinline__ void gates_compute(const typename Vec8<Tin>::T (&raw)[2], const float *ea, int n,
+                                              int lane, int ch0, int qt, float (*G)[DK + 4]) {
+    const int row0 = 16 * qt + lane / 8, cl = ch0 + 8 * (lane % 8);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) ea[e] = expf(p.A[h * DK + cl + e]);
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-        const int row = r0 + RPI * i;
+    for (int i = 0; i < 2; ++i) {
+        const int row = row0 + 8 * i;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             // alpha below 2^-200 is 0 in fp32 either way; the floor keeps the
@@ -355,7 +367,7 @@ __device__ __forceinline__ void prep_gates(const PrefillParams &p, int t0, int n
     const int ch = ch0 + lane;
     float acc = 0.f;
 #pragma unroll
-    for (int j = R0; j < R0 + NR; ++j) {
+    for (int j = 16 * qt; j < 16 * qt + 16; ++j) {
         acc += G[j][ch];
         G[j][ch] = acc;
     }
@@ -398,89 +410,111 @@ __device__ __forceinline__ void lds8(const float *src, float *x) {
     x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
 }
 
+// bf16x3 on v_mfma_f32_16x16x16_bf16 (4 operand elements per lane)
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+struct Split4 {
+    s16x4 hi, lo;
+};
+__device__ __forceinline__ Split4 split4(const float *x) {
+    Split4 s;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const __bf16 h = (__bf16)x[e];
+        s.hi[e] = __builtin_bit_cast(short, h);
+        s.lo[e] = __builtin_bit_cast(short, (__bf16)(x[e] - (float)h));
+    }
+    return s;
+}
+__device__ __forceinline__ f32x4 mma3k16(const Split4 &a, const Split4 &b, f32x4 acc) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.hi, b.hi, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.hi, b.lo, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.lo, b.hi, acc, 0, 0, 0);
+    return acc;
+}
+
 template <int DK, int DV, typename Tin>
 __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(PrefillParams p, PrefillWs ws) {
-    constexpr int KS = DK / 32;
+    constexpr int KS = DK / 32, NC = DK / 64, CH = 2 * DK + DV;
+    constexpr int RW = IntraLds<DK, DV>::RW;
+    constexpr int NCT = (DK + DV) / 16;          // column tiles of [W | U~], one per wave
+    static_assert(NCT <= kIntraWaves && DK / 16 <= 10, "one column tile per wave; W tiles on waves with scratch");
+    using RT = typename ChRaw<Tin, NC>::T;
+    using V8 = typename Vec8<Tin>::T;
     __shared__ IntraLds<DK, DV> L;
-    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-    const int lr = lane % 16, lk = lane / 16;
-    // one-dimensional grid, heads fastest: every real chunk dispatches ahead
-    // of the chunk slots that only exit
-    const int H = p.H, h = (int)(blockIdx.x % (unsigned)H), gidx = (int)(blockIdx.x / (unsigned)H);
+    // the wave index as a scalar: role branches are uniform
+    const int tid = threadIdx.x, lane = tid % kWave, wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int lr = lane % 16;
+    const int H = p.H;
     if (ws.meta[0] != 1) return;
     const int32_t *cs = ws.meta + 1;
-    if (gidx >= cs[p.N_seq]) return;
-    const int s = upper_index(cs, p.N_seq + 1, gidx);
-    const int slot = p.slot_idx[s];
-    if (!slot_ok(slot, p.n_slots)) return;
-    if (p.cu_seqlens[s + 1] - p.cu_seqlens[s] == 1) return;   // a one-token sequence: decode kernel
-    const int c = gidx - cs[s];
-    const int t0 = p.cu_seqlens[s] + c * kChunk;
-    const int n = min(kChunk, p.cu_seqlens[s + 1] - t0);
+    const int nchunks = cs[p.N_seq];   // chunk slots, all of sequences on the chunk path
+    // workgroup w works through chunk slots w / H, w / H + wph, ... of head w % H
+    const int h = (int)(blockIdx.x % (unsigned)H), wph = (int)(gridDim.x / (unsigned)H);
+    int gidx = (int)(blockIdx.x / (unsigned)H);
+    if (gidx >= nchunks) return;
+
+    // roles in step 1: waves 0-7 q^ rows and 8-15 k^ rows, 8 rows each;
+    // waves 0 .. DK / 16 - 1 the decay sums of one 16-row block for 64
+    // channels each; the last wave beta.  In step 6 wave w takes column tile w.
+    const bool isq = wave < 8;
+    const int part = wave % 8;
+    const Tin *xr = static_cast<const Tin *>(isq ? p.x_q : p.x_k);
+    const int choff = isq ? 0 : DK;
+    const int gcg = wave / 4, gqt = wave % 4;
+    const bool gate_wave = wave < 8 && 64 * gcg < DK;   // wave-uniform
+    const bool u_wave = wave >= DK / 16 && wave < NCT;   // wave-uniform
+    const int vcol = 16 * wave + lr - DK;                // a U~ wave's v channel
+    // the head's constants into LDS (read by step 1 and step 6)
+    for (int e = tid; e < CH; e += kIntraThreads) {
+        const float4 v = *reinterpret_cast<const float4 *>(p.conv_wt + ((size_t)h * CH + e) * 4);
+        if (e < 2 * DK) L.Cw[e] = v;
+        else L.Cv[e - 2 * DK] = v;
+    }
+    if (tid < DK) L.Cea[tid] = expf(p.A[h * DK + tid]);
+
+    // chunk slot g: chunk c of its sequence, its first token t0, n tokens,
+    // the sequence's conv window
+    auto locate = [&](int g, int &c_, int &t0_, int &n_, const Tin *&win_) {
+        const int sq = upper_index(cs, p.N_seq + 1, g);
+        const int slot = ld_const(p.slot_idx + sq);
+        c_ = g - ld_const(cs + sq);
+        t0_ = ld_const(p.cu_seqlens + sq) + c_ * kChunk;
+        n_ = min(kChunk, ld_const(p.cu_seqlens + sq + 1) - t0_);
+        win_ = static_cast<const Tin *>(p.window) + ((size_t)slot * H + h) * 3 * CH;
+    };
+    RT rraw[11];
+    V8 graw[2];
+    Tin bv = Tin(0);
+    auto issue_rows = [&](int c_, int t0_, int n_, const Tin *win_, int ln) {
+        rows_issue<Tin, NC>(p, xr, win_, choff, CH, c_, t0_, n_, h, ln, part, rraw);
+        if (gate_wave) gates_issue<DK, Tin>(p, t0_, n_, h, ln, 64 * gcg, gqt, graw);
+        if (wave == kIntraWaves - 1) bv = static_cast<const Tin *>(p.b)[(size_t)(t0_ + min(ln, n_ - 1)) * H + h];
+    };
+    int c, t0, n;
+    const Tin *win;
+    locate(gidx, c, t0, n, win);
+    issue_rows(c, t0, n, win, lane);
+    __syncthreads();
+
+    for (;;) {
+    // fresh copies of the lane indices for each chunk: what is derived from
+    // them (LDS and workspace addresses) is formed where it is used instead
+    // of being kept live in registers across the whole loop
+    int tid;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(tid) : "v"((int)threadIdx.x));
+    const int lane = tid % kWave, lr = lane % 16, lk = lane / 16;
     const size_t gh = (size_t)gidx * H + h;
-    constexpr int CH = 2 * DK + DV;
-    const Tin *win = static_cast<const Tin *>(p.window) + ((size_t)slot * H + h) * 3 * CH;
-
-    // the raw inputs of the V operand of step 6, requested with the chunk's
-    // other inputs (the compiler widens them to fp32 right away, so a later
-    // request would stall the phase it lands in): a lane's v channel
-    // col = 16 ct + lr - d_k for rows 32 k2 + 8 lk .. + 7, plus the three rows
-    // before each run (from the conv window at chunk 0); rows past the
-    // chunk's end repeat its last row (their beta is 0)
-    constexpr int NCT = (DK + DV) / 16;          // column tiles of [W | U~]
-    Tin vraw[2][2][11];
-    float4 vwt[2];
-#pragma unroll
-    for (int ci = 0; ci < 2; ++ci) {
-        const int ct = wave + kIntraWaves * ci;
-        const int col = 16 * ct + lr - DK;
-        if (ct < DK / 16 || ct >= NCT) continue;   // wave-uniform
-        const Tin *xv = static_cast<const Tin *>(p.x_v) + (size_t)h * DV + col;
-        vwt[ci] = *reinterpret_cast<const float4 *>(p.conv_wt + ((size_t)h * CH + 2 * DK + col) * 4);
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-            for (int j = 0; j < 11; ++j) {
-                const int q = 32 * k2 + 8 * lk + j - 3;   // chunk row of the input
-                const Tin *src = q < 0 && c == 0 ? win + (q + 3) * CH + 2 * DK + col
-                                                 : xv + (size_t)(t0 + min(c == 0 ? max(q, 0) : q, n - 1)) * H * DV;
-                vraw[ci][k2][j] = *src;
-            }
-    }
-
-    // 1. the chunk's tokens: waves 0-3 q^ and 4-7 k^ (LDS), 16 rows each;
-    //    waves 8-11 the decay prefix sums (64 channels by half the rows
-    //    each); wave 12 beta.  v is convolved where step 6 needs it (its raw
-    //    inputs are fetched above).
-    {
-        constexpr int RW = IntraLds<DK, DV>::RW;
-        const Tin *xq = static_cast<const Tin *>(p.x_q), *xk = static_cast<const Tin *>(p.x_k);
-        switch (wave) {
-        case 0: prep_rows<DK / 64, 0, 0>(p, xq, win, 0, CH, c, t0, n, h, lane, &L.Q[0][0], RW); break;
-        case 1: prep_rows<DK / 64, 0, 1>(p, xq, win, 0, CH, c, t0, n, h, lane, &L.Q[0][0], RW); break;
-        case 2: prep_rows<DK / 64, 0, 2>(p, xq, win, 0, CH, c, t0, n, h, lane, &L.Q[0][0], RW); break;
-        case 3: prep_rows<DK / 64, 0, 3>(p, xq, win, 0, CH, c, t0, n, h, lane, &L.Q[0][0], RW); break;
-        case 4: prep_rows<DK / 64, 1, 0>(p, xk, win, DK, CH, c, t0, n, h, lane, &L.K[0][0], RW); break;
-        case 5: prep_rows<DK / 64, 1, 1>(p, xk, win, DK, CH, c, t0, n, h, lane, &L.K[0][0], RW); break;
-        case 6: prep_rows<DK / 64, 1, 2>(p, xk, win, DK, CH, c, t0, n, h, lane, &L.K[0][0], RW); break;
-        case 7: prep_rows<DK / 64, 1, 3>(p, xk, win, DK, CH, c, t0, n, h, lane, &L.K[0][0], RW); break;
-        case 8:
-        case 9: if (64 * (wave - 8) < DK) prep_gates<DK, 0, Tin>(p, t0, n, h, lane, 64 * (wave - 8), L.G); break;
-        case 10:
-        case 11: if (64 * (wave - 10) < DK) prep_gates<DK, 1, Tin>(p, t0, n, h, lane, 64 * (wave - 10), L.G); break;
-        case 12: {
-            const Tin bv = static_cast<const Tin *>(p.b)[(size_t)(t0 + min(lane, n - 1)) * H + h];
-            L.beta[lane] = lane < n ? sigmoid(to_f32(bv)) : 0.f;
-            break;
-        }
-        default: break;
-        }
-    }
+    // 1. the chunk's tokens: q^, k^ rows (conv + SiLU + L2 norm), the decay
+    //    prefix sums and beta into LDS
+    rows_compute<Tin, NC>(p, rraw, &L.Cw[choff + NC * lane], isq ? p.q_scale : 1.0f, n, lane, part,
+                          isq ? &L.Q[0][0] : &L.K[0][0], RW);
+    if (gate_wave) gates_compute<DK, Tin>(graw, &L.Cea[64 * gcg + 8 * (lane % 8)], n, lane, 64 * gcg, gqt, L.G);
+    if (wave == kIntraWaves - 1) L.beta[lane] = lane < n ? sigmoid(to_f32(bv)) : 0.f;
     __syncthreads();
 
     // 2. per 16-token block: may its diagonal tile use scaled factors
-    //    (waves 0-3)?  G at the block starts, block ends, the last token and
-    //    row 31 (the first half's total) (the other waves).
+    //    (waves 0-3)?  G (block-local) at the block starts, the block ends
+    //    (the block totals) and the last token (the other waves).
     const int last = max(n - 1, 0);
     constexpr int NPAIR = IntraLds<DK, DV>::NPAIR;
     if (wave < 4) {
@@ -490,9 +524,9 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
         for (int m = 32; m >= 1; m >>= 1) span = fmaxf(span, __shfl_xor(span, m, kWave));
         if (lane == 0) L.safe[wave] = span <= kSafeSpan ? 1 : 0;
     } else {
-        for (int e = tid - 4 * kWave; e < 10 * DK; e += kIntraThreads - 4 * kWave) {
+        for (int e = tid - 4 * kWave; e < 9 * DK; e += kIntraThreads - 4 * kWave) {
             const int j = e / DK, i = e % DK;
-            const int row = j < 4 ? 16 * j : j < 8 ? 16 * (j - 4) + 15 : j == 8 ? last : kChunk / 2 - 1;
+            const int row = j < 4 ? 16 * j : j < 8 ? 16 * (j - 4) + 15 : last;
             L.Gb[j][i] = L.G[row][i];
         }
     }
@@ -508,7 +542,26 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
             L.A[t][sv] = sv < t ? L.beta[t] * aA[rr] : 0.f;
             aP[rr] = sv <= t ? aP[rr] : 0.f;
         }
-        store_tile_split<kChunk>(L.scratch(wave), aP, lane, Ph, Pl, 16 * bt, 16 * bs);
+        store_tile_split<kChunk>(L.D[wave], aP, lane, Ph, Pl, 16 * bt, 16 * bs);
+        if (bt == bs) {
+            // the diagonal block of T = (I + A)^-1 from this wave's own A
+            // tile: column `lane` of (I + A_bb)^-1 by forward substitution
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            if (lane < 16) {
+                const int j = lane, o = 16 * bt;
+                float x[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    float acc = i == j ? 1.f : 0.f;
+#pragma unroll
+                    for (int m = 0; m < i; ++m) acc = fmaf(-L.A[o + i][o + m], x[m], acc);
+                    x[i] = acc;
+                    L.T[bt][i][j] = i >= j ? acc : 0.f;
+                }
+            }
+        }
     };
 
     // 2b. a block whose decay span is too wide for scaled factors has its
@@ -576,33 +629,82 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
         dg[0] = make_float4(ko[0], ko[1], ko[2], ko[3]);
         dg[1] = make_float4(ko[4], ko[5], ko[6], ko[7]);
     }
-    // (G of rows 32.. restarts from 0: rows of the two halves differ by
-    // the first half's total, Gb[9])
-    for (int e = tid; e < (NPAIR + 8) * DK; e += kIntraThreads) {
-        const int j = e / DK, i = e % DK;
-        const float g31 = L.Gb[9][i], glast = L.Gb[8][i] + (last >= kChunk / 2 ? g31 : 0.f);
-        if (j < NPAIR) {
-            // pair j = bt (bt + 1) / 2 + bs; on the diagonal the factor is
-            // >= 1 (<= 2^60 where it is used: the block passed the span check)
-            const int bt = j < 1 ? 0 : j < 3 ? 1 : j < 6 ? 2 : 3, bs = j - bt * (bt + 1) / 2;
-            L.M[j][i] = exp2_hw((L.Gb[bt][i] + (bt >= 2 ? g31 : 0.f)) - (L.Gb[4 + bs][i] + (bs >= 2 ? g31 : 0.f)));
-        } else if (j < NPAIR + 4) {
-            const int b = j - NPAIR;
-            L.Fq[b][i] = exp2_hw(L.Gb[b][i] + (b >= 2 ? g31 : 0.f));
-        } else {
-            const int b = j - NPAIR - 4;
-            L.Fk[b][i] = exp2_hw(glast - (L.Gb[4 + b][i] + (b >= 2 ? g31 : 0.f)));
+    // Exponents across blocks are sums of block totals Tb (G of a block's
+    // last row) and block-local values: with S_b = G at row 16 b and GL = G
+    // at the last token (block lb),
+    //   M (bt, bs) = e^(S_bt + sum_{bs < b < bt} T_b), or e^(S_b - T_b) on the diagonal;
+    //   Fq (b) = e^(sum_{b' < b} T_b' + S_b)  (block start -> chunk start);
+    //   Fk (b) = e^(sum_{b < b' < lb} T_b' + GL), e^(GL - T_b) for b = lb, 1 past lb;
+    //   e^(G_C) = e^(sum_{b < lb} T_b + GL).
+    if (tid < DK) {
+        const int i = tid, lb = last / 16;
+        float S[4], T[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            S[b] = L.Gb[b][i];
+            T[b] = L.Gb[4 + b][i];
         }
+        const float GL = L.Gb[8][i];
+#pragma unroll
+        for (int bt = 0; bt < 4; ++bt) {
+            float x = S[bt];
+#pragma unroll
+            for (int bs = bt; bs >= 0; --bs) {
+                // on the diagonal the factor is >= 1 (<= 2^60 where it is
+                // used: the block passed the span check)
+                L.M[bt * (bt + 1) / 2 + bs][i] = exp2_hw(bs == bt ? S[bt] - T[bt] : x);
+                if (bs < bt && bs > 0) x += T[bs];
+            }
+        }
+        float off = 0.f;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            L.Fq[b][i] = exp2_hw(off + S[b]);
+            off += T[b];
+        }
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            float x = 0.f;
+            if (b == lb) {
+                x = GL - T[b];
+            } else if (b < lb) {
+                x = GL;
+#pragma unroll
+                for (int b2 = 0; b2 < 4; ++b2)
+                    if (b2 > b && b2 < lb) x += T[b2];
+            }
+            L.Fk[b][i] = exp2_hw(x);
+        }
+        float gc = GL;
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+            if (b < lb) gc += T[b];
+        ws.gC[gh * DK + i] = exp2_hw(gc);
     }
-    if (tid < DK) ws.gC[gh * DK + tid] = exp2_hw(L.Gb[8][tid] + (last >= kChunk / 2 ? L.Gb[9][tid] : 0.f));
     __syncthreads();
 
+    // the raw v inputs of step 6 (U~ columns): a lane's channel vcol for
+    // rows 16 b + 4 lk .. + 3 and the three rows before each run (rows past
+    // the chunk's end repeat its last row; their beta is 0)
+    Tin vraw[4][7];
+    if (u_wave) {
+        const Tin *xv = static_cast<const Tin *>(p.x_v) + (size_t)h * DV + vcol;
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int j = 0; j < 7; ++j) {
+                const int q = 16 * b + 4 * lk + j - 3;   // chunk row of the input
+                const Tin *src = q < 0 && c == 0 ? win + (q + 3) * CH + 2 * DK + vcol
+                                                 : xv + (size_t)(t0 + min(c == 0 ? max(q, 0) : q, n - 1)) * H * DV;
+                vraw[b][j] = *src;
+            }
+    }
     // 4. A and P by token-block pair (bt, bs), bs <= bt: for t in block bt
     //    and s in block bs, e^(G_t - G_s) = e^(G_t - G_r) M_(bt,bs) e^(G_e - G_s)
     //    (r = 16 bt, e = 16 bs + 15): the rewritten q and k rows are the A
     //    operands, the rewritten k rows times the pair's factor the shared B
-    //    operand.  Ten pairs and the six zero P tiles above the diagonal,
-    //    two items per wave.
+    //    operand.  Ten pairs (a diagonal pair also inverts its block of
+    //    I + A) and the six zero P tiles above the diagonal, one item per wave.
     for (int j = wave; j < NPAIR + 6; j += kIntraWaves) {
         if (j >= NPAIR) {
             const int u = j - NPAIR, bt = u < 3 ? 0 : u < 5 ? 1 : 2, bs = u < 3 ? u + 1 : u < 5 ? u - 1 : 3;
@@ -663,115 +765,103 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
         *reinterpret_cast<bf16x8 *>(ws.K_hi + o) = sx.hi;
         *reinterpret_cast<bf16x8 *>(ws.K_lo + o) = sx.lo;
     }
+    __syncthreads();
 
-    // 5. T = (I + A)^-1 by 16 x 16 blocks: the diagonal blocks by forward
-    //    substitution, then block row b = 1, 2, 3 from
-    //    T_bb' = -T_bb sum_{b' <= m < b} A_bm T_mb'  (one wave per b' < b, MFMA)
-    for (int e = tid; e < kChunk * kChunk; e += kIntraThreads) L.T[e / kChunk][e % kChunk] = 0.f;
-    __syncthreads();
-    if (tid < 64) {   // diagonal blocks: column j of (I + A_bb)^-1
-        const int b = tid / 16, j = tid % 16, o = 16 * b;
-        float x[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            float acc = i == j ? 1.f : 0.f;
-#pragma unroll
-            for (int m = 0; m < i; ++m) acc = fmaf(-L.A[o + i][o + m], x[m], acc);
-            x[i] = acc;
-            L.T[o + i][o + j] = i >= j ? acc : 0.f;
-        }
+    const int gnext = gidx + wph;
+    const bool more = gnext < nchunks;
+    int c2 = 0, t02 = 0, n2 = 0;
+    const Tin *win2 = win;
+
+    // 6. [W | U~] = (I + A)^-1 R with R = [diag(beta) K^ e^G | diag(beta) V],
+    //    by block forward substitution in each wave's 16 columns:
+    //    X_b = T_bb (R_b - sum_{m < b} A_bm X_m).  A result tile of
+    //    v_mfma_f32_16x16x16_bf16 is laid out as its B operand (lane l: rows
+    //    4 (l / 16) .. + 3 of column l % 16), so the blocks chain in
+    //    registers.  -W is stored split in operand order, U~ in fp32.
+    if (wave >= NCT && more) {   // wave-uniform: no column tile
+        locate(gnext, c2, t02, n2, win2);
+        issue_rows(c2, t02, n2, win2, lane);
     }
-    __syncthreads();
-    for (int b = 1; b < 4; ++b) {
-        if (wave < b) {
-            const int bp = wave, K = 16 * (b - bp);
-            // Z = A[block b, columns 16 b' .. 16 b) T[rows 16 b' .. 16 b, block b']
-            f32x4 z = {0.f, 0.f, 0.f, 0.f};
-            for (int k0 = 0; k0 < K; k0 += 32) {
-                float xa[8], xb[8];
+    if (wave < NCT) {   // wave-uniform
+        const int ct = wave, col = 16 * ct + lr;
+        const bool isw = ct < DK / 16;   // wave-uniform
+        // conv (+ SiLU) of v for the U~ columns, as the q and k rows were
+        // formed, times beta: the R rows of this lane (the raw inputs die here)
+        float ru[4][4];
+        if (!isw) {
+            const float4 vwt = L.Cv[col - DK];
+            const float vw[4] = {vwt.x, vwt.y, vwt.z, vwt.w};
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int kk = k0 + 8 * lk + e;
-                    xa[e] = kk < K ? L.A[16 * b + lr][16 * bp + kk] : 0.f;
-                    xb[e] = kk < K ? L.T[16 * bp + kk][16 * bp + lr] : 0.f;
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    float a = vw[0] * to_f32(vraw[b][j]);
+                    a = fmaf(vw[1], to_f32(vraw[b][j + 1]), a);
+                    a = fmaf(vw[2], to_f32(vraw[b][j + 2]), a);
+                    a = fmaf(vw[3], to_f32(vraw[b][j + 3]), a);
+                    ru[b][j] = L.beta[16 * b + 4 * lk + j] * (p.silu ? silu_hw(a) : a);
                 }
-                z = mma3(split8(xa), split8(xb), z);
-            }
-            // result layout to operand layout through this wave's scratch
-#pragma unroll
-            for (int r = 0; r < 4; ++r) L.Z[bp][4 * lk + r][lr] = z[r];
-            __builtin_amdgcn_wave_barrier();
-            float xa[8], xb[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int kk = 8 * lk + e;
-                xa[e] = kk < 16 ? L.T[16 * b + lr][16 * b + kk] : 0.f;
-                xb[e] = kk < 16 ? L.Z[bp][kk][lr] : 0.f;
-            }
-            const f32x4 t = mma3(split8(xa), split8(xb), f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-            for (int r = 0; r < 4; ++r) L.T[16 * b + 4 * lk + r][16 * bp + lr] = -t[r];
         }
-        __syncthreads();
-    }
-
-    // 6. [W | U~] = T R with R = [diag(beta) K^ e^G | diag(beta) V]  (MFMA);
-    //    W is stored negated and split for the scan, U~ in fp32
-    Split8 ta[4][2];
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-            float x[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = L.T[16 * rt + lr][32 * k2 + 8 * lk + e];
-            ta[rt][k2] = split8(x);
+        // the next chunk's rows, gates and beta, in flight through the rest
+        // of step 6 (issued once the raw v inputs are used: the registers
+        // are shared)
+        if (more) {
+            locate(gnext, c2, t02, n2, win2);
+            issue_rows(c2, t02, n2, win2, lane);
         }
+        Split4 xs[3];
 #pragma unroll
-    for (int ci = 0; ci < 2; ++ci) {
-        const int ct = wave + kIntraWaves * ci;
-        if (ct >= NCT) continue;                   // wave-uniform
-        const int col = 16 * ct + lr;
-        const bool isw = ct < DK / 16;             // wave-uniform
-        Split8 rb[2];
+        for (int b = 0; b < 4; ++b) {
+            f32x4 acc;
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-            float x[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int sv = 32 * k2 + 8 * lk + e;
+            for (int j = 0; j < 4; ++j) {
+                const int sv = 16 * b + 4 * lk + j;
+                float r;
                 if (isw) {
                     // beta_s k^_s e^(G_s): the rewritten k row (hi + lo) times
                     // e^(G_r) of its block
                     const __bf16 *kr = reinterpret_cast<const __bf16 *>(&L.K[sv][0]) + 2 * (col & ~7) + (col & 7);
-                    x[e] = L.beta[sv] * (((float)kr[0] + (float)kr[8]) * L.Fq[sv / 16][col]);
+                    r = ((float)kr[0] + (float)kr[8]) * L.Fq[b][col];
+                    acc[j] = L.beta[sv] * r;
                 } else {
-                    // conv (+ SiLU) of v, as the q and k rows were formed
-                    const float4 w = vwt[ci];
-                    float acc = w.x * to_f32(vraw[ci][k2][e]);
-                    acc = fmaf(w.y, to_f32(vraw[ci][k2][e + 1]), acc);
-                    acc = fmaf(w.z, to_f32(vraw[ci][k2][e + 2]), acc);
-                    acc = fmaf(w.w, to_f32(vraw[ci][k2][e + 3]), acc);
-                    x[e] = L.beta[sv] * (p.silu ? silu_hw(acc) : acc);
+                    acc[j] = ru[b][j];
                 }
             }
-            rb[k2] = split8(x);
-        }
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            acc = mma3(ta[rt][0], rb[0], acc);
-            if (rt >= 2) acc = mma3(ta[rt][1], rb[1], acc);   // T is lower triangular
+            for (int m = 0; m < b; ++m) {
+                float a4[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) a4[j] = -L.A[16 * b + lr][16 * m + 4 * lk + j];
+                acc = mma3k16(split4(a4), xs[m], acc);
+            }
+            float t4[4], y4[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                t4[j] = L.T[b][lr][4 * lk + j];
+                y4[j] = acc[j];
+            }
+            const f32x4 x = mma3k16(split4(t4), split4(y4), f32x4{0.f, 0.f, 0.f, 0.f});
+            if (b < 3) {
+                float x4[4] = {x[0], x[1], x[2], x[3]};
+                xs[b] = split4(x4);
+            }
             if (isw) {
-                const f32x4 wn = -acc;
-                store_tile_split<DK>(L.scratch(wave), wn, lane, ws.Wn_hi + gh * kChunk * DK, ws.Wn_lo + gh * kChunk * DK,
-                                     16 * rt, 16 * ct);
+                store_tile_split<DK>(L.D[wave], -x, lane, ws.Wn_hi + gh * kChunk * DK, ws.Wn_lo + gh * kChunk * DK,
+                                     16 * b, 16 * ct);
             } else {
 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr)
-                    ws.Ut[gh * kChunk * DV + (16 * rt + 4 * lk + rr) * DV + (col - DK)] = acc[rr];
+                for (int j = 0; j < 4; ++j)
+                    ws.Ut[gh * kChunk * DV + (16 * b + 4 * lk + j) * DV + (col - DK)] = x[j];
             }
         }
+    }
+    if (!more) break;
+    __syncthreads();   // the next chunk's step 1 rewrites what step 6 reads
+    gidx = gnext;
+    c = c2;
+    t0 = t02;
+    n = n2;
+    win = win2;
     }
 }
 
@@ -1154,7 +1244,14 @@ static kda_status launch_prefill_typed(const PrefillParams &p, hipStream_t strea
         const kda_status st = launch_recurrent(r, DK, DV, sizeof(Tin) == 2 ? KDA_BF16 : KDA_F32, RecKind::decode,
                                                stream);
         if (st != KDA_OK) return st;
-        hipLaunchKernelGGL((kda_prefill_intra_kernel<DK, DV, Tin>), dim3((unsigned)((size_t)p.H * ws.G_max)),
+        // one workgroup per compute unit (the LDS of one), each working
+        // through the chunks of one head
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            return KDA_ERR_LAUNCH;
+        const int wph = std::max(1, std::min(ws.G_max, cus / p.H));
+        hipLaunchKernelGGL((kda_prefill_intra_kernel<DK, DV, Tin>), dim3((unsigned)((size_t)p.H * wph)),
                            dim3(kIntraThreads), 0, stream, p, ws);
     }
     hipLaunchKernelGGL((kda_prefill_scan_kernel<DK, DV, Tin>),
