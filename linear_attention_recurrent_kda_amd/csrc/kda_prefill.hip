@@ -31,6 +31,7 @@ namespace kda {
 
 constexpr int kChunk = 64;
 constexpr int kColBlock = 16;
+constexpr int kBufferWord3 = 0x00020000;   // raw 32-bit buffer resource
 constexpr float kLog2e = 1.4426950408889634f;
 
 // Device pointers into the caller's workspace.  The per-chunk factors the
@@ -410,6 +411,27 @@ __device__ __forceinline__ void lds8(const float *src, float *x) {
     x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
 }
 
+// Sum over the four 16-lane rows of a wave (lanes l, l ^ 16, l ^ 32,
+// l ^ 48), every lane receiving it: VALU lane-row swaps.
+__device__ __forceinline__ float row4_sum(float v) {
+    const unsigned u = __float_as_uint(v);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const float s = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const unsigned us = __float_as_uint(s);
+    const auto b = __builtin_amdgcn_permlane32_swap(us, us, false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// One element through a raw buffer load (an offset past the buffer's range
+// reads 0).
+template <typename Tin> __device__ __forceinline__ Tin buffer_load_elem(__amdgpu_buffer_rsrc_t r, unsigned off);
+template <> __device__ __forceinline__ uint16_t buffer_load_elem<uint16_t>(__amdgpu_buffer_rsrc_t r, unsigned off) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+}
+template <> __device__ __forceinline__ float buffer_load_elem<float>(__amdgpu_buffer_rsrc_t r, unsigned off) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+
 // bf16x3 on v_mfma_f32_16x16x16_bf16 (4 operand elements per lane)
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 struct Split4 {
@@ -549,17 +571,20 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            if (lane < 16) {
-                const int j = lane, o = 16 * bt;
-                float x[16];
+            // (the sum over earlier rows is split over the four lane rows,
+            // m = 4 m' + lk, and combined by lane-row swaps; A_bb is zero on
+            // and above its diagonal)
+            const int o = 16 * bt;
+            float xs[4] = {0.f, 0.f, 0.f, 0.f};   // x_m, m = 4 m' + lk
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    float acc = i == j ? 1.f : 0.f;
+            for (int i = 0; i < 16; ++i) {
+                float part = 0.f;
 #pragma unroll
-                    for (int m = 0; m < i; ++m) acc = fmaf(-L.A[o + i][o + m], x[m], acc);
-                    x[i] = acc;
-                    L.T[bt][i][j] = i >= j ? acc : 0.f;
-                }
+                for (int mp = 0; mp < 4; ++mp)
+                    if (4 * mp < i) part = fmaf(L.A[o + i][o + 4 * mp + lk], xs[mp], part);
+                const float xi = (i == lr ? 1.f : 0.f) - row4_sum(part);
+                if (lk == i % 4) xs[i / 4] = xi;
+                if (lk == 0) L.T[bt][i][lr] = xi;
             }
         }
     };
@@ -686,18 +711,29 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
     // the raw v inputs of step 6 (U~ columns): a lane's channel vcol for
     // rows 16 b + 4 lk .. + 3 and the three rows before each run (rows past
     // the chunk's end repeat its last row; their beta is 0)
+    //    As raw buffer loads over rows t0 - sh .. t0 + n - 1 (sh = 3, or 0 at
+    //    chunk 0): a row outside that range reads 0 (past the chunk's end
+    //    beta is 0; before the sequence the conv window supplies it).
     Tin vraw[4][7];
     if (u_wave) {
-        const Tin *xv = static_cast<const Tin *>(p.x_v) + (size_t)h * DV + vcol;
+        const int sh = c == 0 ? 0 : 3;
+        const unsigned rowb = (unsigned)(H * DV * sizeof(Tin));
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<Tin *>(static_cast<const Tin *>(p.x_v) + ((size_t)(t0 - sh) * H + h) * DV + 16 * wave - DK), 0,
+            (int)((unsigned)(n + sh) * rowb), kBufferWord3);
+        const unsigned vo = (unsigned)(4 * lk) * rowb + (unsigned)(lr * sizeof(Tin));
 #pragma unroll
         for (int b = 0; b < 4; ++b)
 #pragma unroll
             for (int j = 0; j < 7; ++j) {
-                const int q = 16 * b + 4 * lk + j - 3;   // chunk row of the input
-                const Tin *src = q < 0 && c == 0 ? win + (q + 3) * CH + 2 * DK + vcol
-                                                 : xv + (size_t)(t0 + min(c == 0 ? max(q, 0) : q, n - 1)) * H * DV;
-                vraw[b][j] = *src;
+                // chunk row 16 b + 4 lk + j - 3; negative offsets wrap past the range
+                const unsigned off = vo + (unsigned)(16 * b + j - 3 + sh) * rowb;
+                vraw[b][j] = buffer_load_elem<Tin>(rs, off);
             }
+        if (c == 0 && lk == 0) {   // rows -3 .. -1 of the first chunk
+#pragma unroll
+            for (int j = 0; j < 3; ++j) vraw[0][j] = win[j * CH + 2 * DK + vcol];
+        }
     }
     // 4. A and P by token-block pair (bt, bs), bs <= bt: for t in block bt
     //    and s in block bs, e^(G_t - G_s) = e^(G_t - G_r) M_(bt,bs) e^(G_e - G_s)
@@ -705,7 +741,11 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
     //    operands, the rewritten k rows times the pair's factor the shared B
     //    operand.  Ten pairs (a diagonal pair also inverts its block of
     //    I + A) and the six zero P tiles above the diagonal, one item per wave.
-    for (int j = wave; j < NPAIR + 6; j += kIntraWaves) {
+    // items by wave: the diagonal pairs 0 2 5 9 on waves 0-3, the other
+    // pairs on 4-9, the zero tiles on 10-15 (waves 8-15 also request the v
+    // inputs of step 6)
+    {
+        const int j = (int)((0xFEDCBA8764319520ull >> (4 * wave)) & 15u);
         if (j >= NPAIR) {
             const int u = j - NPAIR, bt = u < 3 ? 0 : u < 5 ? 1 : 2, bs = u < 3 ? u + 1 : u < 5 ? u - 1 : 3;
             if (lane < 32) {
@@ -714,10 +754,9 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
                 *reinterpret_cast<bf16x8 *>(Ph + o) = z;
                 *reinterpret_cast<bf16x8 *>(Pl + o) = z;
             }
-            continue;
-        }
+        } else {
         const int bt = j < 1 ? 0 : j < 3 ? 1 : j < 6 ? 2 : 3, bs = j - bt * (bt + 1) / 2;
-        if (bt == bs && !L.safe[bt]) continue;   // summed directly above
+        if (!(bt == bs && !L.safe[bt])) {   // else summed directly above
         const int t = 16 * bt + lr, sr = 16 * bs + lr;
         f32x4 aA = {0.f, 0.f, 0.f, 0.f}, aP = aA;
 #pragma unroll
@@ -735,6 +774,8 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
             aP = mma3(Split8{qa[0], qa[1]}, b, aP);
         }
         gram_out(bt, bs, aA, aP);
+        }
+        }
     }
     // decayed factors for the scan: Q^ e^G (rows), (K^ e^(G_C - G))^T
     //    Unit e8 (8 elements) is stored at 8 e8 in operand order, so each wave
