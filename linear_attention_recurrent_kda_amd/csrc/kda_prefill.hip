@@ -376,6 +376,36 @@ __device__ __forceinline__ void gates_compute(const typename Vec8<Tin>::T (&raw)
 
 constexpr float kSafeSpan = 60.f;
 
+// bf16x3 splits with the paired conversion (v_cvt_pk_bf16_f32 rounds two
+// fp32 values to nearest even in one instruction): x = hi + lo, hi = bf16(x),
+// lo = bf16(x - hi), three instructions per value.
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ unsigned pack_bf16(float a, float b) {
+    const f32x2v v = {a, b};
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2v));
+}
+__device__ __forceinline__ void split_pair(float a, float b, unsigned &hi, unsigned &lo) {
+    hi = pack_bf16(a, b);
+    lo = pack_bf16(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
+}
+__device__ __forceinline__ Split8 split8p(const float *x) {
+    u32x4v h, l;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        unsigned a, b;
+        split_pair(x[2 * i], x[2 * i + 1], a, b);
+        h[i] = a;
+        l[i] = b;
+    }
+    Split8 s;
+    s.hi = __builtin_bit_cast(bf16x8, h);
+    s.lo = __builtin_bit_cast(bf16x8, l);
+    return s;
+}
+
 // A 16 x 16 fp32 tile in the MFMA result layout (lane l holds rows
 // 4 (l / 16) + r, column l % 16) written to a split bf16 matrix with K
 // columns in operand order, as 16-byte stores: through the wave's LDS
@@ -388,17 +418,13 @@ __device__ __forceinline__ void store_tile_split(float (*scr)[17], const f32x4 &
     __builtin_amdgcn_wave_barrier();
     if (lane < 32) {
         const int row = lane % 16, kq = lane / 16;
-        bf16x8 hv, lv;
+        float x[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float x = scr[row][8 * kq + e];
-            const __bf16 hb = (__bf16)x;
-            hv[e] = hb;
-            lv[e] = (__bf16)(x - (float)hb);
-        }
+        for (int e = 0; e < 8; ++e) x[e] = scr[row][8 * kq + e];
+        const Split8 sx = split8p(x);
         const size_t o = opnd_off<K>(row0 + row, col0 + 8 * kq);
-        *reinterpret_cast<bf16x8 *>(hi + o) = hv;
-        *reinterpret_cast<bf16x8 *>(lo + o) = lv;
+        *reinterpret_cast<bf16x8 *>(hi + o) = sx.hi;
+        *reinterpret_cast<bf16x8 *>(lo + o) = sx.lo;
     }
     __builtin_amdgcn_wave_barrier();
 }
@@ -438,13 +464,17 @@ struct Split4 {
     s16x4 hi, lo;
 };
 __device__ __forceinline__ Split4 split4(const float *x) {
-    Split4 s;
+    u32x2v h, l;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const __bf16 h = (__bf16)x[e];
-        s.hi[e] = __builtin_bit_cast(short, h);
-        s.lo[e] = __builtin_bit_cast(short, (__bf16)(x[e] - (float)h));
+    for (int i = 0; i < 2; ++i) {
+        unsigned a, b;
+        split_pair(x[2 * i], x[2 * i + 1], a, b);
+        h[i] = a;
+        l[i] = b;
     }
+    Split4 s;
+    s.hi = __builtin_bit_cast(s16x4, h);
+    s.lo = __builtin_bit_cast(s16x4, l);
     return s;
 }
 __device__ __forceinline__ f32x4 mma3k16(const Split4 &a, const Split4 &b, f32x4 acc) {
@@ -506,11 +536,9 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
     };
     RT rraw[11];
     V8 graw[2];
-    Tin bv = Tin(0);
     auto issue_rows = [&](int c_, int t0_, int n_, const Tin *win_, int ln) {
         rows_issue<Tin, NC>(p, xr, win_, choff, CH, c_, t0_, n_, h, ln, part, rraw);
         if (gate_wave) gates_issue<DK, Tin>(p, t0_, n_, h, ln, 64 * gcg, gqt, graw);
-        if (wave == kIntraWaves - 1) bv = static_cast<const Tin *>(p.b)[(size_t)(t0_ + min(ln, n_ - 1)) * H + h];
     };
     int c, t0, n;
     const Tin *win;
@@ -527,7 +555,9 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
     const int lane = tid % kWave, lr = lane % 16, lk = lane / 16;
     const size_t gh = (size_t)gidx * H + h;
     // 1. the chunk's tokens: q^, k^ rows (conv + SiLU + L2 norm), the decay
-    //    prefix sums and beta into LDS
+    //    prefix sums and beta into LDS (beta requested here: one value)
+    Tin bv = Tin(0);
+    if (wave == kIntraWaves - 1) bv = static_cast<const Tin *>(p.b)[(size_t)(t0 + min(lane, n - 1)) * H + h];
     rows_compute<Tin, NC>(p, rraw, &L.Cw[choff + NC * lane], isq ? p.q_scale : 1.0f, n, lane, part,
                           isq ? &L.Q[0][0] : &L.K[0][0], RW);
     if (gate_wave) gates_compute<DK, Tin>(graw, &L.Cea[64 * gcg + 8 * (lane % 8)], n, lane, 64 * gcg, gqt, L.G);
@@ -644,7 +674,7 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
             q[e] *= ein;
             k[e] *= ein;
         }
-        const Split8 sq = split8(q), sk = split8(k);
+        const Split8 sq = split8p(q), sk = split8p(k);
         bf16x8 *dq = reinterpret_cast<bf16x8 *>(&L.Q[t][c0]), *dk = reinterpret_cast<bf16x8 *>(&L.K[t][c0]);
         dq[0] = sq.hi;
         dq[1] = sq.lo;
@@ -769,7 +799,7 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
             lds8(&L.M[j][c0], m);
 #pragma unroll
             for (int e = 0; e < 8; ++e) kb[e] *= m[e];
-            const Split8 b = split8(kb);
+            const Split8 b = split8p(kb);
             aA = mma3(Split8{ka[0], ka[1]}, b, aA);
             aP = mma3(Split8{qa[0], qa[1]}, b, aP);
         }
@@ -789,7 +819,7 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
         lds8(&L.Fq[r / 16][i0], f);
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] = ((float)h8[e] + (float)l8[e]) * f[e];
-        const Split8 sx = split8(x);
+        const Split8 sx = split8p(x);
         const size_t o = gh * kChunk * DK + (size_t)8 * e8;   // = opnd_off<DK>(r, i0)
         *reinterpret_cast<bf16x8 *>(ws.Q_hi + o) = sx.hi;
         *reinterpret_cast<bf16x8 *>(ws.Q_lo + o) = sx.lo;
@@ -801,7 +831,7 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
         float x[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] = L.G[r0 + e][i] * fk;   // k^ rows past n are zero
-        const Split8 sx = split8(x);
+        const Split8 sx = split8p(x);
         const size_t o = gh * DK * kChunk + (size_t)8 * e8;   // = opnd_off<kChunk>(i, r0)
         *reinterpret_cast<bf16x8 *>(ws.K_hi + o) = sx.hi;
         *reinterpret_cast<bf16x8 *>(ws.K_lo + o) = sx.lo;
