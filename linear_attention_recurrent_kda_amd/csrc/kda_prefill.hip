@@ -208,8 +208,12 @@ struct __align__(16) IntraLds {
     float M[NPAIR][DK];                 // e^(G_{16 bt} - G_{16 bs + 15}) per block pair
     float Fq[4][DK];                    // e^(G_{16 b}): block start -> chunk start
     float Fk[4][DK];                    // e^(G_last - G_{16 b + 15}): block end -> chunk end
-    float A[kChunk][kChunk + 1];        // beta_t (K K^T * decay), strictly lower part used
-    float T[4][16][20];                 // the diagonal 16 x 16 blocks of (I + A)^-1
+    // -A (A_ts = beta_t k^_t k^_s decay, s < t; zero on and above the
+    // diagonal) and the diagonal 16 x 16 blocks of T = (I + A)^-1, split into
+    // bf16 pairs: rows of 4 consecutive elements are operands of
+    // v_mfma_f32_16x16x16_bf16
+    __bf16 NAh[kChunk][kChunk + 4], NAl[kChunk][kChunk + 4];
+    __bf16 Th[4][16][20], Tl[4][16][20];
     float Gb[9][DK];                    // G at the block starts, block ends, the last token
     float D[10][16][17];                // per-wave scratch of waves 0..9: direct tiles, tile stores
     float beta[kChunk];
@@ -588,33 +592,43 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
     // split to the workspace, from a tile pair in the MFMA result layout
     uint16_t *Ph = ws.P_hi + gh * kChunk * kChunk, *Pl = ws.P_lo + gh * kChunk * kChunk;
     auto gram_out = [&](int bt, int bs, f32x4 aA, f32x4 aP) {
+        float na[4];
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
             const int t = 16 * bt + 4 * lk + rr, sv = 16 * bs + lr;
-            L.A[t][sv] = sv < t ? L.beta[t] * aA[rr] : 0.f;
+            na[rr] = sv < t ? -L.beta[t] * aA[rr] : 0.f;
+            const __bf16 hb = (__bf16)na[rr];
+            L.NAh[t][sv] = hb;
+            L.NAl[t][sv] = (__bf16)(na[rr] - (float)hb);
             aP[rr] = sv <= t ? aP[rr] : 0.f;
         }
         store_tile_split<kChunk>(L.D[wave], aP, lane, Ph, Pl, 16 * bt, 16 * bs);
         if (bt == bs) {
             // the diagonal block of T = (I + A)^-1 from this wave's own A
-            // tile: column `lane` of (I + A_bb)^-1 by forward substitution
+            // tile (in fp32 through its scratch): column lr of (I + A_bb)^-1
+            // by forward substitution
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) L.D[wave][4 * lk + rr][lr] = na[rr];
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             // (the sum over earlier rows is split over the four lane rows,
             // m = 4 m' + lk, and combined by lane-row swaps; A_bb is zero on
             // and above its diagonal)
-            const int o = 16 * bt;
             float xs[4] = {0.f, 0.f, 0.f, 0.f};   // x_m, m = 4 m' + lk
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 float part = 0.f;
 #pragma unroll
                 for (int mp = 0; mp < 4; ++mp)
-                    if (4 * mp < i) part = fmaf(L.A[o + i][o + 4 * mp + lk], xs[mp], part);
-                const float xi = (i == lr ? 1.f : 0.f) - row4_sum(part);
+                    if (4 * mp < i) part = fmaf(L.D[wave][i][4 * mp + lk], xs[mp], part);
+                const float xi = (i == lr ? 1.f : 0.f) + row4_sum(part);
                 if (lk == i % 4) xs[i / 4] = xi;
-                if (lk == 0) L.T[bt][i][lr] = xi;
+                if (lk == 0) {
+                    const __bf16 hb = (__bf16)xi;
+                    L.Th[bt][i][lr] = hb;
+                    L.Tl[bt][i][lr] = (__bf16)(xi - (float)hb);
+                }
             }
         }
     };
@@ -641,13 +655,13 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
             f32x4 aA, aP;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                L.A[t][r + 4 * lk + j] = da[j];
+                L.D[wave + 4][lr][4 * lk + j] = da[j];
                 L.D[wave][lr][4 * lk + j] = dp[j];
             }
             __builtin_amdgcn_wave_barrier();
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
-                aA[rr] = L.A[r + 4 * lk + rr][r + lr];
+                aA[rr] = L.D[wave + 4][4 * lk + rr][lr];
                 aP[rr] = L.D[wave][4 * lk + rr][lr];
             }
             __builtin_amdgcn_wave_barrier();
@@ -900,18 +914,18 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
             }
 #pragma unroll
             for (int m = 0; m < b; ++m) {
-                float a4[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) a4[j] = -L.A[16 * b + lr][16 * m + 4 * lk + j];
-                acc = mma3k16(split4(a4), xs[m], acc);
+                Split4 na;
+                na.hi = *reinterpret_cast<const s16x4 *>(&L.NAh[16 * b + lr][16 * m + 4 * lk]);
+                na.lo = *reinterpret_cast<const s16x4 *>(&L.NAl[16 * b + lr][16 * m + 4 * lk]);
+                acc = mma3k16(na, xs[m], acc);
             }
-            float t4[4], y4[4];
+            float y4[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                t4[j] = L.T[b][lr][4 * lk + j];
-                y4[j] = acc[j];
-            }
-            const f32x4 x = mma3k16(split4(t4), split4(y4), f32x4{0.f, 0.f, 0.f, 0.f});
+            for (int j = 0; j < 4; ++j) y4[j] = acc[j];
+            Split4 tt;
+            tt.hi = *reinterpret_cast<const s16x4 *>(&L.Th[b][lr][4 * lk]);
+            tt.lo = *reinterpret_cast<const s16x4 *>(&L.Tl[b][lr][4 * lk]);
+            const f32x4 x = mma3k16(tt, split4(y4), f32x4{0.f, 0.f, 0.f, 0.f});
             if (b < 3) {
                 float x4[4] = {x[0], x[1], x[2], x[3]};
                 xs[b] = split4(x4);
