@@ -1240,30 +1240,41 @@ __device__ __forceinline__ void load4(const float *src, float *x) {
 template <int DV, typename Tin>
 __global__ __launch_bounds__(256) void kda_prefill_norm_kernel(PrefillParams p, PrefillWs ws) {
     constexpr int LPR = DV / 4, RPW = kWave / LPR, RPB = 4 * RPW;   // lanes per row, rows per wave / block pass
+    constexpr int NP = kNormRows / RPB;                               // passes, all loads issued first
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     const int H = p.H, c0 = 4 * (lane % LPR);
     const size_t nrows = (size_t)p.total_T * H;
     const bool valid = ws.meta[0] == 1;
     const bool ones = ws.meta[2 * p.N_seq + 3] > 0;   // any rows already final
-#pragma unroll 2
-    for (int pass = 0; pass < kNormRows / RPB; ++pass) {
+    typedef float v4f __attribute__((ext_vector_type(4)));
+    v4f o[NP];
+    float zf[NP][4];
+    size_t rr[NP];
+    bool in[NP];
+#pragma unroll
+    for (int pass = 0; pass < NP; ++pass) {
         const size_t r = (size_t)blockIdx.x * kNormRows + pass * RPB + wave * RPW + lane / LPR;
-        const bool in = r < nrows;
-        const size_t rr = in ? r : 0;
-        const int t = (int)(rr / H), h = (int)(rr % H);
-        bool live = in && valid, done = false;
+        in[pass] = r < nrows;
+        rr[pass] = in[pass] ? r : 0;
+        // y is read once and rewritten: streamed past the caches
+        o[pass] = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(p.y + rr[pass] * DV + c0));
+        load4(static_cast<const Tin *>(p.z) + rr[pass] * DV + c0, zf[pass]);
+    }
+#pragma unroll
+    for (int pass = 0; pass < NP; ++pass) {
+        const int t = (int)(rr[pass] / H), h = (int)(rr[pass] % H);
+        bool live = in[pass] && valid, done = false;
         if (live) {
-            const int sq = upper_index(p.cu_seqlens, p.N_seq + 1, t);
+            const int sq = p.N_seq == 1 ? 0 : upper_index(p.cu_seqlens, p.N_seq + 1, t);
             live = slot_ok(p.slot_idx[sq], p.n_slots);
             // rows of one-token sequences are already final (decode kernel)
             if (ones) done = live && p.cu_seqlens[sq + 1] - p.cu_seqlens[sq] == 1;
         }
-        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (in) o = *reinterpret_cast<const float4 *>(p.y + rr * DV + c0);
-        float ss = o.x * o.x;
-        ss = fmaf(o.y, o.y, ss);
-        ss = fmaf(o.z, o.z, ss);
-        ss = fmaf(o.w, o.w, ss);
+        const v4f v = o[pass];
+        float ss = v.x * v.x;
+        ss = fmaf(v.y, v.y, ss);
+        ss = fmaf(v.z, v.z, ss);
+        ss = fmaf(v.w, v.w, ss);
         // row sums: DPP inside each 16-lane row, then (d_v = 128) across row pairs
         ss = dpp_add<0xB1, 0xF>(ss);
         ss = dpp_add<0x4E, 0xF>(ss);
@@ -1276,16 +1287,14 @@ __global__ __launch_bounds__(256) void kda_prefill_norm_kernel(PrefillParams p, 
             ss = lane < 32 ? s_lo : s_hi;
         }
         const float rn = 1.0f / sqrtf(ss * (1.0f / DV) + p.rms_eps);
-        float zf[4];
-        load4(static_cast<const Tin *>(p.z) + rr * DV + c0, zf);
         const float4 w = *reinterpret_cast<const float4 *>(p.norm_w + h * DV + c0);
-        float4 out;
-        out.x = o.x * rn * (w.x * sigmoid(zf[0]));
-        out.y = o.y * rn * (w.y * sigmoid(zf[1]));
-        out.z = o.z * rn * (w.z * sigmoid(zf[2]));
-        out.w = o.w * rn * (w.w * sigmoid(zf[3]));
-        if (!live) out = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (in && !done) *reinterpret_cast<float4 *>(p.y + rr * DV + c0) = out;
+        v4f out;
+        out.x = v.x * rn * (w.x * sigmoid(zf[pass][0]));
+        out.y = v.y * rn * (w.y * sigmoid(zf[pass][1]));
+        out.z = v.z * rn * (w.z * sigmoid(zf[pass][2]));
+        out.w = v.w * rn * (w.w * sigmoid(zf[pass][3]));
+        if (!live) out = v4f{0.f, 0.f, 0.f, 0.f};
+        if (in[pass] && !done) __builtin_nontemporal_store(out, reinterpret_cast<v4f *>(p.y + rr[pass] * DV + c0));
     }
 }
 
