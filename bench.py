@@ -527,20 +527,20 @@ def decode_b1_leg(torch, api, synth, resident, steps=1000, graph_steps=100):
             "algorithmic_gbs_graph": bl / gs / 1e9, "steps": steps}
 
 
-def prefill_mfma_per_chunk_head(dk, dv, col_block=16):
-    """v_mfma_f32_16x16x32_bf16 instructions the chunked prefill issues per
-    (chunk, head); bf16x3 makes three of them per fp32 16x16x32 product.
-    intra: the 10 Gram tiles on or below the diagonal, A and P, d_k/32 steps
-    each; [W | U~] = T R over (d_k + d_v)/16 column tiles, 1+1+2+2 steps over
-    the four lower-triangular row tiles of T; the off-diagonal blocks of T
-    itself, 13 steps (Z = A T then -T_bb Z for the six blocks below the
-    diagonal, K = 16, 32 or 48 padded to steps of 32).  scan, per block of 16 state
-    columns: W S and Q S (d_k/32 steps for each of 4 row tiles), P U (1, 1, 2
-    and 2 steps for the 4 row tiles: P is lower triangular), Kd^T U (2 steps x
-    d_k/16 row tiles)."""
+def prefill_mfma_flops_per_chunk_head(dk, dv, col_block=16):
+    """Flops the chunked prefill issues on MFMA per (chunk, head); bf16x3 makes
+    three MFMA products per fp32 product.
+    intra: the 10 Gram tile pairs on or below the diagonal, A and P, d_k/32
+    steps of v_mfma_f32_16x16x32_bf16 each; [W | U~] by block forward
+    substitution over (d_k + d_v)/16 column tiles, 1 + 2 + 3 + 4 products of
+    v_mfma_f32_16x16x16_bf16 per tile.  scan, per block of 16 state columns
+    (16x16x32): W S and Q S (d_k/32 steps for each of 4 row tiles), P U (1, 1,
+    2 and 2 steps for the 4 row tiles: P is lower triangular), Kd^T U (2 steps
+    x d_k/16 row tiles)."""
     ks = dk // 32
-    intra = 3 * (10 * 2 * ks + (dk + dv) // 16 * 6 + 13)
-    scan = 3 * (dv // col_block) * (4 * 2 * ks + 6 + (dk // 16) * 2)
+    x32, x16 = 16 * 16 * 32 * 2, 16 * 16 * 16 * 2
+    intra = 3 * (10 * 2 * ks) * x32 + 3 * (dk + dv) // 16 * 10 * x16
+    scan = 3 * (dv // col_block) * (4 * 2 * ks + 6 + (dk // 16) * 2) * x32
     return intra + scan
 
 
@@ -580,7 +580,7 @@ def prefill_extra(torch, api, synth, stream):
     st_b = 2 * H * dk * dv * 4
     tot = in_b + out_b + st_b
     chunk_heads = (T + 63) // 64 * H
-    mfma_flops = prefill_mfma_per_chunk_head(dk, dv) * 16 * 16 * 32 * 2 * chunk_heads
+    mfma_flops = prefill_mfma_flops_per_chunk_head(dk, dv) * chunk_heads
     alg_flops = prefill_algorithmic_flops_per_chunk_head(dk, dv) * chunk_heads
     # the same call keeping a state checkpoint every 8192 tokens (4 per call)
     ck = torch.arange(1, 5, dtype=torch.int32, device="cuda:0").reshape(1, 4)

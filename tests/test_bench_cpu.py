@@ -29,13 +29,15 @@ def test_verify_and_commit_bytes():
 
 
 def test_prefill_flop_counts_are_positive_and_ordered():
-    issued = bench.prefill_mfma_per_chunk_head(128, 128)
-    # intra 567 + scan 1296 v_mfma_f32_16x16x32_bf16 (the count the MFMA
-    # instruction counter reads: 500.1 GFLOP per 32768-token call)
-    assert issued == 567 + 1296
-    assert issued * 16 * 16 * 32 * 2 * (32768 // 64) * 32 == 500095254528
+    issued = bench.prefill_mfma_flops_per_chunk_head(128, 128)
+    # intra: 240 v_mfma_f32_16x16x32_bf16 (Gram) + 480 v_mfma_f32_16x16x16_bf16
+    # ([W | U~]); scan: 1296 of 16x16x32 -- the flops the MFMA instruction
+    # counter reads: 476.7 GFLOP per 32768-token call
+    x32, x16 = 16 * 16 * 32 * 2, 16 * 16 * 16 * 2
+    assert issued == (240 + 1296) * x32 + 480 * x16
+    assert issued * (32768 // 64) * 32 == 476741369856
     alg = bench.prefill_algorithmic_flops_per_chunk_head(128, 128)
-    assert 0 < alg < issued * 16 * 16 * 32 * 2
+    assert 0 < alg < issued
 
 
 def test_bench_refuses_more_than_one_gpu():
