@@ -170,24 +170,30 @@ __global__ __launch_bounds__(64) void kda_prefill_meta_kernel(PrefillParams p, P
 }
 
 // ---------------------------------------------------------------------------
-// intra: one workgroup (8 waves) per (chunk, head).  The chunk's tokens are
-// first brought in (conv + SiLU, L2 norms, gates); then the Gram matrices A,
-// P, the triangular inverse T = (I + A)^-1 and [W | U~] = T [diag(beta) K^ e^G
-// | diag(beta) V] are formed; every contraction runs on MFMA in bf16x3.
+// intra: persistent workgroups of 16 waves, one per CU; workgroup w works
+// through every (CUs / H)-th chunk of head w mod H.  Per chunk: the tokens are
+// brought in (conv + SiLU, L2 norms, gates; the inputs were requested while
+// the previous chunk was computed), then the Gram matrices A and P, the
+// diagonal 16 x 16 blocks of T = (I + A)^-1 and [W | U~] = T [diag(beta) K^ e^G
+// | diag(beta) V]; every contraction runs on MFMA in bf16x3.
 //
-// Gram tiles are 16 x 16 token blocks.  For a t-block starting at token r,
-// e^(G_t - G_s) = e^(G_t - G_r) e^(G_r - G_s): the first factor is <= 1 for
-// t >= r and the second is <= 1 for s < r, so an off-diagonal tile is a plain
-// product of two scaled operands.  In a diagonal tile s >= r makes the second
-// factor >= 1; it is used only when the block's decay span is at most 2^60
-// (checked per block), otherwise the tile is summed directly with one
-// exponential per term.
+// Gram tiles are 16 x 16 token blocks.  For t in block bt (first row r) and s
+// in block bs (last row e), e^(G_t - G_s) = e^(G_t - G_r) M e^(G_e - G_s) with
+// M = e^(G_r - G_e) per channel: each row is scaled once to its own block's
+// start and end, and a tile multiplies one of them by its pair's factor.  Off
+// the diagonal every factor is <= 1.  On the diagonal M >= 1; it is used only
+// when the block's decay span is at most 2^60 (checked per block), otherwise
+// the tile is summed directly with one exponential per term.
 //
-// LDS holds q^, k^ (rows, zero past the chunk's end), the decay prefix sums,
-// A and T: about 143 KiB at d_k = 128, one workgroup per CU.  v is convolved
-// from its raw inputs where [W | U~] needs it (no workspace round trip).  The
-// factors for the scan (P, Q^ e^G, Kd^T, -W as bf16 hi/lo; U~ in fp32) are
-// written in the order its loads read.
+// [W | U~] is the solution X of (I + A) X = R, found block by block: X_b =
+// T_bb (R_b - sum_{m < b} A_bm X_m), each wave for its own 16 columns.
+//
+// LDS holds the token rows (q^, k^, G, then their scaled forms), -A and the
+// diagonal blocks of T split into bf16 pairs, the block factors and the
+// head's constants: about 152 KiB at d_k = 128, one workgroup per CU.  v is
+// convolved from its raw inputs where [W | U~] needs it.  The factors for the
+// scan (P, Q^ e^G, Kd^T, -W as bf16 hi/lo; U~ in fp32) are written in the
+// order its loads read.
 // ---------------------------------------------------------------------------
 constexpr int kIntraThreads = 1024;
 constexpr int kIntraWaves = kIntraThreads / kWave;
@@ -511,7 +517,7 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
 
     // roles in step 1: waves 0-7 q^ rows and 8-15 k^ rows, 8 rows each;
     // waves 0 .. DK / 16 - 1 the decay sums of one 16-row block for 64
-    // channels each; the last wave beta.  In step 6 wave w takes column tile w.
+    // channels each; the last wave beta.  In step 5 wave w takes column tile w.
     const bool isq = wave < 8;
     const int part = wave % 8;
     const Tin *xr = static_cast<const Tin *>(isq ? p.x_q : p.x_k);
@@ -520,7 +526,7 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
     const bool gate_wave = wave < 8 && 64 * gcg < DK;   // wave-uniform
     const bool u_wave = wave >= DK / 16 && wave < NCT;   // wave-uniform
     const int vcol = 16 * wave + lr - DK;                // a U~ wave's v channel
-    // the head's constants into LDS (read by step 1 and step 6)
+    // the head's constants into LDS (read by step 1 and step 5)
     for (int e = tid; e < CH; e += kIntraThreads) {
         const float4 v = *reinterpret_cast<const float4 *>(p.conv_wt + ((size_t)h * CH + e) * 4);
         if (e < 2 * DK) L.Cw[e] = v;
@@ -752,7 +758,7 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
     }
     __syncthreads();
 
-    // the raw v inputs of step 6 (U~ columns): a lane's channel vcol for
+    // the raw v inputs of step 5 (U~ columns): a lane's channel vcol for
     // rows 16 b + 4 lk .. + 3 and the three rows before each run (rows past
     // the chunk's end repeat its last row; their beta is 0)
     //    As raw buffer loads over rows t0 - sh .. t0 + n - 1 (sh = 3, or 0 at
@@ -787,7 +793,7 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
     //    I + A) and the six zero P tiles above the diagonal, one item per wave.
     // items by wave: the diagonal pairs 0 2 5 9 on waves 0-3, the other
     // pairs on 4-9, the zero tiles on 10-15 (waves 8-15 also request the v
-    // inputs of step 6)
+    // inputs of step 5)
     {
         const int j = (int)((0xFEDCBA8764319520ull >> (4 * wave)) & 15u);
         if (j >= NPAIR) {
@@ -857,7 +863,7 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
     int c2 = 0, t02 = 0, n2 = 0;
     const Tin *win2 = win;
 
-    // 6. [W | U~] = (I + A)^-1 R with R = [diag(beta) K^ e^G | diag(beta) V],
+    // 5. [W | U~] = (I + A)^-1 R with R = [diag(beta) K^ e^G | diag(beta) V],
     //    by block forward substitution in each wave's 16 columns:
     //    X_b = T_bb (R_b - sum_{m < b} A_bm X_m).  A result tile of
     //    v_mfma_f32_16x16x16_bf16 is laid out as its B operand (lane l: rows
@@ -888,7 +894,7 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
                 }
         }
         // the next chunk's rows, gates and beta, in flight through the rest
-        // of step 6 (issued once the raw v inputs are used: the registers
+        // of step 5 (issued once the raw v inputs are used: the registers
         // are shared)
         if (more) {
             locate(gnext, c2, t02, n2, win2);
@@ -941,7 +947,7 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
         }
     }
     if (!more) break;
-    __syncthreads();   // the next chunk's step 1 rewrites what step 6 reads
+    __syncthreads();   // the next chunk's step 1 rewrites what step 5 reads
     gidx = gnext;
     c = c2;
     t0 = t02;
