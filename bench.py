@@ -429,7 +429,8 @@ def mixed_extra(torch, api, synth, prompt=4096, n_one=64):
     """A mixed prefill + decode batch in one kda_chunk_prefill call: one
     `prompt`-token sequence and `n_one` one-token (decode) rows, H=32, d=128;
     beside the prompt alone and the one-token rows alone (same call), and the
-    one-token rows through kda_decode."""
+    one-token rows through kda_decode; and eight `prompt`-token sequences in
+    one call (the scan then takes 64-column blocks)."""
     dev = "cuda:0"
     H, dk, dv = 32, 128, 128
     g = synth.rng(106)
@@ -439,7 +440,7 @@ def mixed_extra(torch, api, synth, prompt=4096, n_one=64):
     stream = torch.cuda.current_stream()
     out = {}
     for name, lens in (("prompt_plus_decode_rows", [prompt] + [1] * n_one), ("prompt_only", [prompt]),
-                       ("decode_rows_only", [1] * n_one)):
+                       ("decode_rows_only", [1] * n_one), ("eight_prompts", [prompt] * 8)):
         N, total = len(lens), sum(lens)
         cache = api.Cache(torch.zeros((N, H, dk, dv), device=dev),
                           torch.zeros((N, H, 3, 2 * dk + dv), dtype=torch.bfloat16, device=dev))
@@ -454,7 +455,8 @@ def mixed_extra(torch, api, synth, prompt=4096, n_one=64):
             yd = torch.empty((N, H, dv), device=dev)
             out["decode_rows_via_kda_decode_us"] = timed(
                 torch, stream, lambda: api.kda_decode(layer, cache, sl, I, yd), 10) * 1e6
-    out["config"] = f"{prompt}-token prompt + {n_one} one-token rows, H={H}, d={dk}, bf16"
+    out["eight_prompts_tokens_per_s"] = 8 * prompt / (out["eight_prompts_us"] * 1e-6)
+    out["config"] = f"{prompt}-token prompt + {n_one} one-token rows, H={H}, d={dk}, bf16; eight {prompt}-token prompts"
     return out
 
 

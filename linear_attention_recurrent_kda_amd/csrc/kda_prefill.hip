@@ -968,14 +968,14 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
 // ---------------------------------------------------------------------------
 constexpr int kScanThreads = 512;
 
-template <int DK>
+template <int DK, int NCB>
 struct ScanOps {
     static constexpr int KS = DK / 32, TS = DK / 64;
     Split8 w[KS];          // -W rows (A operand, K = d_k), pre-split
     Split8 q[KS];          // Q^ e^G rows
     Split8 pm[2];          // P rows (K = token)
     Split8 kd[TS][2];      // Kd^T rows (K = token)
-    float ut[4];           // U~ (result layout)
+    float ut[NCB][4];      // U~ of each 16-column tile (result layout)
     float gc[TS][4];       // e^(G_C) of the state rows this lane updates
 };
 
@@ -988,8 +988,9 @@ __device__ __forceinline__ Split8 load_split8(const uint16_t *hi, const uint16_t
 
 // first half of a chunk's operands: the d_k-contraction rows (-W, Q^ e^G)
 // and the P rows
-template <int DK>
-__device__ __forceinline__ void scan_load_a(const PrefillWs &ws, size_t gh, int w4, int lr, int lk, ScanOps<DK> &o) {
+template <int DK, int NCB>
+__device__ __forceinline__ void scan_load_a(const PrefillWs &ws, size_t gh, int w4, int lr, int lk,
+                                            ScanOps<DK, NCB> &o) {
     constexpr int KS = DK / 32;
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
@@ -1004,9 +1005,9 @@ __device__ __forceinline__ void scan_load_a(const PrefillWs &ws, size_t gh, int 
 }
 
 // second half: Kd^T, U~ and e^(G_C)
-template <int DK, int DV>
+template <int DK, int DV, int NCB>
 __device__ __forceinline__ void scan_load_b(const PrefillWs &ws, size_t gh, int w4, int lr, int lk, int j0,
-                                            ScanOps<DK> &o) {
+                                            ScanOps<DK, NCB> &o) {
     constexpr int TS = DK / 64;
 #pragma unroll
     for (int m = 0; m < TS; ++m) {
@@ -1018,12 +1019,15 @@ __device__ __forceinline__ void scan_load_b(const PrefillWs &ws, size_t gh, int 
         for (int r = 0; r < 4; ++r) o.gc[m][r] = ws.gC[gh * DK + 16 * (TS * w4 + m) + 4 * lk + r];
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) o.ut[r] = ws.Ut[gh * kChunk * DV + (16 * w4 + 4 * lk + r) * DV + j0 + lr];
+    for (int ct = 0; ct < NCB; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            o.ut[ct][r] = ws.Ut[gh * kChunk * DV + (16 * w4 + 4 * lk + r) * DV + j0 + 16 * ct + lr];
 }
 
-template <int DK, int DV, typename Tin>
+template <int DK, int DV, typename Tin, int CB>
 __global__ __launch_bounds__(kScanThreads) void kda_prefill_scan_kernel(PrefillParams p, PrefillWs ws) {
-    constexpr int CB = kColBlock, CH = 2 * DK + DV, KS = DK / 32, TS = DK / 64;
+    constexpr int CH = 2 * DK + DV, KS = DK / 32, TS = DK / 64, NCB = CB / 16;
     static_assert(CH <= kScanThreads, "one thread per conv channel");
     // S in fp32 (two buffers) and, for the MFMA B operands, S and U split into
     // bf16 hi / lo and transposed (a lane's 8 consecutive rows are one 16-byte
@@ -1122,13 +1126,13 @@ __global__ __launch_bounds__(kScanThreads) void kda_prefill_scan_kernel(PrefillP
     auto sum3 = [](const Acc3 &a, int r) { return a.hh[r] + (a.hl[r] + a.lh[r]); };
 
     const int seq_t0 = p.cu_seqlens[s], seq_t1 = p.cu_seqlens[s + 1];
-    ScanOps<DK> ops;
+    ScanOps<DK, NCB> ops;
     if (team == 0 && nch > 0) {
-        scan_load_a<DK>(ws, (size_t)g0 * H + h, w4, lr, lk, ops);
-        scan_load_b<DK, DV>(ws, (size_t)g0 * H + h, w4, lr, lk, j0, ops);
+        scan_load_a<DK, NCB>(ws, (size_t)g0 * H + h, w4, lr, lk, ops);
+        scan_load_b<DK, DV, NCB>(ws, (size_t)g0 * H + h, w4, lr, lk, j0, ops);
     }
     __syncthreads();
-    Acc3 ao;
+    Acc3 ao[NCB];
     for (int c = 0; c < nch; ++c) {
         const int cur = c & 1;
         const bool mine = cur == team;            // wave-uniform
@@ -1136,68 +1140,76 @@ __global__ __launch_bounds__(kScanThreads) void kda_prefill_scan_kernel(PrefillP
         // segment 1: U = U~ - W S and O = Q^e^G S  |  the other team loads
         if (mine) {
             __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this chunk's operands have landed
-            Split8 sb[KS];
 #pragma unroll
-            for (int k = 0; k < KS; ++k) {
-                sb[k].hi = *reinterpret_cast<const bf16x8 *>(&Sh[cur][lr][32 * k + 8 * lk]);
-                sb[k].lo = *reinterpret_cast<const bf16x8 *>(&Sl[cur][lr][32 * k + 8 * lk]);
-            }
-            Acc3 au;
-            zero3(au);
-            zero3(ao);
+            for (int ct = 0; ct < NCB; ++ct) {
+                const int cl = 16 * ct + lr;   // this lane's state column in the block
+                Split8 sb[KS];
 #pragma unroll
-            for (int k = 0; k < KS; ++k) {
-                mma3s(ops.w[k], sb[k], au);
-                mma3s(ops.q[k], sb[k], ao);
-            }
+                for (int k = 0; k < KS; ++k) {
+                    sb[k].hi = *reinterpret_cast<const bf16x8 *>(&Sh[cur][cl][32 * k + 8 * lk]);
+                    sb[k].lo = *reinterpret_cast<const bf16x8 *>(&Sl[cur][cl][32 * k + 8 * lk]);
+                }
+                Acc3 au;
+                zero3(au);
+                zero3(ao[ct]);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float u = ops.ut[r] + sum3(au, r);
-                const __bf16 hb = (__bf16)u;
-                Uh[lr][16 * w4 + 4 * lk + r] = hb;
-                Ul[lr][16 * w4 + 4 * lk + r] = (__bf16)(u - (float)hb);
+                for (int k = 0; k < KS; ++k) {
+                    mma3s(ops.w[k], sb[k], au);
+                    mma3s(ops.q[k], sb[k], ao[ct]);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float u = ops.ut[ct][r] + sum3(au, r);
+                    const __bf16 hb = (__bf16)u;
+                    Uh[cl][16 * w4 + 4 * lk + r] = hb;
+                    Ul[cl][16 * w4 + 4 * lk + r] = (__bf16)(u - (float)hb);
+                }
             }
         } else if (c + 1 < nch) {
-            scan_load_a<DK>(ws, gnext, w4, lr, lk, ops);
+            scan_load_a<DK, NCB>(ws, gnext, w4, lr, lk, ops);
         }
         __syncthreads();
         // segment 2: O += P U, S' = diag(e^G_C) S + Kd^T U  |  the other team loads
         if (mine) {
             const int t0 = seq_t0 + c * kChunk;
             const int n = min(kChunk, seq_t1 - t0);
-            Split8 ub[2];
 #pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                ub[k].hi = *reinterpret_cast<const bf16x8 *>(&Uh[lr][32 * k + 8 * lk]);
-                ub[k].lo = *reinterpret_cast<const bf16x8 *>(&Ul[lr][32 * k + 8 * lk]);
-            }
-            // P rows beyond the chunk and above the diagonal are 0
+            for (int ct = 0; ct < NCB; ++ct) {
+                const int cl = 16 * ct + lr;
+                Split8 ub[2];
 #pragma unroll
-            for (int k = 0; k < 2; ++k)
-                if (w4 >= 2 || k == 0) mma3s(ops.pm[k], ub[k], ao);
+                for (int k = 0; k < 2; ++k) {
+                    ub[k].hi = *reinterpret_cast<const bf16x8 *>(&Uh[cl][32 * k + 8 * lk]);
+                    ub[k].lo = *reinterpret_cast<const bf16x8 *>(&Ul[cl][32 * k + 8 * lk]);
+                }
+                // P rows beyond the chunk and above the diagonal are 0
 #pragma unroll
-            for (int m = 0; m < TS; ++m) {
-                Acc3 as;
-                zero3(as);
+                for (int k = 0; k < 2; ++k)
+                    if (w4 >= 2 || k == 0) mma3s(ops.pm[k], ub[k], ao[ct]);
 #pragma unroll
-                for (int k = 0; k < 2; ++k) mma3s(ops.kd[m][k], ub[k], as);
+                for (int m = 0; m < TS; ++m) {
+                    Acc3 as;
+                    zero3(as);
+#pragma unroll
+                    for (int k = 0; k < 2; ++k) mma3s(ops.kd[m][k], ub[k], as);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int row = 16 * (TS * w4 + m) + 4 * lk + r;
+                        const float x = ops.gc[m][r] * S[cur][row][cl] + sum3(as, r);
+                        const __bf16 hb = (__bf16)x;
+                        S[cur ^ 1][row][cl] = x;
+                        Sh[cur ^ 1][cl][row] = hb;
+                        Sl[cur ^ 1][cl][row] = (__bf16)(x - (float)hb);
+                    }
+                }
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int row = 16 * (TS * w4 + m) + 4 * lk + r;
-                    const float x = ops.gc[m][r] * S[cur][row][lr] + sum3(as, r);
-                    const __bf16 hb = (__bf16)x;
-                    S[cur ^ 1][row][lr] = x;
-                    Sh[cur ^ 1][lr][row] = hb;
-                    Sl[cur ^ 1][lr][row] = (__bf16)(x - (float)hb);
+                    const int t = 16 * w4 + 4 * lk + r;
+                    if (t < n) p.y[((size_t)(t0 + t) * H + h) * DV + j0 + cl] = sum3(ao[ct], r);
                 }
             }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 16 * w4 + 4 * lk + r;
-                if (t < n) p.y[((size_t)(t0 + t) * H + h) * DV + j0 + lr] = sum3(ao, r);
-            }
         } else if (c + 1 < nch) {
-            scan_load_b<DK, DV>(ws, gnext, w4, lr, lk, j0, ops);
+            scan_load_b<DK, DV, NCB>(ws, gnext, w4, lr, lk, j0, ops);
         }
         __syncthreads();
         // interval checkpoint: the state after this chunk is in S[(c + 1) & 1],
@@ -1325,6 +1337,10 @@ static kda_status launch_prefill_typed(const PrefillParams &p, hipStream_t strea
     ws.gC = reinterpret_cast<float *>(base + l.gC);
     ws.G_max = p.total_T / kChunk + p.N_seq;
 
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        return KDA_ERR_LAUNCH;
     hipLaunchKernelGGL(kda_prefill_meta_kernel, dim3(1), dim3(64), 0, stream, p, ws);
     if (p.total_T > 0) {
         // one-token sequences (decode rows of a mixed batch) take the decode
@@ -1346,17 +1362,23 @@ static kda_status launch_prefill_typed(const PrefillParams &p, hipStream_t strea
         if (st != KDA_OK) return st;
         // one workgroup per compute unit (the LDS of one), each working
         // through the chunks of one head
-        int dev = 0, cus = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-            return KDA_ERR_LAUNCH;
         const int wph = std::max(1, std::min(ws.G_max, cus / p.H));
         hipLaunchKernelGGL((kda_prefill_intra_kernel<DK, DV, Tin>), dim3((unsigned)((size_t)p.H * wph)),
                            dim3(kIntraThreads), 0, stream, p, ws);
     }
-    hipLaunchKernelGGL((kda_prefill_scan_kernel<DK, DV, Tin>),
-                       dim3((unsigned)((size_t)p.H * (DV / kColBlock) * p.N_seq)), dim3(kScanThreads), 0, stream, p,
-                       ws);
+    // the scan's column blocks: 64 columns per workgroup load the chunk's
+    // shared operands once for four times the columns (about 2.4x the
+    // columns per CU and second), when the batch has the prompts and heads to
+    // fill the GPU with them (by the host's view: enough rows, and on average
+    // four chunks per row, so that one-token rows are not counted as
+    // prompts); else 16 (a single long prompt: all CUs busy)
+    if ((size_t)p.H * (DV / 64) * p.N_seq >= (size_t)cus && (size_t)p.total_T >= (size_t)4 * kChunk * p.N_seq)
+        hipLaunchKernelGGL((kda_prefill_scan_kernel<DK, DV, Tin, 64>),
+                           dim3((unsigned)((size_t)p.H * (DV / 64) * p.N_seq)), dim3(kScanThreads), 0, stream, p, ws);
+    else
+        hipLaunchKernelGGL((kda_prefill_scan_kernel<DK, DV, Tin, kColBlock>),
+                           dim3((unsigned)((size_t)p.H * (DV / kColBlock) * p.N_seq)), dim3(kScanThreads), 0, stream,
+                           p, ws);
     if (p.total_T > 0) {
         const size_t rows = (size_t)p.total_T * p.H;
         hipLaunchKernelGGL((kda_prefill_norm_kernel<DV, Tin>), dim3((unsigned)((rows + kNormRows - 1) / kNormRows)),

@@ -170,6 +170,53 @@ def test_many_sequences_mixed_lengths():
     assert worst <= TOL
 
 
+def test_many_sequences_wide_scan_blocks():
+    """40 packed sequences x 8 heads at d = 128: enough workgroups that the
+    scan takes 64-column blocks.  Every output, final state and window against
+    the oracle, and the outputs bitwise equal to the same sequences run alone
+    (16-column blocks)."""
+    g = synth.rng(976)
+    H, dk, dv = 8, 128, 128
+    params = synth.layer_params(g, H, dk, dv)
+    dl, ol = layer_pair(params)
+    lens = [int(x) for x in g.integers(200, 601, size=40)]   # ~16K tokens: four chunks per row on average
+    lens[:5] = [0, 1, 64, 200, 129]
+    n_slots = 44
+    slots = [int(x) for x in g.permutation(n_slots)[:40]]
+    slots[11] = -1
+    total = sum(lens)
+    inp = synth.token_inputs(g, (total,), H, dk, dv, "bf16")
+    cache = new_cache(n_slots, H, dk, dv, "bf16", fill_seed=5)
+    s_before = host(cache.state)
+    w_before = host(cache.conv_state)
+    y, cu = run_prefill(dl, cache, slots, lens, inp, "bf16")
+    assert cache.err_flag.item() == 0
+    worst = 0.0
+    for i, (sl, ln) in enumerate(zip(slots, lens)):
+        a, b = cu[i], cu[i + 1]
+        if sl < 0:
+            assert np.all(y[a:b] == 0.0)
+            continue
+        o = oracle_seq(ol, s_before[sl], w_before[sl], inp, a, b)
+        if ln:
+            errs = [parity_error(y[t], o["y"][0][t - a]) for t in range(a, b)]
+            worst = max(worst, max(errs))
+        assert state_rel_err(host(cache.state[sl:sl + 1]), o["state"]) < 1e-4
+        assert np.array_equal(host(cache.conv_state[sl:sl + 1]), o["window"])
+    print(f"  prefill parity over {len(lens)} sequences x {H} heads: worst max|d|/RMS = {worst:.3e}", flush=True)
+    assert worst <= TOL
+    # sequence 3 (200 tokens) alone: one sequence, 16-column scan blocks
+    i = 3
+    a, b = cu[i], cu[i + 1]
+    one = {k: v[a:b] for k, v in inp.items()}
+    c1 = new_cache(n_slots, H, dk, dv, "bf16")
+    c1.state.copy_(torch.from_numpy(s_before).to(DEV))
+    c1.conv_state.copy_(torch.from_numpy(w_before).to(DEV).to(torch.bfloat16))
+    y1, _ = run_prefill(dl, c1, [slots[i]], [lens[i]], one, "bf16")
+    assert np.array_equal(y1, y[a:b])
+    assert np.array_equal(host(c1.state[slots[i]]), host(cache.state[slots[i]]))
+
+
 def test_prefill_then_decode_continues_the_sequence():
     g = synth.rng(980)
     H, dk, dv, T, D = 4, 128, 128, 100, 20
