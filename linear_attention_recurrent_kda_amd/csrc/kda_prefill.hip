@@ -1038,22 +1038,25 @@ __global__ __launch_bounds__(kScanThreads) void kda_prefill_scan_kernel(PrefillP
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int team = wave / 4, w4 = wave % 4;
     const int lr = lane % 16, lk = lane / 16;
-    // one-dimensional grid: workgroup x = h + H * column block + NX * k for
-    // the k-th chunk-path sequence, so all real work dispatches ahead of the
-    // workgroups that only exit, and the column blocks of a head share an
-    // XCD (workgroups go to XCDs round-robin; H a multiple of 8)
+    // persistent: work item x = h + H * column block + NX * k for the k-th
+    // chunk-path sequence (counted on the device), workgroup w taking items
+    // w, w + grid, ...  With the grid a multiple of 8 the column blocks of a
+    // head share an XCD (workgroups go to XCDs round-robin; H a multiple of
+    // 8); a batch of one-token rows costs one exit per workgroup, not one per
+    // (sequence, head, column block).
     const int H = p.H, NX = H * (DV / CB);
-    const int xb = (int)(blockIdx.x % (unsigned)NX), k = (int)(blockIdx.x / (unsigned)NX);
-    const int h = xb % H, zb = xb / H, j0 = zb * CB;
     if (ws.meta[0] != 1) return;
-    if (k >= ws.meta[p.N_seq + 2]) return;
+    const int nitems = NX * ws.meta[p.N_seq + 2];
+    for (int item = (int)blockIdx.x; item < nitems; item += (int)gridDim.x) {
+    const int xb = item % NX, k = item / NX;
+    const int h = xb % H, zb = xb / H, j0 = zb * CB;
     const int s = ws.meta[p.N_seq + 3 + k];
     const int slot = p.slot_idx[s];
-    if (!slot_ok(slot, p.n_slots)) return;
+    if (!slot_ok(slot, p.n_slots)) continue;
     const int32_t *cs = ws.meta + 1;
     const int g0 = cs[s], nch = cs[s + 1] - cs[s];
     const int len = p.cu_seqlens[s + 1] - p.cu_seqlens[s];
-    if (len == 1) return;   // a one-token sequence: decode kernel (state, window, output)
+    if (len == 1) continue;   // a one-token sequence: decode kernel (state, window, output)
 
     // the window after the sequence: the last 3 raw inputs (older rows from
     // the previous window when len < 3); read everything, then write
@@ -1232,6 +1235,8 @@ __global__ __launch_bounds__(kScanThreads) void kda_prefill_scan_kernel(PrefillP
     }
     const int fin = nch & 1;
     for (int e = tid; e < DK * CB; e += kScanThreads) Sg[(e / CB) * DV + j0 + e % CB] = S[fin][e / CB][e % CB];
+    __syncthreads();   // the next item's state load rewrites S
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1374,11 +1379,12 @@ static kda_status launch_prefill_typed(const PrefillParams &p, hipStream_t strea
     // prompts); else 16 (a single long prompt: all CUs busy)
     if ((size_t)p.H * (DV / 64) * p.N_seq >= (size_t)cus && (size_t)p.total_T >= (size_t)4 * kChunk * p.N_seq)
         hipLaunchKernelGGL((kda_prefill_scan_kernel<DK, DV, Tin, 64>),
-                           dim3((unsigned)((size_t)p.H * (DV / 64) * p.N_seq)), dim3(kScanThreads), 0, stream, p, ws);
+                           dim3((unsigned)std::min((size_t)p.H * (DV / 64) * p.N_seq, (size_t)cus)),
+                           dim3(kScanThreads), 0, stream, p, ws);
     else
         hipLaunchKernelGGL((kda_prefill_scan_kernel<DK, DV, Tin, kColBlock>),
-                           dim3((unsigned)((size_t)p.H * (DV / kColBlock) * p.N_seq)), dim3(kScanThreads), 0, stream,
-                           p, ws);
+                           dim3((unsigned)std::min((size_t)p.H * (DV / kColBlock) * p.N_seq, (size_t)cus)),
+                           dim3(kScanThreads), 0, stream, p, ws);
     if (p.total_T > 0) {
         const size_t rows = (size_t)p.total_T * p.H;
         hipLaunchKernelGGL((kda_prefill_norm_kernel<DV, Tin>), dim3((unsigned)((rows + kNormRows - 1) / kNormRows)),
