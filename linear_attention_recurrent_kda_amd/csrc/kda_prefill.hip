@@ -15,13 +15,15 @@
 //
 // Kernels, in stream order:
 //   meta   one workgroup: validates cu_seqlens, chunk offsets per sequence
-//   intra  one workgroup per (chunk, head): conv + SiLU, L2 norms and gates of
-//          the chunk's tokens, prefix sums, A, P, the triangular solve for W
-//          and U~, the decayed Q and K factors
-//   scan   one workgroup per (sequence, head, 16 columns of d_v): the fp32 state
-//          carried from chunk to chunk (state columns are independent given the
-//          chunk factors), unnormalised outputs O written to y
-//   norm   RMSNorm over d_v, weight, sigmoid gate on the rows of y
+//   intra  persistent, one workgroup per CU working through the chunks of one
+//          head: conv + SiLU, L2 norms and gates of the chunk's tokens, prefix
+//          sums, A, P, the triangular solve for W and U~, the decayed Q and K
+//          factors
+//   scan   persistent, one workgroup per (sequence, head, 16 or 64 columns of
+//          d_v) at a time: the fp32 state carried from chunk to chunk (state
+//          columns are independent given the chunk factors) and the outputs:
+//          O, then RMSNorm over d_v (the column workgroups of a head exchange
+//          per-row partial sums of squares), weight and sigmoid gate
 #include <algorithm>
 
 #include "kda_device.h"
@@ -33,6 +35,9 @@ constexpr int kChunk = 64;
 constexpr int kColBlock = 16;
 constexpr int kBufferWord3 = 0x00020000;   // raw 32-bit buffer resource
 constexpr float kLog2e = 1.4426950408889634f;
+// An empty slot of the scan's row-sum exchange: a NaN bit pattern that no sum
+// of squares is stored as (a NaN sum is stored as the canonical quiet NaN).
+constexpr uint32_t kXpEmpty = 0xFFFFFFFFu;
 
 // Device pointers into the caller's workspace.  The per-chunk factors the
 // scan multiplies on MFMA are stored pre-split as bf16 pairs (hi = bf16(x),
@@ -47,6 +52,7 @@ struct PrefillWs {
     uint16_t *P_hi, *P_lo;    // [G, H] x (64 x 64)
     float *Ut;                // [G, H, 64, d_v]
     float *gC;                // [G, H, d_k]  e^(G_C)
+    uint32_t *Xp;             // [G, H, 64, d_v / 16]  sums of squares of O rows over 16 columns
     int G_max;
 };
 
@@ -61,7 +67,7 @@ __device__ __forceinline__ size_t opnd_off(int row, int k) {
 }
 
 struct WsLayout {
-    size_t meta, Wn_hi, Wn_lo, Q_hi, Q_lo, K_hi, K_lo, P_hi, P_lo, Ut, gC, total;
+    size_t meta, Wn_hi, Wn_lo, Q_hi, Q_lo, K_hi, K_lo, P_hi, P_lo, Ut, gC, Xp, total;
 };
 
 static size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
@@ -83,6 +89,7 @@ static WsLayout ws_layout(int H, int dk, int dv, int total_T, int N_seq) {
     l.P_lo = take(2 * GH * kChunk * kChunk);
     l.Ut = take(4 * GH * kChunk * dv);
     l.gC = take(4 * GH * dk);
+    l.Xp = take(4 * GH * kChunk * (dv / 16));
     l.total = off;
     return l;
 }
@@ -804,6 +811,12 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
                 *reinterpret_cast<bf16x8 *>(Ph + o) = z;
                 *reinterpret_cast<bf16x8 *>(Pl + o) = z;
             }
+            // the chunk's slots of the scan's row-sum exchange, marked empty
+            // (waves 10 and 11; the scan runs after this kernel)
+            const int e4 = (wave - NPAIR) * kWave + lane;
+            if (e4 < kChunk * (DV / 16) / 4)
+                reinterpret_cast<uint4 *>(ws.Xp + gh * kChunk * (DV / 16))[e4] =
+                    make_uint4(kXpEmpty, kXpEmpty, kXpEmpty, kXpEmpty);
         } else {
         const int bt = j < 1 ? 0 : j < 3 ? 1 : j < 6 ? 2 : 3, bs = j - bt * (bt + 1) / 2;
         if (!(bt == bs && !L.safe[bt])) {   // else summed directly above
@@ -957,16 +970,69 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
 }
 
 // ---------------------------------------------------------------------------
-// scan: one workgroup per (sequence, head, 16 state columns), two teams of 4
-// waves.  Team 0 computes the even chunks and team 1 the odd ones; while one
-// team computes a chunk, the other loads the operands of the next one into
-// its registers, so the operand traffic (bound by the L1's outstanding-miss
-// capacity) runs under the other team's MFMA work.  Inside a team, wave w
-// owns rows 16w..16w+15 of the chunk and state row tiles TS*w .. TS*w+TS-1;
-// all products run on MFMA in bf16x3 with fp32 accumulation.  The state is
-// handed from team to team through LDS (two buffers).
+// scan: persistent workgroups, each taking one (sequence, head, CB state
+// columns) item at a time, two teams of 4 waves.  Team 0 computes the even
+// chunks and team 1 the odd ones; while one team computes a chunk, the other
+// loads the operands of the next one into its registers, so the operand
+// traffic (bound by the L1's outstanding-miss capacity) runs under the other
+// team's MFMA work.  Inside a team, wave w owns rows 16w..16w+15 of the chunk
+// and state row tiles TS*w .. TS*w+TS-1; all products run on MFMA in bf16x3
+// with fp32 accumulation.  The state is handed from team to team through LDS
+// (two buffers).
+//
+// Outputs with 16-column blocks: the RMSNorm of a row of O needs all d_v
+// columns, which the d_v / 16 workgroups of a (sequence, head) hold between
+// them.  Each wave keeps its 16 rows of O of the team's last two chunks in
+// LDS (4 consecutive columns per lane) and publishes, for every row, the sum
+// of squares of its 16 columns into the chunk's exchange slots (marked empty
+// by the intra kernel) with relaxed device-scope atomic stores.  Two team
+// chunks later it reads the row's d_v / 16 slots of that chunk with relaxed
+// device-scope atomic loads until none is empty: each slot is written once
+// per call, so a value that is not the empty mark is the final one, and no
+// fence is needed.  The row sum adds the slots as a pairwise tree (the same
+// bits in every workgroup); then the rows are scaled, weighted, gated and
+// stored.  The workgroups of one (sequence, head) must run at the same time:
+// items are ordered so that its d_v / CB items are 8 apart inside an aligned
+// run of 8 d_v / CB items (all on one XCD, as workgroups go to XCDs
+// round-robin), and the grid is a multiple of that run and at most one
+// workgroup per CU.  The wait is bounded: if it ever runs out, the workgroup
+// waits no more and flags the error.  With 64-column blocks the LDS is full:
+// the scan writes O and the norm kernel below normalises it with the same
+// arithmetic (both give the same bits).
 // ---------------------------------------------------------------------------
 constexpr int kScanThreads = 512;
+template <typename Tin> struct Vec4 {
+    typedef Tin T __attribute__((ext_vector_type(4)));
+};
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// RMSNorm arithmetic shared by the scan's in-place normalisation (16-column
+// blocks) and the norm kernel (64-column blocks), so both give the same bits:
+// a lane holds 4 consecutive columns of a row and a quad of lanes one
+// 16-column tile.  The tile's sum of squares: the lane's columns in order,
+// then the quad's lanes as (0 + 1) + (2 + 3).  The row's sum adds the tiles
+// as a pairwise tree, ((0 + 1) + (2 + 3)) + ((4 + 5) + (6 + 7)).
+__device__ __forceinline__ float tile_sumsq(v4f y) {
+    float s = y.x * y.x;
+    s = fmaf(y.y, y.y, s);
+    s = fmaf(y.z, y.z, s);
+    s = fmaf(y.w, y.w, s);
+    s = dpp_add<0xB1, 0xF>(s);      // quad_perm [1,0,3,2]
+    return dpp_add<0x4E, 0xF>(s);   // quad_perm [2,3,0,1]
+}
+// y / sqrt(mean(y^2) + eps) * (w * sigmoid(z)) for the lane's 4 columns:
+// the gate factors g = w * sigmoid(z), then the row's scale
+template <typename Tin>
+__device__ __forceinline__ v4f gate4(v4f w, typename Vec4<Tin>::T z) {
+    return v4f{w.x * sigmoid(to_f32(z[0])), w.y * sigmoid(to_f32(z[1])), w.z * sigmoid(to_f32(z[2])),
+               w.w * sigmoid(to_f32(z[3]))};
+}
+template <int DV>
+__device__ __forceinline__ v4f rms_apply(v4f y, float ss, float eps, v4f g) {
+    const float rn = 1.0f / sqrtf(ss * (1.0f / DV) + eps);
+    return v4f{y.x * rn * g.x, y.y * rn * g.y, y.z * rn * g.z, y.w * rn * g.w};
+}
+constexpr int kXpSpin = 1 << 20;   // polls of the exchange slots before giving up (about a second)
 
 template <int DK, int NCB>
 struct ScanOps {
@@ -1027,7 +1093,10 @@ __device__ __forceinline__ void scan_load_b(const PrefillWs &ws, size_t gh, int 
 
 template <int DK, int DV, typename Tin, int CB>
 __global__ __launch_bounds__(kScanThreads) void kda_prefill_scan_kernel(PrefillParams p, PrefillWs ws) {
-    constexpr int CH = 2 * DK + DV, KS = DK / 32, TS = DK / 64, NCB = CB / 16;
+    constexpr int CH = 2 * DK + DV, KS = DK / 32, TS = DK / 64, NCB = CB / 16, NZ = DV / CB, NT = DV / 16;
+    // 16-column blocks normalise their outputs in place (row sums exchanged);
+    // 64-column blocks write O and the norm kernel follows (no LDS to spare)
+    constexpr bool FUSE = CB == kColBlock;
     static_assert(CH <= kScanThreads, "one thread per conv channel");
     // S in fp32 (two buffers) and, for the MFMA B operands, S and U split into
     // bf16 hi / lo and transposed (a lane's 8 consecutive rows are one 16-byte
@@ -1035,21 +1104,32 @@ __global__ __launch_bounds__(kScanThreads) void kda_prefill_scan_kernel(PrefillP
     __shared__ __align__(16) float S[2][DK][CB];
     __shared__ __align__(16) __bf16 Sh[2][CB][DK + 8], Sl[2][CB][DK + 8];
     __shared__ __align__(16) __bf16 Uh[CB][kChunk + 8], Ul[CB][kChunk + 8];
+    // per wave: its 16 rows of O of the team's last two chunks (by the team's
+    // chunk count mod 2), written in the MFMA result layout, read as 4
+    // consecutive columns per lane
+    __shared__ __align__(16) float Yst[FUSE ? kScanThreads / kWave : 1][2][16][CB + 4];
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int team = wave / 4, w4 = wave % 4;
     const int lr = lane % 16, lk = lane / 16;
-    // persistent: work item x = h + H * column block + NX * k for the k-th
-    // chunk-path sequence (counted on the device), workgroup w taking items
-    // w, w + grid, ...  With the grid a multiple of 8 the column blocks of a
-    // head share an XCD (workgroups go to XCDs round-robin; H a multiple of
-    // 8); a batch of one-token rows costs one exit per workgroup, not one per
-    // (sequence, head, column block).
-    const int H = p.H, NX = H * (DV / CB);
-    if (ws.meta[0] != 1) return;
-    const int nitems = NX * ws.meta[p.N_seq + 2];
+    const int H = p.H, H8 = (H + 7) / 8;
+    bool xp_live = true;   // false once a wait for the exchange ran out
+    if (ws.meta[0] != 1) {
+        // tables that failed validation: every output row is zero
+        v4f *y4 = reinterpret_cast<v4f *>(p.y);
+        const size_t n4 = (size_t)p.total_T * H * DV / 4;
+        for (size_t e = (size_t)blockIdx.x * kScanThreads + tid; e < n4; e += (size_t)gridDim.x * kScanThreads)
+            y4[e] = v4f{0.f, 0.f, 0.f, 0.f};
+        return;
+    }
+    // persistent: item hl + 8 (zb + NZ (h8 + H8 k)) is head 8 h8 + hl, column
+    // block zb of the k-th chunk-path sequence (counted on the device);
+    // workgroup w takes items w, w + grid, ...  (a batch of one-token rows
+    // costs one exit per workgroup, not one per item)
+    const int nitems = 8 * NZ * H8 * ws.meta[p.N_seq + 2];
     for (int item = (int)blockIdx.x; item < nitems; item += (int)gridDim.x) {
-    const int xb = item % NX, k = item / NX;
-    const int h = xb % H, zb = xb / H, j0 = zb * CB;
+    const int hl = item % 8, zb = (item / 8) % NZ, rest = item / (8 * NZ);
+    const int h = 8 * (rest % H8) + hl, k = rest / H8, j0 = zb * CB;
+    if (h >= H) continue;   // heads padded to a multiple of 8
     const int s = ws.meta[p.N_seq + 3 + k];
     const int slot = p.slot_idx[s];
     if (!slot_ok(slot, p.n_slots)) continue;
@@ -1129,6 +1209,78 @@ __global__ __launch_bounds__(kScanThreads) void kda_prefill_scan_kernel(PrefillP
     auto sum3 = [](const Acc3 &a, int r) { return a.hh[r] + (a.hl[r] + a.lh[r]); };
 
     const int seq_t0 = p.cu_seqlens[s], seq_t1 = p.cu_seqlens[s + 1];
+    // in-place RMSNorm (16-column blocks): the lane's row of the wave's 16
+    // (rho) and columns 4 qd .. 4 qd + 3 of each 16-column tile
+    const int rho = lane / 4, qd = lane % 4;
+    using ZT = typename Vec4<Tin>::T;
+    v4f nw[NCB];   // the norm weights of those columns
+    if constexpr (FUSE) {
+#pragma unroll
+        for (int ct = 0; ct < NCB; ++ct) nw[ct] = *reinterpret_cast<const v4f *>(p.norm_w + h * DV + j0 + 16 * ct + 4 * qd);
+    }
+    // the team's two previous chunks, older first (-1: none); their rows of O
+    // wait in the wave's scratch
+    int pc1 = -1, pc2 = -1;
+    // The older one's RMSNorm in two steps: fin_issue requests the gate inputs and the
+    // row-sum slots (the quad of the row reads PL slots per lane), fin_done
+    // waits until no slot is empty and stores the results.  The chunk's own
+    // products run in between.
+    constexpr int PL = NT / 4;
+    struct Fin {
+        ZT z[NCB];
+        uint64_t sl;
+        const uint32_t *src;
+    };
+    auto fin_src = [&](int cc) {
+        return ws.Xp + (((size_t)(g0 + cc) * H + h) * kChunk + 16 * w4 + rho) * NT + PL * qd;
+    };
+    auto poll = [&](const uint32_t *src) -> uint64_t {
+        if constexpr (PL == 2)
+            return __hip_atomic_load(reinterpret_cast<const uint64_t *>(src), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else   // (the second word a stand-in that is never empty)
+            return (uint64_t)__hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) |
+                   ((uint64_t)0x7FC00000u << 32);
+    };
+    auto fin_issue = [&](int cc, Fin &f) {
+        const int t0c = seq_t0 + cc * kChunk, nc = min(kChunk, seq_t1 - t0c);
+        const size_t row = (size_t)(t0c + min(16 * w4 + rho, nc - 1)) * H + h;
+#pragma unroll
+        for (int ct = 0; ct < NCB; ++ct)
+            f.z[ct] = *reinterpret_cast<const ZT *>(static_cast<const Tin *>(p.z) + row * DV + j0 + 16 * ct + 4 * qd);
+        f.src = fin_src(cc);
+        f.sl = poll(f.src);
+    };
+    auto fin_done = [&](int cc, Fin &f) {
+        const int t0c = seq_t0 + cc * kChunk, nc = min(kChunk, seq_t1 - t0c);
+        // the gate factors and the lane's rows of O do not wait for the sums
+        v4f gz[NCB], yo[NCB];
+#pragma unroll
+        for (int ct = 0; ct < NCB; ++ct) {
+            gz[ct] = gate4<Tin>(nw[ct], f.z[ct]);
+            yo[ct] = *reinterpret_cast<const v4f *>(&Yst[wave][(cc / 2) & 1][rho][16 * ct + 4 * qd]);
+        }
+        auto full = [](uint64_t v) { return (uint32_t)v != kXpEmpty && (uint32_t)(v >> 32) != kXpEmpty; };
+        // (a wave vote: one path for all lanes; a wait that runs out stops all
+        // later ones of the workgroup, and the error is flagged at its end)
+        for (int tries = 0; xp_live && !__all(full(f.sl)); ++tries) {
+            xp_live = tries < kXpSpin;
+            __builtin_amdgcn_s_sleep(8);
+            f.sl = poll(f.src);
+        }
+        // the row's sum over its tiles, in the tree order, on its quad
+        float a = __uint_as_float((uint32_t)f.sl);
+        if (PL == 2) a += __uint_as_float((uint32_t)(f.sl >> 32));
+        a = dpp_add<0xB1, 0xF>(a);   // quad_perm [1,0,3,2]
+        a = dpp_add<0x4E, 0xF>(a);   // quad_perm [2,3,0,1]
+        const int t = 16 * w4 + rho;
+        if (t < nc) {
+#pragma unroll
+            for (int ct = 0; ct < NCB; ++ct)
+                __builtin_nontemporal_store(rms_apply<DV>(yo[ct], a, p.rms_eps, gz[ct]),
+                                            reinterpret_cast<v4f *>(p.y + ((size_t)(t0c + t) * H + h) * DV + j0 +
+                                                                    16 * ct + 4 * qd));
+        }
+    };
     ScanOps<DK, NCB> ops;
     if (team == 0 && nch > 0) {
         scan_load_a<DK, NCB>(ws, (size_t)g0 * H + h, w4, lr, lk, ops);
@@ -1174,8 +1326,19 @@ __global__ __launch_bounds__(kScanThreads) void kda_prefill_scan_kernel(PrefillP
         __syncthreads();
         // segment 2: O += P U, S' = diag(e^G_C) S + Kd^T U  |  the other team loads
         if (mine) {
+            const size_t ghc = (size_t)(g0 + c) * H + h;
             const int t0 = seq_t0 + c * kChunk;
             const int n = min(kChunk, seq_t1 - t0);
+            // the team's chunk before last: its inputs requested now, its rows
+            // finished after this chunk's products (their sums are in by then,
+            // as a rule).  The operands landed before segment 1; saying so
+            // here keeps the compiler from waiting for these new loads before
+            // the products (it cannot tell that the loads of the other team's
+            // branch are not pending on this one).
+            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+            Fin f;
+            if (FUSE && pc1 >= 0) fin_issue(pc1, f);
+            float yv[NCB][4];
 #pragma unroll
             for (int ct = 0; ct < NCB; ++ct) {
                 const int cl = 16 * ct + lr;
@@ -1206,10 +1369,44 @@ __global__ __launch_bounds__(kScanThreads) void kda_prefill_scan_kernel(PrefillP
                     }
                 }
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = 16 * w4 + 4 * lk + r;
-                    if (t < n) p.y[((size_t)(t0 + t) * H + h) * DV + j0 + cl] = sum3(ao[ct], r);
+                for (int r = 0; r < 4; ++r) yv[ct][r] = sum3(ao[ct], r);
+            }
+            if constexpr (FUSE) {
+                // (the previous chunk finishes before this one's stores: with
+                // no store issued after its loads, the wait for them is exact)
+                if (pc1 >= 0) fin_done(pc1, f);
+                pc1 = pc2;   // this chunk's rows wait for the team's chunk after next
+                pc2 = c;
+                // into the wave's scratch (the slot just finished: its reads
+                // by other lanes come first); each quad's tile sum of squares
+                // into the exchange
+                const int sb = (c / 2) & 1;
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+                for (int ct = 0; ct < NCB; ++ct)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) Yst[wave][sb][4 * lk + r][16 * ct + lr] = yv[ct][r];
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+                for (int ct = 0; ct < NCB; ++ct) {
+                    const float ps = tile_sumsq(*reinterpret_cast<const v4f *>(&Yst[wave][sb][rho][16 * ct + 4 * qd]));
+                    const uint32_t bits = ps != ps ? 0x7FC00000u : __float_as_uint(ps);
+                    if (qd == 0)
+                        __hip_atomic_store(ws.Xp + (ghc * kChunk + 16 * w4 + rho) * NT + zb * NCB + ct, bits,
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
+            } else {
+#pragma unroll
+                for (int ct = 0; ct < NCB; ++ct)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int t = 16 * w4 + 4 * lk + r;
+                        if (t < n) p.y[((size_t)(t0 + t) * H + h) * DV + j0 + 16 * ct + lr] = yv[ct][r];
+                    }
             }
         } else if (c + 1 < nch) {
             scan_load_b<DK, DV, NCB>(ws, gnext, w4, lr, lk, j0, ops);
@@ -1233,45 +1430,52 @@ __global__ __launch_bounds__(kScanThreads) void kda_prefill_scan_kernel(PrefillP
             }
         }
     }
+    if (FUSE) {   // each team's last two chunks
+        for (int i = 0; i < 2; ++i) {
+            const int cc = i ? pc2 : pc1;
+            if (cc >= 0) {
+                Fin f;
+                fin_issue(cc, f);
+                fin_done(cc, f);
+            }
+        }
+    }
     const int fin = nch & 1;
     for (int e = tid; e < DK * CB; e += kScanThreads) Sg[(e / CB) * DV + j0 + e % CB] = S[fin][e / CB][e % CB];
     __syncthreads();   // the next item's state load rewrites S
     }
+    if (!xp_live && lane == 0) flag_error(p.err_flag);
+    // rows of sequences that no kernel computes (padding, a bad slot) are zero
+    for (int sq = (int)(blockIdx.x * kScanThreads) + tid; sq < p.N_seq; sq += (int)(gridDim.x * kScanThreads)) {
+        const int a0 = p.cu_seqlens[sq], a1 = p.cu_seqlens[sq + 1];
+        if (a1 > a0 && !slot_ok(p.slot_idx[sq], p.n_slots)) {
+            v4f *d = reinterpret_cast<v4f *>(p.y + (size_t)a0 * H * DV);
+            for (size_t e = 0; e < (size_t)(a1 - a0) * H * DV / 4; ++e) d[e] = v4f{0.f, 0.f, 0.f, 0.f};
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
-// norm: y = O / sqrt(mean(O^2) + eps) * w * sigmoid(z) over rows r = t*H + h
-// of y (contiguous).  A lane holds 4 consecutive columns, a row spans d_v/4
-// lanes (a wave covers 2 rows at d_v = 128, 4 at d_v = 64); a workgroup
-// walks kNormRows consecutive rows.
+// norm (after the scan with 64-column blocks): y = O / sqrt(mean(O^2) + eps)
+// * w * sigmoid(z) over rows r = t*H + h of y (contiguous), with the scan's
+// in-place arithmetic (tile sums, then the tiles as a pairwise tree).  A lane
+// holds 4 consecutive columns, a row spans d_v/4 lanes (a wave covers 2 rows
+// at d_v = 128, 4 at d_v = 64); a workgroup walks kNormRows consecutive rows.
 // ---------------------------------------------------------------------------
 constexpr int kNormRows = 64;
-
-// 4 consecutive inputs (8- or 16-byte aligned) as fp32
-__device__ __forceinline__ void load4(const uint16_t *src, float *x) {
-    const uint2 v = *reinterpret_cast<const uint2 *>(src);
-    x[0] = __uint_as_float(v.x << 16);
-    x[1] = __uint_as_float(v.x & 0xffff0000u);
-    x[2] = __uint_as_float(v.y << 16);
-    x[3] = __uint_as_float(v.y & 0xffff0000u);
-}
-__device__ __forceinline__ void load4(const float *src, float *x) {
-    const float4 v = *reinterpret_cast<const float4 *>(src);
-    x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
-}
 
 template <int DV, typename Tin>
 __global__ __launch_bounds__(256) void kda_prefill_norm_kernel(PrefillParams p, PrefillWs ws) {
     constexpr int LPR = DV / 4, RPW = kWave / LPR, RPB = 4 * RPW;   // lanes per row, rows per wave / block pass
     constexpr int NP = kNormRows / RPB;                               // passes, all loads issued first
+    using ZT = typename Vec4<Tin>::T;
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     const int H = p.H, c0 = 4 * (lane % LPR);
     const size_t nrows = (size_t)p.total_T * H;
     const bool valid = ws.meta[0] == 1;
     const bool ones = ws.meta[2 * p.N_seq + 3] > 0;   // any rows already final
-    typedef float v4f __attribute__((ext_vector_type(4)));
     v4f o[NP];
-    float zf[NP][4];
+    ZT zr[NP];
     size_t rr[NP];
     bool in[NP];
 #pragma unroll
@@ -1281,7 +1485,7 @@ __global__ __launch_bounds__(256) void kda_prefill_norm_kernel(PrefillParams p, 
         rr[pass] = in[pass] ? r : 0;
         // y is read once and rewritten: streamed past the caches
         o[pass] = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(p.y + rr[pass] * DV + c0));
-        load4(static_cast<const Tin *>(p.z) + rr[pass] * DV + c0, zf[pass]);
+        zr[pass] = *reinterpret_cast<const ZT *>(static_cast<const Tin *>(p.z) + rr[pass] * DV + c0);
     }
 #pragma unroll
     for (int pass = 0; pass < NP; ++pass) {
@@ -1293,29 +1497,13 @@ __global__ __launch_bounds__(256) void kda_prefill_norm_kernel(PrefillParams p, 
             // rows of one-token sequences are already final (decode kernel)
             if (ones) done = live && p.cu_seqlens[sq + 1] - p.cu_seqlens[sq] == 1;
         }
-        const v4f v = o[pass];
-        float ss = v.x * v.x;
-        ss = fmaf(v.y, v.y, ss);
-        ss = fmaf(v.z, v.z, ss);
-        ss = fmaf(v.w, v.w, ss);
-        // row sums: DPP inside each 16-lane row, then (d_v = 128) across row pairs
-        ss = dpp_add<0xB1, 0xF>(ss);
-        ss = dpp_add<0x4E, 0xF>(ss);
-        ss = dpp_add<0x141, 0xF>(ss);
-        ss = dpp_add<0x140, 0xF>(ss);
-        if (LPR == 32) {
-            ss = dpp_add<0x142, 0xA>(ss);   // rows 1, 3 += rows 0, 2
-            const float s_lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ss), 31));
-            const float s_hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ss), 63));
-            ss = lane < 32 ? s_lo : s_hi;
-        }
-        const float rn = 1.0f / sqrtf(ss * (1.0f / DV) + p.rms_eps);
-        const float4 w = *reinterpret_cast<const float4 *>(p.norm_w + h * DV + c0);
-        v4f out;
-        out.x = v.x * rn * (w.x * sigmoid(zf[pass][0]));
-        out.y = v.y * rn * (w.y * sigmoid(zf[pass][1]));
-        out.z = v.z * rn * (w.z * sigmoid(zf[pass][2]));
-        out.w = v.w * rn * (w.w * sigmoid(zf[pass][3]));
+        // tile sums (quads), then the tiles pairwise: quads 4 and 8 (and 16) lanes apart
+        float ss = tile_sumsq(o[pass]);
+        ss += __shfl_xor(ss, 4, kWave);
+        ss += __shfl_xor(ss, 8, kWave);
+        if (LPR == 32) ss += __shfl_xor(ss, 16, kWave);
+        const v4f w = *reinterpret_cast<const v4f *>(p.norm_w + h * DV + c0);
+        v4f out = rms_apply<DV>(o[pass], ss, p.rms_eps, gate4<Tin>(w, zr[pass]));
         if (!live) out = v4f{0.f, 0.f, 0.f, 0.f};
         if (in[pass] && !done) __builtin_nontemporal_store(out, reinterpret_cast<v4f *>(p.y + rr[pass] * DV + c0));
     }
@@ -1340,6 +1528,7 @@ static kda_status launch_prefill_typed(const PrefillParams &p, hipStream_t strea
     ws.P_lo = reinterpret_cast<uint16_t *>(base + l.P_lo);
     ws.Ut = reinterpret_cast<float *>(base + l.Ut);
     ws.gC = reinterpret_cast<float *>(base + l.gC);
+    ws.Xp = reinterpret_cast<uint32_t *>(base + l.Xp);
     ws.G_max = p.total_T / kChunk + p.N_seq;
 
     int dev = 0, cus = 0;
@@ -1376,20 +1565,26 @@ static kda_status launch_prefill_typed(const PrefillParams &p, hipStream_t strea
     // columns per CU and second), when the batch has the prompts and heads to
     // fill the GPU with them (by the host's view: enough rows, and on average
     // four chunks per row, so that one-token rows are not counted as
-    // prompts); else 16 (a single long prompt: all CUs busy)
-    if ((size_t)p.H * (DV / 64) * p.N_seq >= (size_t)cus && (size_t)p.total_T >= (size_t)4 * kChunk * p.N_seq)
-        hipLaunchKernelGGL((kda_prefill_scan_kernel<DK, DV, Tin, 64>),
-                           dim3((unsigned)std::min((size_t)p.H * (DV / 64) * p.N_seq, (size_t)cus)),
+    // prompts); else 16 (a single long prompt: all CUs busy).  The grid: a
+    // multiple of the aligned run of 8 d_v / CB items that holds whole
+    // (sequence, head) groups, at most one workgroup per CU (all resident at
+    // once: a group's workgroups exchange row sums), at least one run.
+    const size_t H8 = ((size_t)p.H + 7) / 8;
+    auto scan_grid = [&](int nz) {
+        const size_t run = 8 * (size_t)nz, items = run * H8 * (size_t)p.N_seq;
+        return (unsigned)std::min(items, std::max(run, (size_t)cus / run * run));
+    };
+    if ((size_t)p.H * (DV / 64) * p.N_seq >= (size_t)cus && (size_t)p.total_T >= (size_t)4 * kChunk * p.N_seq) {
+        hipLaunchKernelGGL((kda_prefill_scan_kernel<DK, DV, Tin, 64>), dim3(scan_grid(DV / 64)), dim3(kScanThreads), 0,
+                           stream, p, ws);
+        if (p.total_T > 0) {
+            const size_t rows = (size_t)p.total_T * p.H;
+            hipLaunchKernelGGL((kda_prefill_norm_kernel<DV, Tin>), dim3((unsigned)((rows + kNormRows - 1) / kNormRows)),
+                               dim3(256), 0, stream, p, ws);
+        }
+    } else
+        hipLaunchKernelGGL((kda_prefill_scan_kernel<DK, DV, Tin, kColBlock>), dim3(scan_grid(DV / kColBlock)),
                            dim3(kScanThreads), 0, stream, p, ws);
-    else
-        hipLaunchKernelGGL((kda_prefill_scan_kernel<DK, DV, Tin, kColBlock>),
-                           dim3((unsigned)std::min((size_t)p.H * (DV / kColBlock) * p.N_seq, (size_t)cus)),
-                           dim3(kScanThreads), 0, stream, p, ws);
-    if (p.total_T > 0) {
-        const size_t rows = (size_t)p.total_T * p.H;
-        hipLaunchKernelGGL((kda_prefill_norm_kernel<DV, Tin>), dim3((unsigned)((rows + kNormRows - 1) / kNormRows)),
-                           dim3(256), 0, stream, p, ws);
-    }
     return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
