@@ -1022,14 +1022,17 @@ __device__ __forceinline__ float tile_sumsq(v4f y) {
 }
 // y / sqrt(mean(y^2) + eps) * (w * sigmoid(z)) for the lane's 4 columns:
 // the gate factors g = w * sigmoid(z), then the row's scale
+__device__ __forceinline__ float sigmoid_hw(float x) {
+    return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x * kLog2e));
+}
 template <typename Tin>
 __device__ __forceinline__ v4f gate4(v4f w, typename Vec4<Tin>::T z) {
-    return v4f{w.x * sigmoid(to_f32(z[0])), w.y * sigmoid(to_f32(z[1])), w.z * sigmoid(to_f32(z[2])),
-               w.w * sigmoid(to_f32(z[3]))};
+    return v4f{w.x * sigmoid_hw(to_f32(z[0])), w.y * sigmoid_hw(to_f32(z[1])), w.z * sigmoid_hw(to_f32(z[2])),
+               w.w * sigmoid_hw(to_f32(z[3]))};
 }
 template <int DV>
 __device__ __forceinline__ v4f rms_apply(v4f y, float ss, float eps, v4f g) {
-    const float rn = 1.0f / sqrtf(ss * (1.0f / DV) + eps);
+    const float rn = __builtin_amdgcn_rsqf(ss * (1.0f / DV) + eps);
     return v4f{y.x * rn * g.x, y.y * rn * g.y, y.z * rn * g.z, y.w * rn * g.w};
 }
 constexpr int kXpSpin = 1 << 20;   // polls of the exchange slots before giving up (about a second)
