@@ -1554,9 +1554,12 @@ static kda_status launch_prefill_typed(const PrefillParams &p, hipStream_t strea
         r.B = p.N_seq; r.H = p.H; r.T = 1;
         r.seq_start = p.cu_seqlens;
         r.seq_ok = ws.meta;
-        const kda_status st = launch_recurrent(r, DK, DV, sizeof(Tin) == 2 ? KDA_BF16 : KDA_F32, RecKind::decode,
-                                               stream);
-        if (st != KDA_OK) return st;
+        // (a single sequence of two or more tokens has no such row)
+        if (!(p.N_seq == 1 && p.total_T >= 2)) {
+            const kda_status st = launch_recurrent(r, DK, DV, sizeof(Tin) == 2 ? KDA_BF16 : KDA_F32, RecKind::decode,
+                                                   stream);
+            if (st != KDA_OK) return st;
+        }
         // one workgroup per compute unit (the LDS of one), each working
         // through the chunks of one head
         const int wph = std::max(1, std::min(ws.G_max, cus / p.H));
