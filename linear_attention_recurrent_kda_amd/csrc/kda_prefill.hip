@@ -840,10 +840,13 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
         }
         }
     }
-    // decayed factors for the scan: Q^ e^G (rows), (K^ e^(G_C - G))^T
-    //    Unit e8 (8 elements) is stored at 8 e8 in operand order, so each wave
-    //    writes whole lines: tile e8 / 64, lane e8 % 64 of that tile.
-    for (int e8 = tid; e8 < kChunk * DK / 8; e8 += kIntraThreads) {
+    // decayed factors for the scan: Q^ e^G (rows), (K^ e^(G_C - G))^T, by
+    //    waves 4-15 (waves 0-3, which invert the diagonal blocks, are the
+    //    last to finish their items).  Unit e8 (8 elements) is stored at 8 e8
+    //    in operand order, so each wave writes whole lines: tile e8 / 64,
+    //    lane e8 % 64 of that tile.
+    for (int e8 = tid - 4 * kWave; e8 < kChunk * DK / 8; e8 += kIntraThreads - 4 * kWave) {
+        if (e8 < 0) break;
         const int tl = e8 / kWave, ln = e8 % kWave;
         const int r = 16 * (tl / KS) + ln % 16, i0 = 32 * (tl % KS) + 8 * (ln / 16);
         const bf16x8 *src = reinterpret_cast<const bf16x8 *>(&L.Q[r][i0]);
@@ -857,7 +860,8 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
         *reinterpret_cast<bf16x8 *>(ws.Q_hi + o) = sx.hi;
         *reinterpret_cast<bf16x8 *>(ws.Q_lo + o) = sx.lo;
     }
-    for (int e8 = tid; e8 < kChunk * DK / 8; e8 += kIntraThreads) {
+    for (int e8 = tid - 4 * kWave; e8 < kChunk * DK / 8; e8 += kIntraThreads - 4 * kWave) {
+        if (e8 < 0) break;
         const int tl = e8 / kWave, ln = e8 % kWave;
         const int i = 16 * (tl / 2) + ln % 16, r0 = 32 * (tl % 2) + 8 * (ln / 16);
         const float fk = L.Fk[r0 / 16][i];
