@@ -217,6 +217,38 @@ def test_many_sequences_wide_scan_blocks():
     assert np.array_equal(host(c1.state[slots[i]]), host(cache.state[slots[i]]))
 
 
+def test_head_count_not_a_multiple_of_8_many_rounds():
+    """12 heads (padded to 16 in the scan's item order) x 6 sequences at
+    d = 64: more 16-column scan items than workgroups, so the groups of
+    column workgroups that exchange row sums come in several rounds, beside
+    items of padded heads that only exit.  Every output, final state and
+    window against the oracle."""
+    g = synth.rng(977)
+    H, dk, dv = 12, 64, 64
+    params = synth.layer_params(g, H, dk, dv)
+    dl, ol = layer_pair(params)
+    lens = [130, 64, 257, 2, 1, 190]
+    n_slots = 8
+    slots = [5, 0, 7, 2, 3, 6]
+    total = sum(lens)
+    inp = synth.token_inputs(g, (total,), H, dk, dv, "bf16")
+    cache = new_cache(n_slots, H, dk, dv, "bf16", fill_seed=6)
+    s_before = host(cache.state)
+    w_before = host(cache.conv_state)
+    y, cu = run_prefill(dl, cache, slots, lens, inp, "bf16")
+    assert cache.err_flag.item() == 0
+    worst = 0.0
+    for i, (sl, ln) in enumerate(zip(slots, lens)):
+        a, b = cu[i], cu[i + 1]
+        o = oracle_seq(ol, s_before[sl], w_before[sl], inp, a, b)
+        errs = [parity_error(y[t], o["y"][0][t - a]) for t in range(a, b)]
+        worst = max(worst, max(errs))
+        assert state_rel_err(host(cache.state[sl:sl + 1]), o["state"]) < 1e-4
+        assert np.array_equal(host(cache.conv_state[sl:sl + 1]), o["window"])
+    print(f"  prefill parity over {len(lens)} sequences x {H} heads: worst max|d|/RMS = {worst:.3e}", flush=True)
+    assert worst <= TOL
+
+
 def test_prefill_then_decode_continues_the_sequence():
     g = synth.rng(980)
     H, dk, dv, T, D = 4, 128, 128, 100, 20
