@@ -267,6 +267,11 @@ kda_status kda_spec_commit_delta(const kda_layer *layer, const kda_cache *cache,
  * kda_decode on those rows), so a mixed prefill + decode batch is one call.  total_T = 0 is
  * allowed: inputs' pointers and y are then not read and may be NULL (the
  * dtype must still be valid); cu_seqlens is still checked.
+ * Concurrency: the workgroups that hold one head's output columns exchange
+ * row sums for the RMSNorm and wait for each other (at most one workgroup
+ * per compute unit is launched, so on a GPU free of other work they all run
+ * at once).  Each wait is bounded (about a second): if other work holds
+ * compute units that long, err_flag is set and the affected rows are wrong.
  */
 kda_status kda_chunk_prefill(const kda_layer *layer, const kda_cache *cache,
                              const int32_t *slot_idx, const int32_t *cu_seqlens,
