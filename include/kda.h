@@ -272,6 +272,7 @@ kda_status kda_spec_commit_delta(const kda_layer *layer, const kda_cache *cache,
  * per compute unit is launched, so on a GPU free of other work they all run
  * at once).  Each wait is bounded (about a second): if other work holds
  * compute units that long, err_flag is set and the affected rows are wrong.
+ * Two prefill calls running at once on one GPU are such work: serialise them.
  */
 kda_status kda_chunk_prefill(const kda_layer *layer, const kda_cache *cache,
                              const int32_t *slot_idx, const int32_t *cu_seqlens,
