@@ -270,9 +270,13 @@ kda_status kda_spec_commit_delta(const kda_layer *layer, const kda_cache *cache,
  * Concurrency: the workgroups that hold one head's output columns exchange
  * row sums for the RMSNorm and wait for each other (at most one workgroup
  * per compute unit is launched, so on a GPU free of other work they all run
- * at once).  Each wait is bounded (about a second): if other work holds
- * compute units that long, err_flag is set and the affected rows are wrong.
- * Two prefill calls running at once on one GPU are such work: serialise them.
+ * at once).  Each wait is bounded (about a second): rows whose sums did not
+ * come in time are normalised by a small kernel after the scan, with the
+ * same arithmetic (bitwise the same results), so other work on the GPU
+ * (another prefill call on another stream, say) costs time, not
+ * correctness.  The bound is read from the environment variable KDA_XP_SPIN
+ * at each call if set (polls; a negative value takes no row as in time):
+ * a testing knob.
  */
 kda_status kda_chunk_prefill(const kda_layer *layer, const kda_cache *cache,
                              const int32_t *slot_idx, const int32_t *cu_seqlens,

@@ -24,7 +24,11 @@
 //          columns are independent given the chunk factors) and the outputs:
 //          O, then RMSNorm over d_v (the column workgroups of a head exchange
 //          per-row partial sums of squares), weight and sigmoid gate
+//   repair after 16-column scans: rows whose sums came too late (marked by
+//          the scan), normalised once every sum is in; exits when none are
+//   norm   after 64-column scans: RMSNorm, weight and gate of every row
 #include <algorithm>
+#include <cstdlib>
 
 #include "kda_device.h"
 #include "kda_internal.h"
@@ -45,7 +49,8 @@ constexpr uint32_t kXpEmpty = 0xFFFFFFFFu;
 struct PrefillWs {
     int32_t *meta;            // [0]: 1 if cu_seqlens is valid; [1 + s]: first chunk of s, s <= N;
                               // [N + 2]: number of chunk-path sequences; [N + 3 + k]: the k-th;
-                              // [2N + 3]: number of one-token sequences (decode kernel)
+                              // [2N + 3]: number of one-token sequences (decode kernel);
+                              // [2N + 4]: nonzero if rows were left for the repair kernel
     uint16_t *Wn_hi, *Wn_lo;  // [G, H] x (64 x d_k)  -W
     uint16_t *Q_hi, *Q_lo;    // [G, H] x (64 x d_k)  Q^ e^G
     uint16_t *K_hi, *K_lo;    // [G, H] x (d_k x 64)  (K^ e^(G_C - G))^T
@@ -53,7 +58,9 @@ struct PrefillWs {
     float *Ut;                // [G, H, 64, d_v]
     float *gC;                // [G, H, d_k]  e^(G_C)
     uint32_t *Xp;             // [G, H, 64, d_v / 16]  sums of squares of O rows over 16 columns
+    uint32_t *Xf;             // [G, H, d_v / 16, 4]  nonzero: the 16 rows of a wave left unnormalised
     int G_max;
+    int xp_spin;              // polls of the exchange before a wave stops waiting
 };
 
 // Offset of element (row, k) of an R x K matrix stored in MFMA A-operand
@@ -67,7 +74,7 @@ __device__ __forceinline__ size_t opnd_off(int row, int k) {
 }
 
 struct WsLayout {
-    size_t meta, Wn_hi, Wn_lo, Q_hi, Q_lo, K_hi, K_lo, P_hi, P_lo, Ut, gC, Xp, total;
+    size_t meta, Wn_hi, Wn_lo, Q_hi, Q_lo, K_hi, K_lo, P_hi, P_lo, Ut, gC, Xp, Xf, total;
 };
 
 static size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
@@ -78,7 +85,7 @@ static WsLayout ws_layout(int H, int dk, int dv, int total_T, int N_seq) {
     WsLayout l{};
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes); return o; };
-    l.meta = take(sizeof(int32_t) * (2 * (size_t)N_seq + 4));
+    l.meta = take(sizeof(int32_t) * (2 * (size_t)N_seq + 5));
     l.Wn_hi = take(2 * GH * kChunk * dk);
     l.Wn_lo = take(2 * GH * kChunk * dk);
     l.Q_hi = take(2 * GH * kChunk * dk);
@@ -90,6 +97,7 @@ static WsLayout ws_layout(int H, int dk, int dv, int total_T, int N_seq) {
     l.Ut = take(4 * GH * kChunk * dv);
     l.gC = take(4 * GH * dk);
     l.Xp = take(4 * GH * kChunk * (dv / 16));
+    l.Xf = take(4 * GH * (dv / 16) * 4);
     l.total = off;
     return l;
 }
@@ -169,6 +177,7 @@ __global__ __launch_bounds__(64) void kda_prefill_meta_kernel(PrefillParams p, P
     bad_slot = __any(bad_slot);
     ones = wave_incl_scan(ones, lane);
     if (lane == kWave - 1) ws.meta[2 * N + 3] = ok ? ones : 0;
+    if (lane == 0) ws.meta[2 * N + 4] = 0;
     if (lane == 0) {
         ws.meta[0] = ok ? 1 : 0;
         ws.meta[N + 2] = ok ? longs : 0;
@@ -817,6 +826,9 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
             if (e4 < kChunk * (DV / 16) / 4)
                 reinterpret_cast<uint4 *>(ws.Xp + gh * kChunk * (DV / 16))[e4] =
                     make_uint4(kXpEmpty, kXpEmpty, kXpEmpty, kXpEmpty);
+            // and its marks of rows left for the repair kernel cleared
+            else if (e4 < kChunk * (DV / 16) / 4 + DV / 16)
+                reinterpret_cast<uint4 *>(ws.Xf + gh * (DV / 16) * 4)[e4 - kChunk * (DV / 16) / 4] = make_uint4(0, 0, 0, 0);
         } else {
         const int bt = j < 1 ? 0 : j < 3 ? 1 : j < 6 ? 2 : 3, bs = j - bt * (bt + 1) / 2;
         if (!(bt == bs && !L.safe[bt])) {   // else summed directly above
@@ -1119,7 +1131,8 @@ __global__ __launch_bounds__(kScanThreads) void kda_prefill_scan_kernel(PrefillP
     const int team = wave / 4, w4 = wave % 4;
     const int lr = lane % 16, lk = lane / 16;
     const int H = p.H, H8 = (H + 7) / 8;
-    bool xp_live = true;   // false once a wait for the exchange ran out
+    // false once a wait for the exchange ran out (a negative bound: at once)
+    bool xp_live = ws.xp_spin >= 0;
     if (ws.meta[0] != 1) {
         // tables that failed validation: every output row is zero
         v4f *y4 = reinterpret_cast<v4f *>(p.y);
@@ -1228,6 +1241,9 @@ __global__ __launch_bounds__(kScanThreads) void kda_prefill_scan_kernel(PrefillP
     // the team's two previous chunks, older first (-1: none); their rows of O
     // wait in the wave's scratch
     int pc1 = -1, pc2 = -1;
+    // the first of the team's chunks whose rows the wave left unnormalised
+    // (-1: none); every later one of the item is left too
+    int miss = -1;
     // The older one's RMSNorm in two steps: fin_issue requests the gate inputs and the
     // row-sum slots (the quad of the row reads PL slots per lane), fin_done
     // waits until no slot is empty and stores the results.  The chunk's own
@@ -1267,13 +1283,15 @@ __global__ __launch_bounds__(kScanThreads) void kda_prefill_scan_kernel(PrefillP
             yo[ct] = *reinterpret_cast<const v4f *>(&Yst[wave][(cc / 2) & 1][rho][16 * ct + 4 * qd]);
         }
         auto full = [](uint64_t v) { return (uint32_t)v != kXpEmpty && (uint32_t)(v >> 32) != kXpEmpty; };
-        // (a wave vote: one path for all lanes; a wait that runs out stops all
-        // later ones of the workgroup, and the error is flagged at its end)
+        // (a wave vote: one path for all lanes; once a wait runs out, this
+        // chunk's rows and those of the wave's later chunks stay unnormalised)
         for (int tries = 0; xp_live && !__all(full(f.sl)); ++tries) {
-            xp_live = tries < kXpSpin;
+            xp_live = tries < ws.xp_spin;
             __builtin_amdgcn_s_sleep(8);
             f.sl = poll(f.src);
         }
+        const bool got = xp_live && __all(full(f.sl));
+        if (!got && miss < 0) miss = cc;
         // the row's sum over its tiles, in the tree order, on its quad
         float a = __uint_as_float((uint32_t)f.sl);
         if (PL == 2) a += __uint_as_float((uint32_t)(f.sl >> 32));
@@ -1283,7 +1301,7 @@ __global__ __launch_bounds__(kScanThreads) void kda_prefill_scan_kernel(PrefillP
         if (t < nc) {
 #pragma unroll
             for (int ct = 0; ct < NCB; ++ct)
-                __builtin_nontemporal_store(rms_apply<DV>(yo[ct], a, p.rms_eps, gz[ct]),
+                __builtin_nontemporal_store(got ? rms_apply<DV>(yo[ct], a, p.rms_eps, gz[ct]) : yo[ct],
                                             reinterpret_cast<v4f *>(p.y + ((size_t)(t0c + t) * H + h) * DV + j0 +
                                                                     16 * ct + 4 * qd));
         }
@@ -1446,12 +1464,22 @@ __global__ __launch_bounds__(kScanThreads) void kda_prefill_scan_kernel(PrefillP
                 fin_done(cc, f);
             }
         }
+        if (miss >= 0 && lane == 0) {
+            // rows whose sums did not come in time stay unnormalised: the
+            // wave's rows in chunks miss, miss + 2, ... to the end of the
+            // sequence, marked for the repair kernel (which runs after this
+            // one, when every sum is in); the marks are stored here, not in
+            // the chunk loop, so that its waits for loads stay loose
+#pragma unroll
+            for (int ct = 0; ct < NCB; ++ct)
+                ws.Xf[(((size_t)(g0 + miss) * H + h) * NT + zb * NCB + ct) * 4 + w4] = 1;
+            ws.meta[2 * p.N_seq + 4] = 1;
+        }
     }
     const int fin = nch & 1;
     for (int e = tid; e < DK * CB; e += kScanThreads) Sg[(e / CB) * DV + j0 + e % CB] = S[fin][e / CB][e % CB];
     __syncthreads();   // the next item's state load rewrites S
     }
-    if (!xp_live && lane == 0) flag_error(p.err_flag);
     // rows of sequences that no kernel computes (padding, a bad slot) are zero
     for (int sq = (int)(blockIdx.x * kScanThreads) + tid; sq < p.N_seq; sq += (int)(gridDim.x * kScanThreads)) {
         const int a0 = p.cu_seqlens[sq], a1 = p.cu_seqlens[sq + 1];
@@ -1517,6 +1545,54 @@ __global__ __launch_bounds__(256) void kda_prefill_norm_kernel(PrefillParams p, 
 }
 
 // ---------------------------------------------------------------------------
+// repair (after the 16-column scan): rows whose row sums did not reach their
+// wave in time (other work holding compute units, so that a group's
+// workgroups did not all run at once) were stored unnormalised, and the wave
+// marked the first chunk it left so.  Once the scan has ended every sum is
+// in, so they are normalised here with the scan's arithmetic (the same bits).
+// Without marks the workgroups exit at once.
+// ---------------------------------------------------------------------------
+constexpr int kRepairBlocks = 64;
+
+template <int DV, typename Tin>
+__global__ __launch_bounds__(256) void kda_prefill_repair_kernel(PrefillParams p, PrefillWs ws) {
+    constexpr int NT = DV / 16, PL = NT / 4;
+    using ZT = typename Vec4<Tin>::T;
+    if (ws.meta[0] != 1 || ws.meta[2 * p.N_seq + 4] == 0) return;
+    const int lane = threadIdx.x % kWave, H = p.H;
+    const int32_t *cs = ws.meta + 1;
+    const size_t nmarks = (size_t)cs[p.N_seq] * H * NT * 4;
+    const size_t nwaves = (size_t)gridDim.x * (blockDim.x / kWave);
+    const int rho = lane / 4, qd = lane % 4;
+    // mark e = ((g H + h) NT + tile) 4 + w4: rows 16 w4 .. + 15 of head h,
+    // columns 16 tile .. + 15, in chunk slot g and every second chunk after it
+    // in its sequence; a mark per wave, a lane taking row 16 w4 + lane / 4 and
+    // 4 columns as in the scan
+    for (size_t e = (size_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave; e < nmarks; e += nwaves) {
+        if (ws.Xf[e] == 0) continue;   // the same word on every lane
+        const int w4 = (int)(e % 4), tile = (int)((e / 4) % NT);
+        const int g = (int)(e / (4 * NT) / H), h = (int)(e / (4 * NT) % H);
+        const int sq = upper_index(cs, p.N_seq + 1, g);
+        const int t = 16 * w4 + rho;
+        for (int gc = g; gc < cs[sq + 1]; gc += 2) {
+            const int t0 = p.cu_seqlens[sq] + (gc - cs[sq]) * kChunk, n = min(kChunk, p.cu_seqlens[sq + 1] - t0);
+            const uint32_t *src = ws.Xp + (((size_t)gc * H + h) * kChunk + t) * NT + PL * qd;
+            float a = __uint_as_float(src[0]);
+            if (PL == 2) a += __uint_as_float(src[1]);
+            a = dpp_add<0xB1, 0xF>(a);   // quad_perm [1,0,3,2]
+            a = dpp_add<0x4E, 0xF>(a);   // quad_perm [2,3,0,1]
+            if (t < n) {
+                const size_t off = ((size_t)(t0 + t) * H + h) * DV + 16 * tile + 4 * qd;
+                const v4f y = *reinterpret_cast<const v4f *>(p.y + off);
+                const v4f w = *reinterpret_cast<const v4f *>(p.norm_w + h * DV + 16 * tile + 4 * qd);
+                const ZT z = *reinterpret_cast<const ZT *>(static_cast<const Tin *>(p.z) + off);
+                *reinterpret_cast<v4f *>(p.y + off) = rms_apply<DV>(y, a, p.rms_eps, gate4<Tin>(w, z));
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // launcher
 // ---------------------------------------------------------------------------
 template <int DK, int DV, typename Tin>
@@ -1536,6 +1612,9 @@ static kda_status launch_prefill_typed(const PrefillParams &p, hipStream_t strea
     ws.Ut = reinterpret_cast<float *>(base + l.Ut);
     ws.gC = reinterpret_cast<float *>(base + l.gC);
     ws.Xp = reinterpret_cast<uint32_t *>(base + l.Xp);
+    ws.Xf = reinterpret_cast<uint32_t *>(base + l.Xf);
+    ws.xp_spin = kXpSpin;
+    if (const char *e = getenv("KDA_XP_SPIN")) ws.xp_spin = atoi(e);   // testing: a short bound (negative: no row in time)
     ws.G_max = p.total_T / kChunk + p.N_seq;
 
     int dev = 0, cus = 0;
@@ -1592,9 +1671,12 @@ static kda_status launch_prefill_typed(const PrefillParams &p, hipStream_t strea
             hipLaunchKernelGGL((kda_prefill_norm_kernel<DV, Tin>), dim3((unsigned)((rows + kNormRows - 1) / kNormRows)),
                                dim3(256), 0, stream, p, ws);
         }
-    } else
+    } else {
         hipLaunchKernelGGL((kda_prefill_scan_kernel<DK, DV, Tin, kColBlock>), dim3(scan_grid(DV / kColBlock)),
                            dim3(kScanThreads), 0, stream, p, ws);
+        if (p.total_T > 0)
+            hipLaunchKernelGGL((kda_prefill_repair_kernel<DV, Tin>), dim3(kRepairBlocks), dim3(256), 0, stream, p, ws);
+    }
     return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 

@@ -249,6 +249,44 @@ def test_head_count_not_a_multiple_of_8_many_rounds():
     assert worst <= TOL
 
 
+@pytest.mark.parametrize("dk,dv,dtype", [(128, 128, "bf16"), (64, 64, "f32")])
+def test_rows_left_for_the_repair_kernel(dk, dv, dtype, monkeypatch):
+    """The 16-column scan normalises O rows with row sums that other
+    workgroups publish.  A row whose sums do not arrive within the wait
+    bound is stored unnormalised and marked, and a kernel after the scan
+    normalises it with the same arithmetic.  KDA_XP_SPIN bounds the wait
+    (a negative value: no row is taken as in time, so every row goes the
+    repair way; 0: one poll).  Both give bitwise the outputs and states of
+    the ordinary call, with no error flag, and match the oracle."""
+    g = synth.rng(981 + dk)
+    H = 8
+    params = synth.layer_params(g, H, dk, dv)
+    dl, ol = layer_pair(params)
+    lens = [300, 1, 129, 64]
+    slots = [2, 0, 3, 1]
+    inp = synth.token_inputs(g, (sum(lens),), H, dk, dv, dtype)
+    runs = {}
+    for spin in (None, "-1", "0"):
+        if spin is None:
+            monkeypatch.delenv("KDA_XP_SPIN", raising=False)
+        else:
+            monkeypatch.setenv("KDA_XP_SPIN", spin)
+        cache = new_cache(4, H, dk, dv, dtype, fill_seed=9)
+        if spin is None:
+            s_before, w_before = host(cache.state), host(cache.conv_state)
+        y, cu = run_prefill(dl, cache, slots, lens, inp, dtype)
+        assert cache.err_flag.item() == 0
+        runs[spin] = (y, host(cache.state), host(cache.conv_state))
+    monkeypatch.delenv("KDA_XP_SPIN", raising=False)
+    for spin in ("-1", "0"):
+        for a, b in zip(runs[None], runs[spin]):
+            assert np.array_equal(a, b), f"KDA_XP_SPIN={spin}"
+    y = runs["-1"][0]
+    for i, (sl, ln) in enumerate(zip(slots, lens)):
+        o = oracle_seq(ol, s_before[sl], w_before[sl], inp, cu[i], cu[i + 1])
+        check_tokens(y[cu[i]:cu[i + 1]], o["y"][0])
+
+
 def test_prefill_then_decode_continues_the_sequence():
     g = synth.rng(980)
     H, dk, dv, T, D = 4, 128, 128, 100, 20
