@@ -287,6 +287,44 @@ def test_rows_left_for_the_repair_kernel(dk, dv, dtype, monkeypatch):
         check_tokens(y[cu[i]:cu[i + 1]], o["y"][0])
 
 
+def test_two_calls_at_once_on_two_streams(monkeypatch):
+    """Two prefill calls launched on two streams at once, each with its own
+    cache and (allocated) workspace: the column workgroups of one call can
+    find compute units held by the other's, so some waits for row sums may
+    run out (the bound is cut to 4096 polls to keep such waits short) and
+    those rows take the repair kernel.  Outputs and states are bitwise those
+    of the same calls run one after the other."""
+    monkeypatch.setenv("KDA_XP_SPIN", "4096")
+    g = synth.rng(986)
+    H, dk, dv, T = 32, 128, 128, 2048
+    params = synth.layer_params(g, H, dk, dv)
+    dl, _ = layer_pair(params)
+    inps = [dev_inputs(synth.token_inputs(g, (T,), H, dk, dv, "bf16"), "bf16") for _ in range(2)]
+    sl = torch.zeros(1, dtype=torch.int32, device=DEV)
+    cu = torch.tensor([0, T], dtype=torch.int32, device=DEV)
+
+    def fresh():
+        return [new_cache(1, H, dk, dv, "bf16", fill_seed=11 + i) for i in range(2)], \
+               [torch.full((T, H, dv), 7.0, device=DEV) for _ in range(2)]
+
+    caches, ys = fresh()
+    for i in range(2):
+        api.kda_chunk_prefill(dl, caches[i], sl, cu, inps[i], ys[i])
+    torch.cuda.synchronize()
+    want = [(host(ys[i]), host(caches[i].state)) for i in range(2)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for _ in range(3):
+        caches, ys = fresh()
+        torch.cuda.synchronize()
+        for i in range(2):
+            api.kda_chunk_prefill(dl, caches[i], sl, cu, inps[i], ys[i], stream=streams[i])
+        torch.cuda.synchronize()
+        for i in range(2):
+            assert caches[i].err_flag.item() == 0
+            assert np.array_equal(host(ys[i]), want[i][0])
+            assert np.array_equal(host(caches[i].state), want[i][1])
+
+
 def test_prefill_then_decode_continues_the_sequence():
     g = synth.rng(980)
     H, dk, dv, T, D = 4, 128, 128, 100, 20
