@@ -325,6 +325,60 @@ def test_two_calls_at_once_on_two_streams(monkeypatch):
             assert np.array_equal(host(caches[i].state), want[i][1])
 
 
+@pytest.mark.parametrize("static", [False, True])
+def test_prefill_in_a_hip_graph_matches_eager(static):
+    """A mixed batch (prompts and one-token rows: the metadata, decode, intra,
+    scan and repair launches) captured in a HIP graph, with a caller
+    workspace or in the library's static array, and replayed three times;
+    before each replay the start states and windows are copied back eagerly,
+    and an eager call on other buffers runs between replays.  Every replay's
+    outputs, states and windows equal the eager call's bitwise."""
+    g = synth.rng(991)
+    H, dk, dv = 8, 128, 128
+    params = synth.layer_params(g, H, dk, dv)
+    dl, _ = layer_pair(params)
+    lens, slots = [300, 1, 130, 1], [2, 0, 3, 1]
+    total = sum(lens)
+    inp = dev_inputs(synth.token_inputs(g, (total,), H, dk, dv, "bf16"), "bf16")
+    sl = torch.from_numpy(np.asarray(slots, np.int32)).to(DEV)
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)).to(DEV)
+    ws = torch.empty(api.kda_chunk_prefill_workspace_bytes(dl, total, len(lens)), dtype=torch.uint8, device=DEV)
+
+    def call(cache, y):
+        if static:
+            api.kda_chunk_prefill_static(dl, cache, sl, cu, inp, y)
+        else:
+            api.kda_chunk_prefill(dl, cache, sl, cu, inp, y, ws)
+
+    cache = new_cache(4, H, dk, dv, "bf16", fill_seed=31)
+    s0, w0 = cache.state.clone(), cache.conv_state.clone()
+    y = torch.full((total, H, dv), 7.0, device=DEV)
+    call(cache, y)
+    torch.cuda.synchronize()
+    want = (y.clone(), cache.state.clone(), cache.conv_state.clone())
+    other = new_cache(4, H, dk, dv, "bf16", fill_seed=32)
+    y_other = torch.empty_like(y)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        call(cache, y)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for r in range(3):
+        cache.state.copy_(s0)
+        cache.conv_state.copy_(w0)
+        y.fill_(7.0)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, want[0]), r
+        assert torch.equal(cache.state, want[1]), r
+        assert torch.equal(cache.conv_state, want[2]), r
+        assert cache.err_flag.item() == 0
+        call(other, y_other)   # eager work between replays
+        torch.cuda.synchronize()
+
+
 def test_prefill_then_decode_continues_the_sequence():
     g = synth.rng(980)
     H, dk, dv, T, D = 4, 128, 128, 100, 20
