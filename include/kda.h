@@ -270,7 +270,7 @@ kda_status kda_spec_commit_delta(const kda_layer *layer, const kda_cache *cache,
  * Concurrency: the workgroups that hold one head's output columns exchange
  * row sums for the RMSNorm and wait for each other (at most one workgroup
  * per compute unit is launched, so on a GPU free of other work they all run
- * at once).  Each wait is bounded (about a second): rows whose sums did not
+ * at once).  Each wait is bounded (about 25 ms): rows whose sums did not
  * come in time are normalised by a small kernel after the scan, with the
  * same arithmetic (bitwise the same results), so other work on the GPU
  * (another prefill call on another stream, say) costs time, not

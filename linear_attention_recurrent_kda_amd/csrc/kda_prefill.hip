@@ -1051,7 +1051,10 @@ __device__ __forceinline__ v4f rms_apply(v4f y, float ss, float eps, v4f g) {
     const float rn = __builtin_amdgcn_rsqf(ss * (1.0f / DV) + eps);
     return v4f{y.x * rn * g.x, y.y * rn * g.y, y.z * rn * g.z, y.w * rn * g.w};
 }
-constexpr int kXpSpin = 1 << 20;   // polls of the exchange slots before giving up (about a second)
+// Polls of the exchange slots before a wave stops waiting (each a sleep and
+// a load, ~1.5 us: about 25 ms in all, thousands of times the usual wait of
+// a few chunks; rows left then are finished by the repair kernel)
+constexpr int kXpSpin = 1 << 14;
 
 template <int DK, int NCB>
 struct ScanOps {
