@@ -1011,8 +1011,11 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_prefill_intra_kernel(Pre
 // items are ordered so that its d_v / CB items are 8 apart inside an aligned
 // run of 8 d_v / CB items (all on one XCD, as workgroups go to XCDs
 // round-robin), and the grid is a multiple of that run and at most one
-// workgroup per CU.  The wait is bounded: if it ever runs out, the workgroup
-// waits no more and flags the error.  With 64-column blocks the LDS is full:
+// workgroup per CU.  The wait is bounded: if it ever runs out (other work
+// holding compute units), the wave waits no more, stores its rows of that and
+// its later chunks unnormalised and marks them; the repair kernel after the
+// scan normalises them with the same arithmetic.  With 64-column blocks the
+// LDS is full:
 // the scan writes O and the norm kernel below normalises it with the same
 // arithmetic (both give the same bits).
 // ---------------------------------------------------------------------------
