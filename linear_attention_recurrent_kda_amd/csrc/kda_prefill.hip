@@ -247,9 +247,11 @@ struct __align__(16) IntraLds {
     float Cea[DK];
 };
 
-// Sum over the 64 lanes of a wave (all lanes active), every lane receiving
-// the same value (the DPP form of kda_device.h).
-__device__ __forceinline__ float wave_sum_dpp(float v) { return lane_sum<kWave>(v); }
+// The value of the lane the DPP control selects inside each quad of lanes.
+template <int CTRL>
+__device__ __forceinline__ float quad_get(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
 
 // Hardware exp2 / log2 / reciprocal forms for the per-token preparation
 // (about 1 ulp each; the chunk algebra's bf16x3 contractions are ~1e-5).
@@ -332,26 +334,47 @@ __device__ __forceinline__ void rows_compute(const PrefillParams &p, const typen
         const float4 v = wt[e];
         w[e][0] = v.x; w[e][1] = v.y; w[e][2] = v.z; w[e][3] = v.w;
     }
+    float y[8][NC], ss[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        const int row = 8 * part + j;
-        float y[NC];
 #pragma unroll
         for (int e = 0; e < NC; ++e) {
             float acc = w[e][0] * R::get(raw[j], e);
             acc = fmaf(w[e][1], R::get(raw[j + 1], e), acc);
             acc = fmaf(w[e][2], R::get(raw[j + 2], e), acc);
             acc = fmaf(w[e][3], R::get(raw[j + 3], e), acc);
-            y[e] = p.silu ? silu_hw(acc) : acc;
+            y[j][e] = p.silu ? silu_hw(acc) : acc;
         }
-        float ss = 0.f;
+        ss[j] = 0.f;
 #pragma unroll
-        for (int e = 0; e < NC; ++e) ss = fmaf(y[e], y[e], ss);
-        ss = wave_sum_dpp(ss);
-        const float sc = row < n ? scale * __builtin_amdgcn_rsqf(ss + p.l2_eps) : 0.f;
+        for (int e = 0; e < NC; ++e) ss[j] = fmaf(y[j][e], y[j][e], ss[j]);
+    }
+    // The eight row sums over the wave, by halving exchanges: at each step a
+    // lane keeps the half of its partial sums that its lane bit selects and
+    // adds the partner's partials of that half (the partner lane differs in
+    // that bit), so after lane bits 0, 1 and 2 it holds one row, l % 8, and
+    // the sums over lane bits 3, 4 and 5 complete it.  One rsqrt per lane
+    // instead of one per row.
+    const bool b0 = lane & 1, b1 = lane & 2, b2 = lane & 4;
+    float r1[4], r2[2];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)   // partner lane ^ 1: quad_perm [1,0,3,2]
+        r1[k] = (b0 ? ss[2 * k + 1] : ss[2 * k]) + quad_get<0xB1>(b0 ? ss[2 * k] : ss[2 * k + 1]);
+#pragma unroll
+    for (int k = 0; k < 2; ++k)   // partner lane ^ 2: quad_perm [2,3,0,1]
+        r2[k] = (b1 ? r1[2 * k + 1] : r1[2 * k]) + quad_get<0x4E>(b1 ? r1[2 * k] : r1[2 * k + 1]);
+    float r3 = (b2 ? r2[1] : r2[0]) + __shfl_xor(b2 ? r2[0] : r2[1], 4, kWave);
+    r3 += __shfl_xor(r3, 8, kWave);
+    r3 += __shfl_xor(r3, 16, kWave);
+    r3 += __shfl_xor(r3, 32, kWave);
+    const float scl = 8 * part + (lane & 7) < n ? scale * __builtin_amdgcn_rsqf(r3 + p.l2_eps) : 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int row = 8 * part + j;
+        const float sc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, scl), j));
         float *dst = out + row * ostride + cb;
-        if (NC == 2) *reinterpret_cast<float2 *>(dst) = make_float2(y[0] * sc, y[NC - 1] * sc);
-        else dst[0] = y[0] * sc;
+        if (NC == 2) *reinterpret_cast<float2 *>(dst) = make_float2(y[j][0] * sc, y[j][NC - 1] * sc);
+        else dst[0] = y[j][0] * sc;
     }
 }
 
